@@ -1,0 +1,473 @@
+"""Float64 CPU oracle for entropy-guided, head-adaptive sparse prefill attention
+and decode-time KV retention.
+
+TEST INFRASTRUCTURE ONLY.  Only the test-suite, the smoke check and the CPU
+baseline leg of the benchmark may import this module.  The library's HIP path
+never calls it, and this module shares no code, table or helper with the HIP
+path: it is plain numpy in float64, written step by step from the pages.
+
+Sources (cited by page title and section / equation / algorithm):
+  [EI]  "From Rigid to Dynamic: Entropy-Guided Adaptive Inference for
+        Long-Context LLMs" (EntropyInfer), arXiv 2606.09508.
+  [KV]  Blog notes "attention-kv-cache-mechanics", section on InfoKV
+        (eq. 4 window-mean attention score, eq. 8 fused score).
+  [EP]  "EntroPrefill: Renyi-Guided Context Pruning with Conditional Stability
+        Guarantees for Retrieval-Augmented Generation", Sec. 2.1 (GQA attention,
+        observer-pooled measure), Sec. 3.1 (sink-isolated Renyi pooling,
+        regularized head weights), Sec. 8.1 (online softmax / compaction).
+
+Readings taken where the pages are silent or garbled are listed in each
+function's docstring (R-numbers match the design notes).
+
+Parity status: every function here is pinned by the not-gpu tests
+(closed forms, worked example, library special cases, brute force) except the
+tie-free part of selection beyond brute force, which is pinned only by
+sorting-library brute force and planted recall.
+"""
+from __future__ import annotations
+
+import math
+from typing import Optional, Sequence
+
+import numpy as np
+
+__all__ = [
+    "causal_blocks", "pool_mean", "pool_maxmin", "observation_rows",
+    "observation_rows_maxmin", "shannon", "renyi", "entropy_of_rows",
+    "entropy_score", "classify", "kclamp", "allocate_budget", "select_topk",
+    "select_blocks", "qblock_list", "sparse_prefill_attn",
+    "sparse_prefill_attn_rows", "window_mean", "head_weights", "kv_retain",
+    "kv_retain_slice", "sparse_decode_attn", "softmax",
+]
+
+MODE_FIXED, MODE_TWO_LEVEL, MODE_PROPORTIONAL, MODE_ALG3 = 0, 1, 2, 3
+SHANNON, RENYI = 0, 1
+
+
+# ----------------------------------------------------------------------------
+# helpers (plain definitions)
+# ----------------------------------------------------------------------------
+def softmax(z: np.ndarray, axis: int = -1) -> np.ndarray:
+    """exp(z - max) / sum exp(z - max) along `axis`; -inf entries get 0."""
+    z = np.asarray(z, dtype=np.float64)
+    m = np.max(z, axis=axis, keepdims=True)
+    e = np.exp(z - m)
+    return e / np.sum(e, axis=axis, keepdims=True)
+
+
+def causal_blocks(s: int, L_S: int, L_B: int) -> int:
+    """C_B(s) = (s+1) * L_S / L_B: key blocks visible to segment s.
+    [EI] Sec. 4.1 notation (C_{B_i} per segment); block-causal reading R3."""
+    return (s + 1) * L_S // L_B
+
+
+def _sm_scale(d: int, sm_scale: Optional[float]) -> float:
+    # [EI] Sec. 2 / Sec. 3.1: softmax(Q K^T / sqrt(d)); applied everywhere (R2).
+    return 1.0 / math.sqrt(d) if not sm_scale else float(sm_scale)
+
+
+# ----------------------------------------------------------------------------
+# Step 1: pooling
+# ----------------------------------------------------------------------------
+def pool_mean(K: np.ndarray, L_B: int) -> np.ndarray:
+    """Mean of the keys of every L_B-token block: K [Hkv, N, d] -> [Hkv, N/L_B, d].
+    The block partition follows [EI] Sec. 4.2 (observation matrix built from
+    blocks, after CritiPrefill) and App. A eq. (1) (C_S x C_B entries).  Mean
+    pooling with a query probe is the reading R1."""
+    K = np.asarray(K, dtype=np.float64)
+    H, N, d = K.shape
+    return K.reshape(H, N // L_B, L_B, d).mean(axis=2)
+
+
+def pool_maxmin(X: np.ndarray, L: int):
+    """Element-wise max and min over every chunk of L rows ([EI] Sec. 4.2,
+    Alg. 1: Q_Max / Q_Min by reshape(N_S, L_S, d) then max / min over dim 1;
+    K_Rep "follows a similar process", taken per key block)."""
+    X = np.asarray(X, dtype=np.float64)
+    H, N, d = X.shape
+    r = X.reshape(H, N // L, L, d)
+    return r.max(axis=2), r.min(axis=2)
+
+
+# ----------------------------------------------------------------------------
+# Steps 2-4: observation rows
+# ----------------------------------------------------------------------------
+def observation_rows(Q, K, L_S: int, L_B: int, P: int, sm_scale=None) -> np.ndarray:
+    """Probe observation rows a_bar [Hq, C_S, C_B] (mean-probe mode).
+
+    For head h (KV group g = h // r, reading R12) and segment s:
+      probe rows u = last P queries of segment s         (R1; CateKV rebuttal:
+                                                            last queries observe best)
+      z_{u,j} = sigma * q_{h,u} . kbar_{g,j},  j < C_B(s) (R3: block-causal)
+      a_{u,.} = softmax_j(z_{u,.})
+      a_bar_{h,s,j} = (1/P) sum_u a_{u,j}                 ([KV] eq. 4 window mean;
+                                                            [EP] Sec. 2.1 observer pool)
+    Entries j >= C_B(s) hold the sentinel -1."""
+    Q = np.asarray(Q, dtype=np.float64)
+    Hq, N, d = Q.shape
+    Hkv = K.shape[0]
+    r = Hq // Hkv
+    C_S, C_B = N // L_S, N // L_B
+    sc = _sm_scale(d, sm_scale)
+    kbar = pool_mean(K, L_B)
+    abar = np.full((Hq, C_S, C_B), -1.0)
+    for h in range(Hq):
+        g = h // r
+        for s in range(C_S):
+            cb = causal_blocks(s, L_S, L_B)
+            probe = Q[h, (s + 1) * L_S - P:(s + 1) * L_S]
+            z = sc * (probe @ kbar[g, :cb].T)
+            abar[h, s, :cb] = softmax(z, axis=1).mean(axis=0)
+    return abar
+
+
+def observation_rows_maxmin(Q, K, L_S: int, L_B: int, sm_scale=None) -> np.ndarray:
+    """Paper-literal observation rows ([EI] Sec. 4.2, Alg. 1 and Alg. 2).
+
+    Q_max/Q_min per segment, K_max/K_min per key block;
+    S1..S4 = softmax over the causal blocks of sigma * (Q_x . K_y);
+    A_obs = elementwise max((S1+S2)/2, (S3+S4)/2), renormalised to sum 1 (R5).
+    sigma = 1/sqrt(d) is applied although Alg. 2 omits it (R2)."""
+    Q = np.asarray(Q, dtype=np.float64)
+    Hq, N, d = Q.shape
+    Hkv = K.shape[0]
+    r = Hq // Hkv
+    C_S, C_B = N // L_S, N // L_B
+    sc = _sm_scale(d, sm_scale)
+    qmax, qmin = pool_maxmin(Q, L_S)
+    kmax, kmin = pool_maxmin(K, L_B)
+    abar = np.full((Hq, C_S, C_B), -1.0)
+    for h in range(Hq):
+        g = h // r
+        for s in range(C_S):
+            cb = causal_blocks(s, L_S, L_B)
+            s1 = softmax(sc * kmax[g, :cb] @ qmax[h, s])
+            s2 = softmax(sc * kmin[g, :cb] @ qmax[h, s])
+            s3 = softmax(sc * kmax[g, :cb] @ qmin[h, s])
+            s4 = softmax(sc * kmin[g, :cb] @ qmin[h, s])
+            a = np.maximum((s1 + s2) / 2.0, (s3 + s4) / 2.0)
+            abar[h, s, :cb] = a / a.sum()
+    return abar
+
+
+# ----------------------------------------------------------------------------
+# Step 5: entropy
+# ----------------------------------------------------------------------------
+def shannon(p) -> float:
+    """H(p) = -sum_j p_j ln p_j with 0 ln 0 = 0 (natural log).
+    [EI] Sec. 2 and Sec. 3.1 (row-wise attention entropy); [EP] Sec. 2.2
+    (natural logarithms)."""
+    p = np.asarray(p, dtype=np.float64)
+    p = p[p > 0]
+    return float(-np.sum(p * np.log(p)))
+
+
+def renyi(p, alpha: float) -> float:
+    """Renyi entropy of order alpha: ln(sum_j p_j^alpha) / (1 - alpha).
+    alpha = 1 is Shannon.  [EP] Sec. 3.1 (order two: -ln of the collision sum),
+    Sec. 3.2 (the Renyi family, monotone in alpha).  alpha <= 0 is rejected
+    (reading R18)."""
+    if not alpha > 0 or not math.isfinite(alpha):
+        raise ValueError("renyi order must be finite and > 0")
+    if alpha == 1.0:
+        return shannon(p)
+    p = np.asarray(p, dtype=np.float64)
+    p = p[p > 0]
+    return float(np.log(np.sum(p ** alpha)) / (1.0 - alpha))
+
+
+def entropy_of_rows(abar: np.ndarray, L_S: int, L_B: int, kind: int = SHANNON,
+                    alpha: float = 2.0) -> np.ndarray:
+    """E[h, s] = entropy of the observation row over its causal blocks
+    ([EI] Sec. 4.2: entropy of every row of A_obs; reading R4)."""
+    Hq, C_S, _ = abar.shape
+    E = np.zeros((Hq, C_S))
+    for h in range(Hq):
+        for s in range(C_S):
+            row = abar[h, s, :causal_blocks(s, L_S, L_B)]
+            E[h, s] = shannon(row) if kind == SHANNON else renyi(row, alpha)
+    return E
+
+
+def entropy_score(Q, K, L_S, L_B, P, kind=SHANNON, alpha=2.0, sm_scale=None,
+                  pool="mean"):
+    """Steps 1-5 together: (a_bar [Hq, C_S, C_B], E [Hq, C_S])."""
+    if pool == "mean":
+        abar = observation_rows(Q, K, L_S, L_B, P, sm_scale)
+    elif pool == "maxmin":
+        abar = observation_rows_maxmin(Q, K, L_S, L_B, sm_scale)
+    else:
+        raise ValueError(pool)
+    return abar, entropy_of_rows(abar, L_S, L_B, kind, alpha)
+
+
+# ----------------------------------------------------------------------------
+# Steps 6-7: classification and budgets
+# ----------------------------------------------------------------------------
+def classify(E: np.ndarray, threshold: float) -> np.ndarray:
+    """Rigid(h) <=> max over segments of E[h, s] < e_t.
+    [EI] Sec. 4.2, Alg. 3 (the head test on the maximum segment entropy)."""
+    return np.max(np.asarray(E, dtype=np.float64), axis=1) < threshold
+
+
+def kclamp(x: float, cb: int) -> int:
+    """Budget in blocks: min(C_B(s), max(1, ceil(x - 1e-9))) (reading R9:
+    a product that lands on an integer up to rounding stays that integer)."""
+    return int(min(cb, max(1, math.ceil(x - 1e-9))))
+
+
+def allocate_budget(E, L_S: int, L_B: int, mode: int, frac=0.25, frac_rigid=0.05,
+                    frac_dynamic=0.30, frac_min=0.02, frac_max=0.50,
+                    entropy_threshold=0.5, base_tokens=2048.0, alg3_alpha=0.5,
+                    alg3_delta_t=0.4):
+    """Per-(head, segment) key-block budgets k [Hq, C_S] and rigid flags [Hq].
+
+    FIXED(f):           k = kclamp(f * C_B(s))
+    TWO_LEVEL(fr, fd):  f = fr for rigid heads, fd otherwise ([EI] Sec. 1:
+                        rigid heads get a fixed minimal budget, dynamic more)
+    PROPORTIONAL:       f = min(fmax, max(fmin, fmax * E / ln C_B(s)))  (R14)
+    ALG3(B_h tokens):   [EI] Sec. 4.2, Alg. 3.  Rigid: B_s = B_h.  Dynamic:
+                        B_0 = B_h; B_s = clamp(B_{s-1} + alpha * B_h *
+                        (|e_s - e_{s-1}| / max(e_{s-1}, e_t) - Delta_t), B_h, 3 B_h)
+                        (R6: garbled clamp read as [B_h, 3 B_h]; R7: guarded
+                        divisor; R8: segments 0..C_S-1);  k = kclamp(B_s / L_B)."""
+    E = np.asarray(E, dtype=np.float64)
+    Hq, C_S = E.shape
+    rigid = classify(E, entropy_threshold)
+    k = np.zeros((Hq, C_S), dtype=np.int64)
+    for h in range(Hq):
+        if mode == MODE_ALG3:
+            Bs = float(base_tokens)
+            for s in range(C_S):
+                if s > 0 and not rigid[h]:
+                    prev = E[h, s - 1]
+                    fluct = abs(E[h, s] - prev) / max(prev, entropy_threshold)
+                    Bs = Bs + alg3_alpha * base_tokens * (fluct - alg3_delta_t)
+                    Bs = min(max(Bs, base_tokens), 3.0 * base_tokens)
+                k[h, s] = kclamp(Bs / L_B, causal_blocks(s, L_S, L_B))
+            continue
+        for s in range(C_S):
+            cb = causal_blocks(s, L_S, L_B)
+            if mode == MODE_FIXED:
+                f = frac
+            elif mode == MODE_TWO_LEVEL:
+                f = frac_rigid if rigid[h] else frac_dynamic
+            elif mode == MODE_PROPORTIONAL:
+                ehat = E[h, s] / math.log(cb) if cb > 1 else 0.0
+                f = min(frac_max, max(frac_min, frac_max * ehat))
+            else:
+                raise ValueError(mode)
+            k[h, s] = kclamp(f * cb, cb)
+    return rigid, k
+
+
+# ----------------------------------------------------------------------------
+# Step 8: top-k selection
+# ----------------------------------------------------------------------------
+def select_topk(scores: Sequence[float], k: int) -> list:
+    """Indices of the k best entries under the order (score descending, index
+    ascending), returned ascending.  Top-k keep rule: [EI] App. A eq. (2)
+    (top-k blocks) and Alg. 4 step 3 (TopK); tie-break to the lower index."""
+    order = sorted(range(len(scores)), key=lambda j: (-float(scores[j]), j))
+    return sorted(order[:k])
+
+
+def select_blocks(abar, budget, L_S: int, L_B: int, k_max: Optional[int] = None):
+    """Sel(h, s) for every (head, segment): block_idx [Hq, C_S, k_max]
+    ascending and padded with -1, block_cnt [Hq, C_S]."""
+    Hq, C_S, _ = abar.shape
+    budget = np.asarray(budget)
+    if k_max is None:
+        k_max = int(budget.max())
+    idx = np.full((Hq, C_S, k_max), -1, dtype=np.int64)
+    cnt = np.zeros((Hq, C_S), dtype=np.int64)
+    for h in range(Hq):
+        for s in range(C_S):
+            cb = causal_blocks(s, L_S, L_B)
+            kk = int(min(budget[h, s], cb, k_max))
+            sel = select_topk(abar[h, s, :cb], kk)
+            idx[h, s, :len(sel)] = sel
+            cnt[h, s] = len(sel)
+    return idx, cnt
+
+
+# ----------------------------------------------------------------------------
+# Steps 9-10: block-sparse causal GQA attention
+# ----------------------------------------------------------------------------
+def qblock_list(block_idx, block_cnt, h: int, b: int, L_S: int, L_B: int) -> list:
+    """L(h, b) = {j in Sel(h, s) : j < b} union {b}, s = segment of q-block b.
+    Reading R10: the own (diagonal) block is always attended, causally masked;
+    selected blocks at or after b are not attended."""
+    s = (b * L_B) // L_S
+    sel = [int(j) for j in block_idx[h, s, :int(block_cnt[h, s])]]
+    return sorted({j for j in sel if 0 <= j < b}) + [b]
+
+
+def sparse_prefill_attn_rows(Q, K, V, block_idx, block_cnt, h: int, b: int,
+                             L_S: int, L_B: int, sm_scale=None):
+    """Output rows of q-block b of head h: (O [L_B, d], lse [L_B]).
+
+    Causal GQA attention ([EP] Sec. 2.1: A_{u,j} = exp z_uj / sum_{v<=u} exp z_uv,
+    z = q_u . k_{g(h), j} / sqrt(d)) restricted to the keys of the blocks in
+    L(h, b) ([EI] App. A eq. (3): attention over the selected blocks only)."""
+    Q = np.asarray(Q); K = np.asarray(K); V = np.asarray(V)
+    Hq, N, d = Q.shape
+    r = Hq // K.shape[0]
+    g = h // r
+    sc = _sm_scale(d, sm_scale)
+    blocks = qblock_list(block_idx, block_cnt, h, b, L_S, L_B)
+    keys = np.concatenate([np.arange(j * L_B, (j + 1) * L_B) for j in blocks])
+    rows = np.arange(b * L_B, (b + 1) * L_B)
+    q = Q[h, rows].astype(np.float64)
+    kk = K[g, keys].astype(np.float64)
+    vv = V[g, keys].astype(np.float64)
+    z = sc * (q @ kk.T)
+    z[keys[None, :] > rows[:, None]] = -np.inf
+    m = z.max(axis=1, keepdims=True)
+    p = np.exp(z - m)
+    l = p.sum(axis=1, keepdims=True)
+    O = (p @ vv) / l
+    lse = (m + np.log(l))[:, 0]
+    return O, lse
+
+
+def sparse_prefill_attn(Q, K, V, block_idx, block_cnt, L_S: int, L_B: int,
+                        sm_scale=None):
+    """Whole output O [Hq, N, d] and lse [Hq, N] (natural log)."""
+    Hq, N, d = Q.shape
+    O = np.zeros((Hq, N, d))
+    lse = np.zeros((Hq, N))
+    for h in range(Hq):
+        for b in range(N // L_B):
+            o, l = sparse_prefill_attn_rows(Q, K, V, block_idx, block_cnt, h, b,
+                                            L_S, L_B, sm_scale)
+            O[h, b * L_B:(b + 1) * L_B] = o
+            lse[h, b * L_B:(b + 1) * L_B] = l
+    return O, lse
+
+
+# ----------------------------------------------------------------------------
+# Step 11: decode-time KV retention
+# ----------------------------------------------------------------------------
+def window_mean(A_rows) -> np.ndarray:
+    """a_t = (1/W) sum_u A_{u,t}: [KV] eq. 4 window-mean attention score;
+    [EP] Sec. 2.1 observer-pooled measure a^h_j."""
+    A_rows = np.asarray(A_rows, dtype=np.float64)
+    return A_rows.sum(axis=0) / A_rows.shape[0]
+
+
+def sink_isolated_entropy(a, n_sink: int, kind: int = SHANNON, alpha: float = 2.0):
+    """[EP] Sec. 3.1: a~_j = a_j / z_h over non-sink positions, then the entropy
+    of a~ (order 2: -ln sum a~^2).  Shannon is the alpha = 1 member."""
+    a = np.asarray(a, dtype=np.float64)[n_sink:]
+    z = a.sum()
+    if not z > 0:
+        return 0.0
+    at = a / z
+    return shannon(at) if kind == SHANNON else renyi(at, alpha)
+
+
+def head_weights(H, zeta: float, tau: float) -> np.ndarray:
+    """w_h = zeta / r + (1 - zeta) * v_h, v_h = softmax_h(-H_h / tau) within the
+    GQA group ([EP] Sec. 3.1: regularized head weighting with group floor zeta
+    and entropy temperature tau; reading R15)."""
+    H = np.asarray(H, dtype=np.float64)
+    r = H.size
+    v = softmax(-H / tau)
+    return zeta / r + (1.0 - zeta) * v
+
+
+def kv_retain_slice(q_obs, k, n_sink: int, n_recent: int, n_keep: int,
+                    kind: int = SHANNON, alpha: float = 2.0, zeta: float = 0.5,
+                    tau: float = 1.0, raw: bool = False, info_alpha: float = 1.0,
+                    token_entropy=None, sm_scale=None):
+    """Retention for one (batch, KV group) slice.
+
+    q_obs [r, W, d] observer queries of the group's heads; k [L, d].
+    Returns (keep [n_total] ascending, mu [L], H [r]).
+
+    Observer u sits at position L - W + u and sees keys t <= L - W + u (R16).
+      A^h_{u,t} = causal softmax          ([EP] Sec. 2.1)
+      a^h_t     = window mean              ([KV] eq. 4)
+      H_h       = sink-isolated entropy    ([EP] Sec. 3.1)
+      w_h       = regularized weights      ([EP] Sec. 3.1)
+      mu_t      = sum_h w_h a^h_t          ([EP] Sec. 3.1 group mixture)
+      optional InfoKV fusion mu <- alpha_I mu + (1 - alpha_I) softmax_t(E_tok)
+                                           ([KV] eq. 8)
+    RAW mode (the literal score of [EI] Alg. 4): mu_t = sum_h sum_u
+    sigma q_{h,u} . k_t with no mask and no softmax.
+    keep = sinks U top-n_keep of [n_sink, L - n_recent) under (-mu, t) U recent
+    (R17), or everything when n_sink + n_recent + n_keep >= L."""
+    q_obs = np.asarray(q_obs, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    r, W, d = q_obs.shape
+    L = k.shape[0]
+    sc = _sm_scale(d, sm_scale)
+    H = np.zeros(r)
+    if raw:
+        mu = np.zeros(L)
+        for h in range(r):
+            mu += (sc * (q_obs[h] @ k.T)).sum(axis=0)
+    else:
+        a = np.zeros((r, L))
+        pos = L - W + np.arange(W)
+        for h in range(r):
+            z = sc * (q_obs[h] @ k.T)
+            z[np.arange(L)[None, :] > pos[:, None]] = -np.inf
+            a[h] = window_mean(softmax(z, axis=1))
+            H[h] = sink_isolated_entropy(a[h], n_sink, kind, alpha)
+        w = head_weights(H, zeta, tau)
+        mu = (w[:, None] * a).sum(axis=0)
+        if token_entropy is not None and info_alpha < 1.0:
+            mu = info_alpha * mu + (1.0 - info_alpha) * softmax(
+                np.asarray(token_entropy, dtype=np.float64))
+    if n_sink + n_recent + n_keep >= L:
+        return np.arange(L), mu, H
+    cand_lo, cand_hi = n_sink, L - n_recent
+    top = select_topk(mu[cand_lo:cand_hi], n_keep)
+    keep = list(range(n_sink)) + [cand_lo + t for t in top] + list(range(cand_hi, L))
+    return np.asarray(sorted(keep), dtype=np.int64), mu, H
+
+
+def kv_retain(q_obs, k, v, n_sink, n_recent, n_keep, kind=SHANNON, alpha=2.0,
+              zeta=0.5, tau=1.0, raw=False, info_alpha=1.0, token_entropy=None,
+              sm_scale=None, slices=None):
+    """All (batch, KV group) slices, or only those listed in `slices`.
+    Returns dict (b, g) -> (keep, k_kept, v_kept, mu, H).  Compaction keeps
+    token order ([EP] Sec. 8.1: gather of retained entries, original order;
+    [EI] Alg. 4 step 4)."""
+    B, Hq, W, d = q_obs.shape
+    Hkv = k.shape[1]
+    r = Hq // Hkv
+    out = {}
+    todo = slices if slices is not None else [(b, g) for b in range(B) for g in range(Hkv)]
+    for (b, g) in todo:
+        te = None if token_entropy is None else token_entropy[b]
+        keep, mu, H = kv_retain_slice(q_obs[b, g * r:(g + 1) * r], k[b, g], n_sink,
+                                      n_recent, n_keep, kind, alpha, zeta, tau, raw,
+                                      info_alpha, te, sm_scale)
+        out[(b, g)] = (keep, np.asarray(k[b, g], dtype=np.float64)[keep],
+                       np.asarray(v[b, g], dtype=np.float64)[keep], mu, H)
+    return out
+
+
+# ----------------------------------------------------------------------------
+# Step 12: decode attention over the kept entries
+# ----------------------------------------------------------------------------
+def sparse_decode_attn(q_new, k_kept, v_kept, sm_scale=None):
+    """o_h = sum_t softmax_t(sigma q_h . k_{g,t}) v_{g,t} over the kept entries
+    (all of them precede the new token, so there is no mask).
+    q_new [B, Hq, d]; k_kept / v_kept [B, Hkv, n_total, d] -> o [B, Hq, d]."""
+    q_new = np.asarray(q_new, dtype=np.float64)
+    B, Hq, d = q_new.shape
+    Hkv = k_kept.shape[1]
+    r = Hq // Hkv
+    sc = _sm_scale(d, sm_scale)
+    o = np.zeros((B, Hq, d))
+    for b in range(B):
+        for h in range(Hq):
+            kk = np.asarray(k_kept[b, h // r], dtype=np.float64)
+            vv = np.asarray(v_kept[b, h // r], dtype=np.float64)
+            p = softmax(sc * (kk @ q_new[b, h]))
+            o[b, h] = p @ vv
+    return o

@@ -1,0 +1,158 @@
+"""Pins for pooling, probe observation rows and per-(head, segment) entropy."""
+import math
+
+import numpy as np
+
+from oracle import egs_oracle as O
+from entropy_guided_sparse_amd import synth
+
+HQ, HKV, D, N, LB, LS, P = 4, 2, 16, 256, 16, 64, 8
+
+
+def _designed_inputs(seed=0):
+    """Q/K whose observation rows are known in closed form.
+
+    Every key of block j in KV group g equals (ln w[g, j] / sigma) * e_j, and
+    every probe query of head h equals beta_h * (1, ..., 1).  Then the probe
+    logit of block j is beta_h * ln w[g(h), j], so the observation row of
+    segment s is w[g, :C_B(s)]**beta_h normalised, whatever the probe length.
+    Non-probe queries hold large random values that must be ignored."""
+    rng = np.random.default_rng(seed)
+    sigma = 1.0 / math.sqrt(D)
+    CB = N // LB
+    w = rng.uniform(0.5, 3.0, size=(HKV, CB))
+    K = np.zeros((HKV, N, D))
+    for g in range(HKV):
+        for j in range(CB):
+            K[g, j * LB:(j + 1) * LB, j] = math.log(w[g, j]) / sigma
+    beta = np.array([1.0, 0.5, 2.0, 1.5])
+    Q = 50.0 * rng.standard_normal((HQ, N, D))
+    for h in range(HQ):
+        for s in range(N // LS):
+            Q[h, (s + 1) * LS - P:(s + 1) * LS] = beta[h]
+    return Q, K, w, beta
+
+
+def test_pool_mean_constant_blocks():
+    rng = np.random.default_rng(0)
+    vals = rng.standard_normal((HKV, N // LB, D))
+    K = np.repeat(vals, LB, axis=1)
+    np.testing.assert_allclose(O.pool_mean(K, LB), vals, atol=1e-14)
+
+
+def test_pool_mean_brute_force():
+    rng = np.random.default_rng(1)
+    K = rng.standard_normal((HKV, N, D))
+    ref = np.zeros((HKV, N // LB, D))
+    for g in range(HKV):
+        for j in range(N // LB):
+            acc = np.zeros(D)
+            for t in range(j * LB, (j + 1) * LB):
+                acc += K[g, t]
+            ref[g, j] = acc / LB
+    np.testing.assert_allclose(O.pool_mean(K, LB), ref, atol=1e-13)
+
+
+def test_observation_rows_closed_form():
+    Q, K, w, beta = _designed_inputs()
+    abar = O.observation_rows(Q, K, LS, LB, P)
+    r = HQ // HKV
+    for h in range(HQ):
+        for s in range(N // LS):
+            cb = (s + 1) * LS // LB
+            expect = w[h // r, :cb] ** beta[h]
+            expect = expect / expect.sum()
+            np.testing.assert_allclose(abar[h, s, :cb], expect, atol=1e-12)
+            assert np.all(abar[h, s, cb:] == -1.0)
+            assert abs(abar[h, s, :cb].sum() - 1.0) < 1e-12
+
+
+def test_observation_rows_use_only_last_probe_rows():
+    Q, K, _, _ = _designed_inputs()
+    a1 = O.observation_rows(Q, K, LS, LB, P)
+    Q2 = Q.copy()
+    for s in range(N // LS):
+        Q2[:, s * LS:(s + 1) * LS - P] *= -3.0     # change every non-probe query
+    a2 = O.observation_rows(Q2, K, LS, LB, P)
+    np.testing.assert_array_equal(a1, a2)
+
+
+def test_identical_keys_give_uniform_rows_and_log_entropy():
+    rng = np.random.default_rng(4)
+    Q = rng.standard_normal((HQ, N, D))
+    K = np.tile(rng.standard_normal(D), (HKV, N, 1))
+    abar, E = O.entropy_score(Q, K, LS, LB, P)
+    for s in range(N // LS):
+        cb = (s + 1) * LS // LB
+        np.testing.assert_allclose(abar[:, s, :cb], 1.0 / cb, atol=1e-14)
+        np.testing.assert_allclose(E[:, s], math.log(cb), atol=1e-12)
+    _, E2 = O.entropy_score(Q, K, LS, LB, P, kind=O.RENYI, alpha=2.0)
+    for s in range(N // LS):
+        np.testing.assert_allclose(E2[:, s], math.log((s + 1) * LS // LB), atol=1e-12)
+
+
+def test_entropy_of_designed_rows():
+    Q, K, w, beta = _designed_inputs()
+    _, E = O.entropy_score(Q, K, LS, LB, P)
+    _, E2 = O.entropy_score(Q, K, LS, LB, P, kind=O.RENYI, alpha=2.0)
+    r = HQ // HKV
+    for h in range(HQ):
+        for s in range(N // LS):
+            cb = (s + 1) * LS // LB
+            p = w[h // r, :cb] ** beta[h]
+            p /= p.sum()
+            assert abs(E[h, s] + sum(x * math.log(x) for x in p)) < 1e-12
+            assert abs(E2[h, s] + math.log(sum(x * x for x in p))) < 1e-12
+
+
+def test_maxmin_mode_reduces_to_mean_probe_on_constant_chunks():
+    # Alg. 1-2 of EntropyInfer: with queries constant over each segment and keys
+    # constant over each block, max == min, so S1 = S2 = S3 = S4 and A_obs is
+    # the same softmax row that the mean probe produces.
+    rng = np.random.default_rng(5)
+    qv = rng.standard_normal((HQ, N // LS, D))
+    kv = rng.standard_normal((HKV, N // LB, D))
+    Q = np.repeat(qv, LS, axis=1)
+    K = np.repeat(kv, LB, axis=1)
+    a_mm = O.observation_rows_maxmin(Q, K, LS, LB)
+    a_mp = O.observation_rows(Q, K, LS, LB, P)
+    np.testing.assert_allclose(a_mm, a_mp, atol=1e-13)
+
+
+def test_maxmin_mode_sums_to_one_and_is_causal():
+    rng = np.random.default_rng(6)
+    Q = rng.standard_normal((HQ, N, D))
+    K = rng.standard_normal((HKV, N, D))
+    a = O.observation_rows_maxmin(Q, K, LS, LB)
+    for s in range(N // LS):
+        cb = (s + 1) * LS // LB
+        np.testing.assert_allclose(a[:, s, :cb].sum(axis=1), 1.0, atol=1e-12)
+        assert np.all(a[:, s, cb:] == -1.0)
+
+
+def test_planted_structure_tiny_workload():
+    cfg = synth.PREFILL_CONFIGS["tiny-2k-f32"]
+    inp = synth.make_prefill(cfg, seed=0)
+    abar, E = O.entropy_score(inp.q, inp.k, cfg.segment_size, cfg.block_size, cfg.probe_len)
+    for h in range(cfg.n_q_heads):
+        if inp.rigid_hs[h, 0]:
+            assert E[h].max() < 1e-3
+        else:
+            assert np.all(np.abs(E[h] - math.log(2)) < 0.1), E[h]
+            for s in range(cfg.n_segments):
+                top2 = set(np.argsort(-abar[h, s])[:2].tolist())
+                assert top2 == set(inp.hot_blocks[(h, s)].tolist())
+
+
+def test_planted_structure_eight_hot_blocks():
+    cfg = synth.small_prefill_config(n_q_heads=8, n_kv_heads=2, head_dim=128,
+                                     seq_len=8192, block_size=128, segment_size=2048,
+                                     head_types="fraction", hot_count="8",
+                                     hot_dist="zipf1.2")
+    inp = synth.make_prefill(cfg, seed=1)
+    _, E = O.entropy_score(inp.q, inp.k, cfg.segment_size, cfg.block_size, cfg.probe_len)
+    for h in range(cfg.n_q_heads):
+        if inp.rigid_hs[h, 0]:
+            assert E[h].max() < 1e-3
+        else:
+            assert np.all(np.abs(E[h] - math.log(8)) < 0.15), E[h]
