@@ -1,0 +1,292 @@
+"""Python entry points with the same names as the C ABI (include/egs.h).
+
+Each function checks tensor placement / dtype / contiguity, allocates the
+outputs and workspace with torch (device memory plumbing), and calls the
+library on torch's current stream.  Nothing is computed here.
+"""
+from __future__ import annotations
+
+import ctypes
+import dataclasses
+from typing import Optional
+
+import torch
+
+from . import _lib as L
+
+__all__ = [
+    "PrefillShape", "BudgetPolicy", "DecodeShape", "RetainParams",
+    "entropy_score", "allocate_budget", "select_blocks", "sparse_prefill_attn",
+    "kv_retain", "sparse_decode_attn", "kv_retain_total",
+]
+
+_DT = {torch.bfloat16: L.EGS_BF16, torch.float32: L.EGS_F32}
+
+
+@dataclasses.dataclass
+class PrefillShape:
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    seq_len: int
+    block_size: int
+    segment_size: int
+    probe_len: int
+    dtype: torch.dtype = torch.bfloat16
+    sm_scale: float = 0.0
+
+    @property
+    def n_blocks(self) -> int:
+        return self.seq_len // self.block_size
+
+    @property
+    def n_segments(self) -> int:
+        return self.seq_len // self.segment_size
+
+    def c(self) -> L.PrefillShapeC:
+        return L.PrefillShapeC(self.n_q_heads, self.n_kv_heads, self.head_dim, self.seq_len,
+                               self.block_size, self.segment_size, self.probe_len,
+                               _DT[self.dtype], self.sm_scale)
+
+
+@dataclasses.dataclass
+class BudgetPolicy:
+    mode: int = L.EGS_BUDGET_FIXED
+    frac: float = 0.25
+    frac_rigid: float = 0.05
+    frac_dynamic: float = 0.30
+    frac_min: float = 0.02
+    frac_max: float = 0.50
+    entropy_threshold: float = 0.5
+    base_tokens: float = 2048.0
+    alg3_alpha: float = 0.5
+    alg3_delta_t: float = 0.4
+
+    def c(self) -> L.BudgetPolicyC:
+        return L.BudgetPolicyC(self.mode, self.frac, self.frac_rigid, self.frac_dynamic,
+                               self.frac_min, self.frac_max, self.entropy_threshold,
+                               self.base_tokens, self.alg3_alpha, self.alg3_delta_t)
+
+
+@dataclasses.dataclass
+class DecodeShape:
+    batch: int
+    n_q_heads: int
+    n_kv_heads: int
+    head_dim: int
+    cache_len: int
+    n_obs: int
+    n_sink: int
+    n_recent: int
+    n_keep: int
+    dtype: torch.dtype = torch.bfloat16
+    sm_scale: float = 0.0
+
+    def c(self) -> L.DecodeShapeC:
+        return L.DecodeShapeC(self.batch, self.n_q_heads, self.n_kv_heads, self.head_dim,
+                              self.cache_len, self.n_obs, self.n_sink, self.n_recent,
+                              self.n_keep, _DT[self.dtype], self.sm_scale)
+
+
+@dataclasses.dataclass
+class RetainParams:
+    entropy_kind: int = L.EGS_SHANNON
+    renyi_alpha: float = 2.0
+    zeta: float = 0.5
+    tau: float = 1.0
+    raw_logit_mode: int = 0
+    info_alpha: float = 1.0
+
+    def c(self) -> L.RetainParamsC:
+        return L.RetainParamsC(self.entropy_kind, self.renyi_alpha, self.zeta, self.tau,
+                               self.raw_logit_mode, self.info_alpha)
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(device: torch.device):
+    return ctypes.c_void_p(torch.cuda.current_stream(device).cuda_stream)
+
+
+def _need(t: torch.Tensor, name: str, shape, dtype, device=None):
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if t.device.type != "cuda":
+        raise ValueError(f"{name} must be on a HIP device")
+    if device is not None and t.device != device:
+        raise ValueError(f"{name} is on {t.device}, expected {device}")
+    if tuple(t.shape) != tuple(shape):
+        raise ValueError(f"{name} has shape {tuple(t.shape)}, expected {tuple(shape)}")
+    if t.dtype != dtype:
+        raise ValueError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+
+
+def _empty(shape, dtype, device):
+    return torch.empty(shape, dtype=dtype, device=device)
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    # torch's caching allocator returns >= 512-byte aligned blocks
+    return torch.empty(max(int(nbytes), 256), dtype=torch.uint8, device=device)
+
+
+# ----------------------------------------------------------------------------
+# prefill path
+# ----------------------------------------------------------------------------
+def entropy_score(shape: PrefillShape, q: torch.Tensor, k: torch.Tensor, kind: int = L.EGS_SHANNON,
+                  renyi_alpha: float = 2.0, pool: int = L.EGS_POOL_MEAN_PROBE,
+                  block_scores: Optional[torch.Tensor] = None,
+                  entropy: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None):
+    """Observation rows a_bar [Hq, C_S, C_B] and entropy E [Hq, C_S]."""
+    s = shape
+    dev = q.device
+    _need(q, "q", (s.n_q_heads, s.seq_len, s.head_dim), s.dtype)
+    _need(k, "k", (s.n_kv_heads, s.seq_len, s.head_dim), s.dtype, dev)
+    sc = s.c()
+    if block_scores is None:
+        block_scores = _empty((s.n_q_heads, s.n_segments, s.n_blocks), torch.float32, dev)
+    if entropy is None:
+        entropy = _empty((s.n_q_heads, s.n_segments), torch.float32, dev)
+    _need(block_scores, "block_scores", (s.n_q_heads, s.n_segments, s.n_blocks), torch.float32, dev)
+    _need(entropy, "entropy", (s.n_q_heads, s.n_segments), torch.float32, dev)
+    wsb = L.LIB.egs_entropy_score_workspace(ctypes.byref(sc))
+    if workspace is None:
+        workspace = _workspace(wsb, dev)
+    L.check(L.LIB.egs_entropy_score(ctypes.byref(sc), pool, kind, renyi_alpha, _ptr(q), _ptr(k),
+                                    _ptr(block_scores), _ptr(entropy), _ptr(workspace),
+                                    workspace.numel(), _stream(dev)))
+    return block_scores, entropy
+
+
+def allocate_budget(shape: PrefillShape, policy: BudgetPolicy, entropy: torch.Tensor,
+                    head_is_rigid: Optional[torch.Tensor] = None,
+                    budget: Optional[torch.Tensor] = None):
+    """Head classes [Hq] int8 and budgets [Hq, C_S] int32 (in blocks)."""
+    s = shape
+    dev = entropy.device
+    _need(entropy, "entropy", (s.n_q_heads, s.n_segments), torch.float32)
+    if head_is_rigid is None:
+        head_is_rigid = _empty((s.n_q_heads,), torch.int8, dev)
+    if budget is None:
+        budget = _empty((s.n_q_heads, s.n_segments), torch.int32, dev)
+    _need(head_is_rigid, "head_is_rigid", (s.n_q_heads,), torch.int8, dev)
+    _need(budget, "budget", (s.n_q_heads, s.n_segments), torch.int32, dev)
+    sc, pc = s.c(), policy.c()
+    L.check(L.LIB.egs_allocate_budget(ctypes.byref(sc), ctypes.byref(pc), _ptr(entropy),
+                                      _ptr(head_is_rigid), _ptr(budget), _stream(dev)))
+    return head_is_rigid, budget
+
+
+def select_blocks(shape: PrefillShape, block_scores: torch.Tensor, budget: torch.Tensor,
+                  k_max: int, block_idx: Optional[torch.Tensor] = None,
+                  block_cnt: Optional[torch.Tensor] = None):
+    """Selected block lists [Hq, C_S, k_max] (ascending, -1 padded) and counts."""
+    s = shape
+    dev = block_scores.device
+    _need(block_scores, "block_scores", (s.n_q_heads, s.n_segments, s.n_blocks), torch.float32)
+    _need(budget, "budget", (s.n_q_heads, s.n_segments), torch.int32, dev)
+    if block_idx is None:
+        block_idx = _empty((s.n_q_heads, s.n_segments, k_max), torch.int32, dev)
+    if block_cnt is None:
+        block_cnt = _empty((s.n_q_heads, s.n_segments), torch.int32, dev)
+    _need(block_idx, "block_idx", (s.n_q_heads, s.n_segments, k_max), torch.int32, dev)
+    _need(block_cnt, "block_cnt", (s.n_q_heads, s.n_segments), torch.int32, dev)
+    sc = s.c()
+    L.check(L.LIB.egs_select_blocks(ctypes.byref(sc), _ptr(block_scores), _ptr(budget), k_max,
+                                    _ptr(block_idx), _ptr(block_cnt), _stream(dev)))
+    return block_idx, block_cnt
+
+
+def sparse_prefill_attn(shape: PrefillShape, q, k, v, block_idx, block_cnt,
+                        out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
+                        return_lse: bool = False):
+    """Block-sparse causal GQA attention output [Hq, N, d] (and lse [Hq, N])."""
+    s = shape
+    dev = q.device
+    _need(q, "q", (s.n_q_heads, s.seq_len, s.head_dim), s.dtype)
+    _need(k, "k", (s.n_kv_heads, s.seq_len, s.head_dim), s.dtype, dev)
+    _need(v, "v", (s.n_kv_heads, s.seq_len, s.head_dim), s.dtype, dev)
+    k_max = block_idx.shape[-1]
+    _need(block_idx, "block_idx", (s.n_q_heads, s.n_segments, k_max), torch.int32, dev)
+    _need(block_cnt, "block_cnt", (s.n_q_heads, s.n_segments), torch.int32, dev)
+    if out is None:
+        out = _empty((s.n_q_heads, s.seq_len, s.head_dim), s.dtype, dev)
+    _need(out, "out", (s.n_q_heads, s.seq_len, s.head_dim), s.dtype, dev)
+    if return_lse and lse is None:
+        lse = _empty((s.n_q_heads, s.seq_len), torch.float32, dev)
+    if lse is not None:
+        _need(lse, "lse", (s.n_q_heads, s.seq_len), torch.float32, dev)
+    sc = s.c()
+    L.check(L.LIB.egs_sparse_prefill_attn(ctypes.byref(sc), _ptr(q), _ptr(k), _ptr(v),
+                                          _ptr(block_idx), _ptr(block_cnt), k_max, _ptr(out),
+                                          _ptr(lse), _stream(dev)))
+    return (out, lse) if (return_lse or lse is not None) else out
+
+
+# ----------------------------------------------------------------------------
+# decode path
+# ----------------------------------------------------------------------------
+def kv_retain_total(shape: DecodeShape) -> int:
+    sc = shape.c()
+    n = L.LIB.egs_kv_retain_total(ctypes.byref(sc))
+    if n < 0:
+        raise L.EgsError(L.EGS_EINVAL, L.LIB.egs_last_error().decode())
+    return n
+
+
+def kv_retain(shape: DecodeShape, params: RetainParams, q_obs, k_cache, v_cache,
+              token_entropy: Optional[torch.Tensor] = None, gather: bool = True,
+              want_head_entropy: bool = True, want_scores: bool = False,
+              workspace: Optional[torch.Tensor] = None):
+    """Returns dict(keep_idx, k_out, v_out, head_entropy, scores)."""
+    s = shape
+    dev = q_obs.device
+    _need(q_obs, "q_obs", (s.batch, s.n_q_heads, s.n_obs, s.head_dim), s.dtype)
+    _need(k_cache, "k_cache", (s.batch, s.n_kv_heads, s.cache_len, s.head_dim), s.dtype, dev)
+    if gather:
+        _need(v_cache, "v_cache", (s.batch, s.n_kv_heads, s.cache_len, s.head_dim), s.dtype, dev)
+    if token_entropy is not None:
+        _need(token_entropy, "token_entropy", (s.batch, s.cache_len), torch.float32, dev)
+    n_total = kv_retain_total(s)
+    keep = _empty((s.batch, s.n_kv_heads, n_total), torch.int32, dev)
+    k_out = _empty((s.batch, s.n_kv_heads, n_total, s.head_dim), s.dtype, dev) if gather else None
+    v_out = _empty((s.batch, s.n_kv_heads, n_total, s.head_dim), s.dtype, dev) if gather else None
+    he = _empty((s.batch, s.n_q_heads), torch.float32, dev) if want_head_entropy else None
+    sco = _empty((s.batch, s.n_kv_heads, s.cache_len), torch.float32, dev) if want_scores else None
+    sc, pc = s.c(), params.c()
+    wsb = L.LIB.egs_kv_retain_workspace(ctypes.byref(sc))
+    if workspace is None:
+        workspace = _workspace(wsb, dev)
+    L.check(L.LIB.egs_kv_retain(ctypes.byref(sc), ctypes.byref(pc), _ptr(q_obs), _ptr(k_cache),
+                                _ptr(v_cache), _ptr(token_entropy), _ptr(keep), _ptr(k_out),
+                                _ptr(v_out), _ptr(he), _ptr(sco), _ptr(workspace),
+                                workspace.numel(), _stream(dev)))
+    return {"keep_idx": keep, "k_out": k_out, "v_out": v_out, "head_entropy": he,
+            "scores": sco}
+
+
+def sparse_decode_attn(shape: DecodeShape, q_new, k_kept, v_kept,
+                       out: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None):
+    s = shape
+    dev = q_new.device
+    n_total = k_kept.shape[2]
+    _need(q_new, "q_new", (s.batch, s.n_q_heads, s.head_dim), s.dtype)
+    _need(k_kept, "k_kept", (s.batch, s.n_kv_heads, n_total, s.head_dim), s.dtype, dev)
+    _need(v_kept, "v_kept", (s.batch, s.n_kv_heads, n_total, s.head_dim), s.dtype, dev)
+    if out is None:
+        out = _empty((s.batch, s.n_q_heads, s.head_dim), s.dtype, dev)
+    _need(out, "out", (s.batch, s.n_q_heads, s.head_dim), s.dtype, dev)
+    sc = s.c()
+    wsb = L.LIB.egs_sparse_decode_attn_workspace(ctypes.byref(sc), n_total)
+    if workspace is None:
+        workspace = _workspace(wsb, dev)
+    L.check(L.LIB.egs_sparse_decode_attn(ctypes.byref(sc), _ptr(q_new), _ptr(k_kept),
+                                         _ptr(v_kept), n_total, _ptr(out), _ptr(workspace),
+                                         workspace.numel(), _stream(dev)))
+    return out

@@ -1,0 +1,380 @@
+// C ABI entry points: host-side validation, workspace sizing and dispatch to
+// the HIP kernels.  Nothing here allocates device memory or synchronizes.
+#include <cmath>
+#include <cstdarg>
+#include <cstdio>
+#include <cstring>
+#include <string>
+
+#include "egs_launch.h"
+
+using egs::DecodeDims;
+using egs::PrefillDims;
+
+namespace {
+
+thread_local std::string g_last_error;
+
+egs_status fail(egs_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+egs_status ok() {
+  return EGS_OK;
+}
+
+egs_status hip_status(hipError_t e, const char* what) {
+  if (e == hipSuccess) return EGS_OK;
+  return fail(EGS_EHIP, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool aligned(const void* p, size_t a) {
+  return (reinterpret_cast<uintptr_t>(p) % a) == 0;
+}
+
+constexpr size_t kWsAlign = 256;
+size_t round_up(size_t x, size_t a) {
+  return (x + a - 1) / a * a;
+}
+
+bool supported_head_dim(int d) {
+  return d == 16 || d == 32 || d == 64 || d == 128;
+}
+
+egs_status check_prefill(const egs_prefill_shape* s, PrefillDims* p) {
+  if (s == nullptr) return fail(EGS_EINVAL, "prefill shape is NULL");
+  if (s->n_q_heads <= 0 || s->n_kv_heads <= 0 || s->head_dim <= 0 || s->seq_len <= 0 ||
+      s->block_size <= 0 || s->segment_size <= 0 || s->probe_len <= 0)
+    return fail(EGS_EINVAL, "prefill shape has a non-positive field");
+  if (s->n_q_heads % s->n_kv_heads != 0)
+    return fail(EGS_EINVAL, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)",
+                s->n_q_heads, s->n_kv_heads);
+  if (s->seq_len % s->segment_size != 0)
+    return fail(EGS_EINVAL, "seq_len (%d) is not a multiple of segment_size (%d)", s->seq_len,
+                s->segment_size);
+  if (s->segment_size % s->block_size != 0)
+    return fail(EGS_EINVAL, "segment_size (%d) is not a multiple of block_size (%d)",
+                s->segment_size, s->block_size);
+  if (s->probe_len > s->segment_size)
+    return fail(EGS_EINVAL, "probe_len (%d) exceeds segment_size (%d)", s->probe_len,
+                s->segment_size);
+  if (s->dtype != EGS_BF16 && s->dtype != EGS_F32)
+    return fail(EGS_EINVAL, "unknown dtype %d", s->dtype);
+  if (!(std::isfinite(s->sm_scale) && s->sm_scale >= 0.f))
+    return fail(EGS_EINVAL, "sm_scale must be finite and >= 0");
+  if (!supported_head_dim(s->head_dim))
+    return fail(EGS_ENOTSUP, "head_dim %d not supported (16, 32, 64, 128)", s->head_dim);
+  if (s->block_size % 16 != 0 || s->block_size > 256)
+    return fail(EGS_ENOTSUP, "block_size %d not supported (multiple of 16, <= 256)",
+                s->block_size);
+  const long long CB = s->seq_len / s->block_size;
+  if (CB > 16384) return fail(EGS_ENOTSUP, "more than 16384 key blocks (%lld)", CB);
+  const long long elems = (long long)s->n_q_heads * s->seq_len * s->head_dim;
+  if (elems > (1LL << 40)) return fail(EGS_ENOTSUP, "tensor too large");
+  p->Hq = s->n_q_heads;
+  p->Hkv = s->n_kv_heads;
+  p->r = s->n_q_heads / s->n_kv_heads;
+  p->D = s->head_dim;
+  p->N = s->seq_len;
+  p->LB = s->block_size;
+  p->LS = s->segment_size;
+  p->P = s->probe_len;
+  p->CS = s->seq_len / s->segment_size;
+  p->CB = (int)CB;
+  p->dtype = s->dtype;
+  p->sm_scale = s->sm_scale > 0.f ? s->sm_scale : 1.0f / std::sqrt((float)s->head_dim);
+  return EGS_OK;
+}
+
+size_t kbar_plane_bytes(const PrefillDims& p) {
+  return round_up((size_t)p.Hkv * p.CB * p.D * 2, kWsAlign);
+}
+
+egs_status need(const void* ptr, const char* name, size_t align) {
+  if (ptr == nullptr) return fail(EGS_EINVAL, "%s is NULL", name);
+  if (!aligned(ptr, align)) return fail(EGS_EINVAL, "%s is not %zu-byte aligned", name, align);
+  return EGS_OK;
+}
+
+egs_status check_decode(const egs_decode_shape* s, DecodeDims* p) {
+  if (s == nullptr) return fail(EGS_EINVAL, "decode shape is NULL");
+  if (s->batch <= 0 || s->n_q_heads <= 0 || s->n_kv_heads <= 0 || s->head_dim <= 0 ||
+      s->cache_len <= 0 || s->n_obs <= 0)
+    return fail(EGS_EINVAL, "decode shape has a non-positive field");
+  if (s->n_sink < 0 || s->n_recent < 0 || s->n_keep < 0)
+    return fail(EGS_EINVAL, "n_sink, n_recent and n_keep must be >= 0");
+  if (s->n_q_heads % s->n_kv_heads != 0)
+    return fail(EGS_EINVAL, "n_q_heads (%d) is not a multiple of n_kv_heads (%d)",
+                s->n_q_heads, s->n_kv_heads);
+  if (s->n_obs > s->cache_len)
+    return fail(EGS_EINVAL, "n_obs (%d) exceeds cache_len (%d)", s->n_obs, s->cache_len);
+  if (!(std::isfinite(s->sm_scale) && s->sm_scale >= 0.f))
+    return fail(EGS_EINVAL, "sm_scale must be finite and >= 0");
+  if (s->dtype != EGS_BF16 && s->dtype != EGS_F32)
+    return fail(EGS_EINVAL, "unknown dtype %d", s->dtype);
+  if (s->dtype != EGS_BF16) return fail(EGS_ENOTSUP, "decode retention supports bf16 only");
+  if (s->head_dim != 64 && s->head_dim != 128)
+    return fail(EGS_ENOTSUP, "decode head_dim %d not supported (64, 128)", s->head_dim);
+  if (s->cache_len > (1 << 26)) return fail(EGS_ENOTSUP, "cache_len above 2^26");
+  if (s->n_q_heads / s->n_kv_heads > 16)
+    return fail(EGS_ENOTSUP, "more than 16 query heads per KV head");
+  p->B = s->batch;
+  p->Hq = s->n_q_heads;
+  p->Hkv = s->n_kv_heads;
+  p->r = s->n_q_heads / s->n_kv_heads;
+  p->D = s->head_dim;
+  p->L = s->cache_len;
+  p->W = s->n_obs;
+  p->n_sink = s->n_sink;
+  p->n_recent = s->n_recent;
+  p->n_keep = s->n_keep;
+  const long long tot = (long long)s->n_sink + s->n_recent + s->n_keep;
+  p->n_total = tot >= s->cache_len ? s->cache_len : (int)tot;
+  p->dtype = s->dtype;
+  p->sm_scale = s->sm_scale > 0.f ? s->sm_scale : 1.0f / std::sqrt((float)s->head_dim);
+  return EGS_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t egs_abi_version(void) {
+  return EGS_ABI_VERSION;
+}
+
+const char* egs_status_string(egs_status st) {
+  switch (st) {
+    case EGS_OK: return "EGS_OK";
+    case EGS_EINVAL: return "EGS_EINVAL: invalid argument";
+    case EGS_ENOTSUP: return "EGS_ENOTSUP: unsupported shape or mode";
+    case EGS_EWORKSPACE: return "EGS_EWORKSPACE: workspace too small";
+    case EGS_EHIP: return "EGS_EHIP: HIP launch failure";
+  }
+  return "unknown egs_status";
+}
+
+const char* egs_last_error(void) {
+  return g_last_error.c_str();
+}
+
+size_t egs_entropy_score_workspace(const egs_prefill_shape* shape) {
+  PrefillDims p;
+  if (check_prefill(shape, &p) != EGS_OK) return 0;
+  return 2 * kbar_plane_bytes(p);
+}
+
+egs_status egs_entropy_score(const egs_prefill_shape* shape, int32_t pool_kind,
+                             int32_t entropy_kind, float renyi_alpha, const void* q,
+                             const void* k, float* block_scores, float* entropy,
+                             void* workspace, size_t workspace_bytes, hipStream_t stream) {
+  PrefillDims p;
+  egs_status st = check_prefill(shape, &p);
+  if (st != EGS_OK) return st;
+  if (pool_kind == EGS_POOL_MAXMIN)
+    return fail(EGS_ENOTSUP, "EGS_POOL_MAXMIN is not available on the GPU path");
+  if (pool_kind != EGS_POOL_MEAN_PROBE) return fail(EGS_EINVAL, "unknown pool_kind %d", pool_kind);
+  int kind = entropy_kind;
+  if (kind != EGS_SHANNON && kind != EGS_RENYI)
+    return fail(EGS_EINVAL, "unknown entropy_kind %d", entropy_kind);
+  if (kind == EGS_RENYI) {
+    if (!(std::isfinite(renyi_alpha) && renyi_alpha > 0.f))
+      return fail(EGS_EINVAL, "renyi_alpha must be finite and > 0");
+    if (renyi_alpha == 1.0f) kind = EGS_SHANNON;
+  }
+  if ((st = need(q, "q", 16)) != EGS_OK) return st;
+  if ((st = need(k, "k", 16)) != EGS_OK) return st;
+  if ((st = need(block_scores, "block_scores", 4)) != EGS_OK) return st;
+  if ((st = need(entropy, "entropy", 4)) != EGS_OK) return st;
+  if ((st = need(workspace, "workspace", kWsAlign)) != EGS_OK) return st;
+  const size_t plane = kbar_plane_bytes(p);
+  if (workspace_bytes < 2 * plane)
+    return fail(EGS_EWORKSPACE, "workspace of %zu bytes is below the %zu required",
+                workspace_bytes, 2 * plane);
+  char* ws = static_cast<char*>(workspace);
+  hipError_t e = egs::launch_pool_keys(p, k, ws, ws + plane, stream);
+  if (e != hipSuccess) return hip_status(e, "pool_keys launch");
+  e = egs::launch_probe_score(p, q, ws, ws + plane, kind, renyi_alpha, block_scores, entropy,
+                              stream);
+  return hip_status(e, "probe_score launch");
+}
+
+egs_status egs_allocate_budget(const egs_prefill_shape* shape, const egs_budget_policy* policy,
+                               const float* entropy, int8_t* head_is_rigid, int32_t* budget,
+                               hipStream_t stream) {
+  PrefillDims p;
+  egs_status st = check_prefill(shape, &p);
+  if (st != EGS_OK) return st;
+  if (policy == nullptr) return fail(EGS_EINVAL, "policy is NULL");
+  const egs_budget_policy& pol = *policy;
+  if (pol.mode < EGS_BUDGET_FIXED || pol.mode > EGS_BUDGET_ALG3)
+    return fail(EGS_EINVAL, "unknown budget mode %d", pol.mode);
+  if (!std::isfinite(pol.entropy_threshold))
+    return fail(EGS_EINVAL, "entropy_threshold must be finite");
+  switch (pol.mode) {
+    case EGS_BUDGET_FIXED:
+      if (!(std::isfinite(pol.frac) && pol.frac >= 0.0)) return fail(EGS_EINVAL, "frac must be >= 0");
+      break;
+    case EGS_BUDGET_TWO_LEVEL:
+      if (!(std::isfinite(pol.frac_rigid) && pol.frac_rigid >= 0.0 &&
+            std::isfinite(pol.frac_dynamic) && pol.frac_dynamic >= 0.0))
+        return fail(EGS_EINVAL, "frac_rigid and frac_dynamic must be >= 0");
+      break;
+    case EGS_BUDGET_PROPORTIONAL:
+      if (!(std::isfinite(pol.frac_min) && std::isfinite(pol.frac_max) && pol.frac_min >= 0.0 &&
+            pol.frac_max >= pol.frac_min))
+        return fail(EGS_EINVAL, "need 0 <= frac_min <= frac_max");
+      break;
+    case EGS_BUDGET_ALG3:
+      if (!(std::isfinite(pol.base_tokens) && pol.base_tokens > 0.0 &&
+            std::isfinite(pol.alg3_alpha) && std::isfinite(pol.alg3_delta_t) &&
+            pol.entropy_threshold > 0.0))
+        return fail(EGS_EINVAL, "ALG3 needs base_tokens > 0, finite alpha / delta_t, e_t > 0");
+      break;
+  }
+  if ((st = need(entropy, "entropy", 4)) != EGS_OK) return st;
+  if ((st = need(head_is_rigid, "head_is_rigid", 1)) != EGS_OK) return st;
+  if ((st = need(budget, "budget", 4)) != EGS_OK) return st;
+  return hip_status(egs::launch_budget(p, pol, entropy, head_is_rigid, budget, stream),
+                    "budget launch");
+}
+
+egs_status egs_select_blocks(const egs_prefill_shape* shape, const float* block_scores,
+                             const int32_t* budget, int32_t k_max, int32_t* block_idx,
+                             int32_t* block_cnt, hipStream_t stream) {
+  PrefillDims p;
+  egs_status st = check_prefill(shape, &p);
+  if (st != EGS_OK) return st;
+  if (k_max < 1 || k_max > p.CB)
+    return fail(EGS_EINVAL, "k_max (%d) must be in [1, C_B = %d]", k_max, p.CB);
+  if ((st = need(block_scores, "block_scores", 4)) != EGS_OK) return st;
+  if ((st = need(budget, "budget", 4)) != EGS_OK) return st;
+  if ((st = need(block_idx, "block_idx", 4)) != EGS_OK) return st;
+  if ((st = need(block_cnt, "block_cnt", 4)) != EGS_OK) return st;
+  return hip_status(egs::launch_select(p, block_scores, budget, k_max, block_idx, block_cnt,
+                                       stream),
+                    "select launch");
+}
+
+egs_status egs_sparse_prefill_attn(const egs_prefill_shape* shape, const void* q, const void* k,
+                                   const void* v, const int32_t* block_idx,
+                                   const int32_t* block_cnt, int32_t k_max, void* out,
+                                   float* lse, hipStream_t stream) {
+  PrefillDims p;
+  egs_status st = check_prefill(shape, &p);
+  if (st != EGS_OK) return st;
+  if (k_max < 1 || k_max > p.CB)
+    return fail(EGS_EINVAL, "k_max (%d) must be in [1, C_B = %d]", k_max, p.CB);
+  if ((st = need(q, "q", 16)) != EGS_OK) return st;
+  if ((st = need(k, "k", 16)) != EGS_OK) return st;
+  if ((st = need(v, "v", 16)) != EGS_OK) return st;
+  if ((st = need(out, "out", 16)) != EGS_OK) return st;
+  if ((st = need(block_idx, "block_idx", 4)) != EGS_OK) return st;
+  if ((st = need(block_cnt, "block_cnt", 4)) != EGS_OK) return st;
+  if (lse != nullptr && !aligned(lse, 4)) return fail(EGS_EINVAL, "lse is not 4-byte aligned");
+  if (out == q || out == k || out == v) return fail(EGS_EINVAL, "out aliases an input");
+  return hip_status(egs::launch_sparse_attn(p, q, k, v, block_idx, block_cnt, k_max, out, lse,
+                                            stream),
+                    "sparse_attn launch");
+}
+
+int32_t egs_kv_retain_total(const egs_decode_shape* shape) {
+  DecodeDims p;
+  if (check_decode(shape, &p) != EGS_OK) return -1;
+  return p.n_total;
+}
+
+size_t egs_kv_retain_workspace(const egs_decode_shape* shape) {
+  DecodeDims p;
+  if (check_decode(shape, &p) != EGS_OK) return 0;
+  return egs::retain_workspace_bytes(p);
+}
+
+egs_status egs_kv_retain(const egs_decode_shape* shape, const egs_retain_params* params,
+                         const void* q_obs, const void* k_cache, const void* v_cache,
+                         const float* token_entropy, int32_t* keep_idx, void* k_out,
+                         void* v_out, float* head_entropy, float* scores, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  DecodeDims p;
+  egs_status st = check_decode(shape, &p);
+  if (st != EGS_OK) return st;
+  if (params == nullptr) return fail(EGS_EINVAL, "params is NULL");
+  egs_retain_params prm = *params;
+  if (prm.raw_logit_mode != 0 && prm.raw_logit_mode != 1)
+    return fail(EGS_EINVAL, "raw_logit_mode must be 0 or 1");
+  if (!prm.raw_logit_mode) {
+    if (prm.entropy_kind != EGS_SHANNON && prm.entropy_kind != EGS_RENYI)
+      return fail(EGS_EINVAL, "unknown entropy_kind %d", prm.entropy_kind);
+    if (prm.entropy_kind == EGS_RENYI) {
+      if (!(std::isfinite(prm.renyi_alpha) && prm.renyi_alpha > 0.f))
+        return fail(EGS_EINVAL, "renyi_alpha must be finite and > 0");
+      if (prm.renyi_alpha == 1.0f) prm.entropy_kind = EGS_SHANNON;
+    }
+    if (!(prm.zeta > 0.0 && prm.zeta <= 1.0)) return fail(EGS_EINVAL, "zeta must be in (0, 1]");
+    if (!(std::isfinite(prm.tau) && prm.tau > 0.0)) return fail(EGS_EINVAL, "tau must be > 0");
+    if (!(prm.info_alpha >= 0.0 && prm.info_alpha <= 1.0))
+      return fail(EGS_EINVAL, "info_alpha must be in [0, 1]");
+  }
+  if ((st = need(q_obs, "q_obs", 16)) != EGS_OK) return st;
+  if ((st = need(k_cache, "k_cache", 16)) != EGS_OK) return st;
+  if ((st = need(keep_idx, "keep_idx", 4)) != EGS_OK) return st;
+  if ((k_out == nullptr) != (v_out == nullptr))
+    return fail(EGS_EINVAL, "k_out and v_out must both be given or both be NULL");
+  if (k_out != nullptr) {
+    if ((st = need(v_cache, "v_cache", 16)) != EGS_OK) return st;
+    if ((st = need(k_out, "k_out", 16)) != EGS_OK) return st;
+    if ((st = need(v_out, "v_out", 16)) != EGS_OK) return st;
+  }
+  if (token_entropy != nullptr && !aligned(token_entropy, 4))
+    return fail(EGS_EINVAL, "token_entropy is not 4-byte aligned");
+  if (head_entropy != nullptr && !aligned(head_entropy, 4))
+    return fail(EGS_EINVAL, "head_entropy is not 4-byte aligned");
+  if (scores != nullptr && !aligned(scores, 4))
+    return fail(EGS_EINVAL, "scores is not 4-byte aligned");
+  if ((st = need(workspace, "workspace", kWsAlign)) != EGS_OK) return st;
+  const size_t wsb = egs::retain_workspace_bytes(p);
+  if (workspace_bytes < wsb)
+    return fail(EGS_EWORKSPACE, "workspace of %zu bytes is below the %zu required",
+                workspace_bytes, wsb);
+  return hip_status(egs::launch_kv_retain(p, prm, q_obs, k_cache, v_cache, token_entropy,
+                                          keep_idx, k_out, v_out, head_entropy, scores,
+                                          workspace, stream),
+                    "kv_retain launch");
+}
+
+size_t egs_sparse_decode_attn_workspace(const egs_decode_shape* shape, int32_t n_total) {
+  DecodeDims p;
+  if (check_decode(shape, &p) != EGS_OK || n_total < 1) return 0;
+  return egs::decode_attn_workspace_bytes(p, n_total);
+}
+
+egs_status egs_sparse_decode_attn(const egs_decode_shape* shape, const void* q_new,
+                                  const void* k_kept, const void* v_kept, int32_t n_total,
+                                  void* out, void* workspace, size_t workspace_bytes,
+                                  hipStream_t stream) {
+  DecodeDims p;
+  egs_status st = check_decode(shape, &p);
+  if (st != EGS_OK) return st;
+  if (n_total < 1 || n_total > p.L)
+    return fail(EGS_EINVAL, "n_total (%d) must be in [1, cache_len = %d]", n_total, p.L);
+  if ((st = need(q_new, "q_new", 16)) != EGS_OK) return st;
+  if ((st = need(k_kept, "k_kept", 16)) != EGS_OK) return st;
+  if ((st = need(v_kept, "v_kept", 16)) != EGS_OK) return st;
+  if ((st = need(out, "out", 16)) != EGS_OK) return st;
+  if ((st = need(workspace, "workspace", kWsAlign)) != EGS_OK) return st;
+  const size_t wsb = egs::decode_attn_workspace_bytes(p, n_total);
+  if (workspace_bytes < wsb)
+    return fail(EGS_EWORKSPACE, "workspace of %zu bytes is below the %zu required",
+                workspace_bytes, wsb);
+  return hip_status(egs::launch_decode_attn(p, q_new, k_kept, v_kept, n_total, out, workspace,
+                                            stream),
+                    "decode_attn launch");
+}
+
+}  // extern "C"

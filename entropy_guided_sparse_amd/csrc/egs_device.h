@@ -1,0 +1,104 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, MFMA
+// wrappers, conversions and wavefront reductions.  CDNA4 only (wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace egs {
+
+typedef __bf16 bf16;
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x4 __attribute__((ext_vector_type(4)));
+typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef float floatx4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+constexpr int kWave = 64;
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+constexpr float kNegBig = -1.0e30f;   // finite "minus infinity" for running maxima
+
+// D(32x32) += A(32x16) * B(16x32), bf16 inputs, fp32 accumulate.
+// Operand layout (both A and B): lane l holds row/column (l % 32) and the
+// 8 consecutive k-slots of group (l / 32).  Accumulator: lane l holds column
+// (l % 32), register i holds row 8*(i/4) + 4*(l/32) + (i%4).
+__device__ __forceinline__ floatx16 mfma32(bf16x8 a, bf16x8 b, floatx16 c) {
+  return __builtin_amdgcn_mfma_f32_32x32x16_bf16(a, b, c, 0, 0, 0);
+}
+
+__device__ __forceinline__ int acc_row(int i, int lane) {
+  return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
+}
+
+__device__ __forceinline__ float bf2f(bf16 x) { return (float)x; }
+__device__ __forceinline__ bf16 f2bf(float x) { return (bf16)x; }   // RNE
+
+__device__ __forceinline__ bf16x8 load8(const bf16* p) {
+  return *reinterpret_cast<const bf16x8*>(p);
+}
+__device__ __forceinline__ void store8(bf16* p, bf16x8 v) {
+  *reinterpret_cast<bf16x8*>(p) = v;
+}
+
+// Load 8 consecutive elements as floats from bf16 or float storage.
+__device__ __forceinline__ void load8f(const bf16* p, float* out) {
+  bf16x8 v = load8(p);
+#pragma unroll
+  for (int e = 0; e < 8; ++e) out[e] = (float)v[e];
+}
+__device__ __forceinline__ void load8f(const float* p, float* out) {
+  floatx4 a = *reinterpret_cast<const floatx4*>(p);
+  floatx4 b = *reinterpret_cast<const floatx4*>(p + 4);
+#pragma unroll
+  for (int e = 0; e < 4; ++e) { out[e] = a[e]; out[e + 4] = b[e]; }
+}
+
+// Split 8 floats into bf16 hi + lo parts (x ~= hi + lo to ~2^-17 relative).
+__device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
+#pragma unroll
+  for (int e = 0; e < 8; ++e) {
+    bf16 h = (bf16)x[e];
+    hi[e] = h;
+    lo[e] = (bf16)(x[e] - (float)h);
+  }
+}
+
+__device__ __forceinline__ float wave_max(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmaxf(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ float wave_sum(float v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+__device__ __forceinline__ double wave_max_d(double v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = fmax(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ int wave_sum_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  return v;
+}
+// Inclusive prefix sum over the 64 lanes of a wave.
+__device__ __forceinline__ int wave_incl_scan(int v) {
+  const int lane = threadIdx.x & 63;
+#pragma unroll
+  for (int o = 1; o < 64; o <<= 1) {
+    int t = __shfl_up(v, o);
+    if (lane >= o) v += t;
+  }
+  return v;
+}
+
+// Order-preserving map of float bits onto unsigned integers.
+__device__ __forceinline__ uint32_t orderable(float f) {
+  uint32_t u = __float_as_uint(f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+}  // namespace egs

@@ -1,0 +1,56 @@
+// Host-side launcher interface between the C ABI (egs_api.cpp) and the HIP
+// kernels.  Shapes reaching these functions have already been validated.
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/egs.h"
+
+namespace egs {
+
+struct PrefillDims {
+  int Hq, Hkv, r, D, N, LB, LS, P, CS, CB;
+  int dtype;         // egs_dtype
+  float sm_scale;    // resolved (never 0)
+};
+
+struct DecodeDims {
+  int B, Hq, Hkv, r, D, L, W, n_sink, n_recent, n_keep, n_total;
+  int dtype;
+  float sm_scale;
+};
+
+// K1: mean of every key block, written as a bf16 hi/lo pair (kbar ~= hi + lo).
+hipError_t launch_pool_keys(const PrefillDims& p, const void* k, void* kb_hi,
+                            void* kb_lo, hipStream_t st);
+// K2: probe observation rows + per-(head, segment) entropy.
+hipError_t launch_probe_score(const PrefillDims& p, const void* q, const void* kb_hi,
+                              const void* kb_lo, int kind, float alpha,
+                              float* scores, float* entropy, hipStream_t st);
+// K3: head classes and budgets (float64 arithmetic).
+hipError_t launch_budget(const PrefillDims& p, const egs_budget_policy& pol,
+                         const float* entropy, int8_t* rigid, int32_t* budget,
+                         hipStream_t st);
+// K4: top-k block lists.
+hipError_t launch_select(const PrefillDims& p, const float* scores,
+                         const int32_t* budget, int k_max, int32_t* idx,
+                         int32_t* cnt, hipStream_t st);
+// K5: block-sparse causal GQA attention.
+hipError_t launch_sparse_attn(const PrefillDims& p, const void* q, const void* k,
+                              const void* v, const int32_t* idx, const int32_t* cnt,
+                              int k_max, void* out, float* lse, hipStream_t st);
+
+// K6/K7: decode retention.  Workspace layout is owned by retain.hip.
+size_t retain_workspace_bytes(const DecodeDims& p);
+hipError_t launch_kv_retain(const DecodeDims& p, const egs_retain_params& prm,
+                            const void* q_obs, const void* k, const void* v,
+                            const float* token_entropy, int32_t* keep_idx,
+                            void* k_out, void* v_out, float* head_entropy,
+                            float* scores, void* ws, hipStream_t st);
+// K8: decode attention over the kept entries (split over the kept range).
+size_t decode_attn_workspace_bytes(const DecodeDims& p, int n_total);
+hipError_t launch_decode_attn(const DecodeDims& p, const void* q_new, const void* k,
+                              const void* v, int n_total, void* out, void* ws,
+                              hipStream_t st);
+
+}  // namespace egs
