@@ -1,0 +1,323 @@
+#!/usr/bin/env python3
+"""Benchmark of the entropy-guided sparse prefill path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input:
+  prefill layer (Llama-3-8B-shaped, 32/8 heads, d 128, 128k tokens, bf16):
+      entropy_score -> allocate_budget -> select_blocks -> sparse_prefill_attn
+  decode retention (batch 8, 32/8 heads, d 128, 128k-token cache, bf16):
+      kv_retain -> sparse_decode_attn
+Inputs are generated once and are resident in HBM before timing starts.
+
+Prints ONE JSON line.  `value` is the executed-block attention throughput of
+the prefill layer (FLOPs of every listed (head, query block, key block) tile,
+4 * L_B^2 * d each) divided by the prefill layer time (all four calls).
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+
+PEAK_BF16_TFLOPS = 2500.0    # MI355X dense bf16 MFMA
+PEAK_HBM_GBS = 8000.0        # MI355X HBM3E
+
+
+def parse_args():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=10)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--config", default="llama3-8b-128k")
+    ap.add_argument("--entropy", default="shannon", choices=["shannon", "renyi2"])
+    ap.add_argument("--no-decode", action="store_true", help="time the prefill layer only")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=12.0,
+                    help="approximate CPU time spent on the oracle sample")
+    ap.add_argument("--json-out", default=None)
+    return ap.parse_args()
+
+
+def log(msg):
+    print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+
+def prefill_policy(api, cfg):
+    L = api.L
+    if cfg.name == "tiny-2k-f32":
+        return api.BudgetPolicy(mode=L.EGS_BUDGET_FIXED, frac=0.25, entropy_threshold=0.5)
+    if cfg.name == "qwen-64k":
+        return api.BudgetPolicy(mode=L.EGS_BUDGET_PROPORTIONAL, frac_min=0.02, frac_max=0.5,
+                                entropy_threshold=0.5)
+    return api.BudgetPolicy(mode=L.EGS_BUDGET_TWO_LEVEL, frac_rigid=0.05, frac_dynamic=0.30,
+                            entropy_threshold=0.5)
+
+
+def k_max_for(pol, api, CB, LB):
+    L = api.L
+    if pol.mode == L.EGS_BUDGET_FIXED:
+        f = pol.frac
+    elif pol.mode == L.EGS_BUDGET_TWO_LEVEL:
+        f = max(pol.frac_rigid, pol.frac_dynamic)
+    elif pol.mode == L.EGS_BUDGET_PROPORTIONAL:
+        f = pol.frac_max
+    else:
+        return min(CB, int(math.ceil(3 * pol.base_tokens / LB)) + 1)
+    return max(1, min(CB, int(math.ceil(f * CB)) + 1))
+
+
+def executed_tiles(idx, cnt, CS, CB, LB, LS):
+    """Listed (head, query block, key block) tiles incl. the own block, and the
+    same count with the own block's causal half (for the exact-causal figure)."""
+    Hq = cnt.shape[0]
+    bps = LS // LB
+    total = 0
+    for h in range(Hq):
+        for s in range(CS):
+            sel = np.sort(idx[h, s, :cnt[h, s]])
+            b = np.arange(s * bps, (s + 1) * bps)
+            total += int(np.searchsorted(sel, b, side="left").sum()) + len(b)
+    return total
+
+
+def scoring_bytes(cfg, k_max, elt):
+    Hq, Hkv, d, N = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.seq_len
+    CS, CB = cfg.n_segments, cfg.n_blocks
+    return (Hkv * N * d * elt                 # K read once
+            + Hq * CS * cfg.probe_len * d * elt   # probe queries
+            + Hq * CS * CB * 4                # observation rows written
+            + Hq * CS * 4 * 2                 # entropy, budgets
+            + Hq * CS * k_max * 4 + Hq * CS * 4)  # block lists, counts
+
+
+def cpu_baseline(cfg, inp, idx, cnt, seconds):
+    """Oracle attention on a seeded sample of (head, query block) pairs."""
+    sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
+    from oracle import egs_oracle as O
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
+    except Exception:
+        cores = os.cpu_count() or 1
+    rng = np.random.default_rng(0)
+    Hq, CB, LB, LS, d = cfg.n_q_heads, cfg.n_blocks, cfg.block_size, cfg.segment_size, cfg.head_dim
+    flops = 0.0
+    n = 0
+    t0 = time.perf_counter()
+    while time.perf_counter() - t0 < seconds and n < 512:
+        h, b = int(rng.integers(Hq)), int(rng.integers(CB))
+        O.sparse_prefill_attn_rows(inp.q, inp.k, inp.v, idx, cnt, h, b, LS, LB)
+        nblk = len(O.qblock_list(idx, cnt, h, b, LS, LB))
+        flops += 4.0 * LB * LB * d * nblk
+        n += 1
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores),
+            "kind": "oracle",
+            "sample": f"float64 oracle sparse attention on {n} seeded random (head, query-block) "
+                      f"pairs of the same {cfg.name} layer using the GPU's block lists, "
+                      f"{dt:.1f} s; executed-block FLOPs / time"}
+
+
+def main():
+    args = parse_args()
+    if args.gpus != 1 or int(os.environ.get("WORLD_SIZE", "1")) != 1:
+        print("bench.py: this library runs on one GPU; multi-GPU runs are not part of this "
+              "build (the path shards by KV head group with no exchange).", file=sys.stderr)
+        sys.exit(2)
+    import torch
+    from entropy_guided_sparse_amd import api, synth
+    L = api.L
+    dev = torch.device("cuda", 0)
+    torch.cuda.set_device(dev)
+
+    def to_dev(store, dtype):
+        t = torch.from_numpy(np.ascontiguousarray(store))
+        return (t.view(torch.bfloat16) if dtype == "bf16" else t).to(dev)
+
+    # ------------------------------------------------------------------ prefill
+    cfg = synth.PREFILL_CONFIGS[args.config]
+    t0 = time.perf_counter()
+    inp = synth.make_prefill(cfg, seed=0)
+    log(f"generated {cfg.name} in {time.perf_counter() - t0:.1f} s")
+    q, k, v = (to_dev(x, cfg.dtype) for x in (inp.q_store, inp.k_store, inp.v_store))
+    tdt = torch.bfloat16 if cfg.dtype == "bf16" else torch.float32
+    shape = api.PrefillShape(cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.seq_len,
+                             cfg.block_size, cfg.segment_size, cfg.probe_len, tdt)
+    pol = prefill_policy(api, cfg)
+    Hq, CS, CB, LB, LS, d = (cfg.n_q_heads, cfg.n_segments, cfg.n_blocks, cfg.block_size,
+                             cfg.segment_size, cfg.head_dim)
+    k_max = k_max_for(pol, api, CB, LB)
+    kind = L.EGS_SHANNON if args.entropy == "shannon" else L.EGS_RENYI
+    scores = torch.empty((Hq, CS, CB), dtype=torch.float32, device=dev)
+    E = torch.empty((Hq, CS), dtype=torch.float32, device=dev)
+    rigid = torch.empty((Hq,), dtype=torch.int8, device=dev)
+    budget = torch.empty((Hq, CS), dtype=torch.int32, device=dev)
+    idx = torch.empty((Hq, CS, k_max), dtype=torch.int32, device=dev)
+    cnt = torch.empty((Hq, CS), dtype=torch.int32, device=dev)
+    out = torch.empty_like(q)
+    import ctypes
+    sc = shape.c()
+    ws = torch.empty(L.LIB.egs_entropy_score_workspace(ctypes.byref(sc)), dtype=torch.uint8,
+                     device=dev)
+
+    def prefill(evs):
+        evs[0].record()
+        api.entropy_score(shape, q, k, kind=kind, renyi_alpha=2.0, block_scores=scores,
+                          entropy=E, workspace=ws)
+        evs[1].record()
+        api.allocate_budget(shape, pol, E, head_is_rigid=rigid, budget=budget)
+        evs[2].record()
+        api.select_blocks(shape, scores, budget, k_max, block_idx=idx, block_cnt=cnt)
+        evs[3].record()
+        api.sparse_prefill_attn(shape, q, k, v, idx, cnt, out=out)
+        evs[4].record()
+
+    # ------------------------------------------------------------------ decode
+    decode = None
+    if not args.no_decode:
+        dcfg = synth.DECODE_CONFIGS["decode-retain-b8-128k"]
+        t0 = time.perf_counter()
+        dinp = synth.make_decode(dcfg, seed=0)
+        log(f"generated {dcfg.name} in {time.perf_counter() - t0:.1f} s")
+        dq, dk, dv, dqn = (to_dev(x, "bf16") for x in (dinp.q_obs_store, dinp.k_store,
+                                                      dinp.v_store, dinp.q_new_store))
+        del dinp
+        dshape = api.DecodeShape(dcfg.batch, dcfg.n_q_heads, dcfg.n_kv_heads, dcfg.head_dim,
+                                 dcfg.cache_len, dcfg.n_obs, dcfg.n_sink, dcfg.n_recent,
+                                 dcfg.n_keep)
+        prm = api.RetainParams(entropy_kind=L.EGS_SHANNON, zeta=0.5, tau=1.0)
+        dsc = dshape.c()
+        dws = torch.empty(L.LIB.egs_kv_retain_workspace(ctypes.byref(dsc)), dtype=torch.uint8,
+                          device=dev)
+        n_total = api.kv_retain_total(dshape)
+        aws = torch.empty(max(256, L.LIB.egs_sparse_decode_attn_workspace(ctypes.byref(dsc),
+                                                                          n_total)),
+                          dtype=torch.uint8, device=dev)
+        dout = torch.empty_like(dqn)
+        decode = dict(cfg=dcfg, shape=dshape, n_total=n_total)
+
+        def decode_step(evs):
+            res = api.kv_retain(dshape, prm, dq, dk, dv, workspace=dws)
+            evs[5].record()
+            api.sparse_decode_attn(dshape, dqn, res["k_out"], res["v_out"], out=dout,
+                                   workspace=aws)
+            evs[6].record()
+
+    def step(evs):
+        prefill(evs)
+        if decode is not None:
+            decode_step(evs)
+
+    new_events = lambda: [torch.cuda.Event(enable_timing=True) for _ in range(7)]
+    for _ in range(args.warmup):
+        step(new_events())
+    torch.cuda.synchronize()
+
+    # lists are deterministic: count executed tiles once
+    g_idx, g_cnt = idx.cpu().numpy(), cnt.cpu().numpy()
+    tiles = executed_tiles(g_idx, g_cnt, CS, CB, LB, LS)
+    dense_tiles = Hq * CB * (CB + 1) // 2
+    tile_flops = 4.0 * LB * LB * d
+
+    all_evs = [new_events() for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(args.steps):
+        step(all_evs[i])
+    torch.cuda.synchronize()
+    wall = (time.perf_counter() - t0) / args.steps
+
+    def mean_ms(a, b):
+        return float(np.mean([ev[a].elapsed_time(ev[b]) for ev in all_evs]))
+
+    t_score = mean_ms(0, 1)
+    t_budget = mean_ms(1, 2)
+    t_select = mean_ms(2, 3)
+    t_attn = mean_ms(3, 4)
+    t_prefill = mean_ms(0, 4)
+    kernel_us = {"entropy_score": 1e3 * t_score, "allocate_budget": 1e3 * t_budget,
+                 "select_blocks": 1e3 * t_select, "sparse_prefill_attn": 1e3 * t_attn}
+    t_decode = None
+    if decode is not None:
+        kernel_us["kv_retain"] = 1e3 * mean_ms(4, 5)
+        kernel_us["sparse_decode_attn"] = 1e3 * mean_ms(5, 6)
+        t_decode = mean_ms(4, 6)
+
+    elt = 2 if cfg.dtype == "bf16" else 4
+    sbytes = scoring_bytes(cfg, k_max, elt)
+    t_scoring = t_score + t_budget + t_select
+    scoring_gbs = sbytes / (t_scoring * 1e-3) / 1e9
+    exec_flops = tiles * tile_flops
+    attn_tflops = exec_flops / (t_attn * 1e-3) / 1e12
+    eff_tflops = exec_flops / (t_prefill * 1e-3) / 1e12
+    dense_equiv = dense_tiles * tile_flops / (t_prefill * 1e-3) / 1e12
+
+    traffic = None
+    prof = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
+                        "traffic_sparse_attn_llama3-8b-128k.json")
+    if os.path.exists(prof) and cfg.name == "llama3-8b-128k":
+        try:
+            traffic = json.load(open(prof)).get("bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    res = {
+        "metric": "sparse prefill ms/layer + effective TFLOP/s at 128k; scoring-pass GB/s",
+        "value": round(eff_tflops, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(wall * 1e3, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16" if cfg.dtype == "bf16" else "f32",
+        "data": "synthetic",
+        "config": {"workload": f"{cfg.name} prefill layer"
+                               + (" + decode-retain-b8-128k" if decode else ""),
+                   "n_q_heads": Hq, "n_kv_heads": cfg.n_kv_heads, "head_dim": d,
+                   "seq_len": cfg.seq_len, "block_size": LB, "segment_size": LS,
+                   "probe_len": cfg.probe_len, "entropy": args.entropy,
+                   "budget": "two-level 5%/30%, e_t 0.5" if pol.mode == L.EGS_BUDGET_TWO_LEVEL
+                   else str(pol.mode),
+                   "parallelism": "single GPU"},
+        "prefill_ms_per_layer": round(t_prefill, 4),
+        "scoring_pass_us": round(t_scoring * 1e3, 2),
+        "scoring_pass_gbps": round(scoring_gbs, 1),
+        "scoring_pass_bytes": sbytes,
+        "attn_ms": round(t_attn, 4),
+        "attn_tflops_executed": round(attn_tflops, 2),
+        "prefill_tflops_dense_equiv": round(dense_equiv, 2),
+        "executed_tiles": tiles,
+        "dense_causal_tiles": dense_tiles,
+        "tile_density": round(tiles / dense_tiles, 4),
+        "kernel_us": {kk: round(vv, 2) for kk, vv in kernel_us.items()},
+        "roofline": {"bound": "mfma", "achieved": round(attn_tflops, 2),
+                     "peak": PEAK_BF16_TFLOPS, "unit": "TFLOP/s",
+                     "frac": round(attn_tflops / PEAK_BF16_TFLOPS, 4), "traffic": traffic},
+        "scoring_roofline": {"bound": "hbm", "achieved": round(scoring_gbs, 1),
+                             "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                             "frac": round(scoring_gbs / PEAK_HBM_GBS, 4)},
+    }
+    if decode is not None:
+        dc = decode["cfg"]
+        kv_bytes = dc.batch * dc.n_kv_heads * dc.cache_len * dc.head_dim * 2
+        res["decode_ms"] = round(t_decode, 4)
+        res["decode_kv_retain_gbps"] = round(kv_bytes / (kernel_us["kv_retain"] * 1e-6) / 1e9, 1)
+        res["decode_n_total"] = decode["n_total"]
+    if not args.no_cpu_baseline:
+        res["cpu_baseline"] = cpu_baseline(cfg, inp, g_idx, g_cnt, args.cpu_seconds)
+    line = json.dumps(res)
+    print(line, flush=True)
+    if args.json_out:
+        with open(args.json_out, "w") as f:
+            f.write(line + "\n")
+
+
+if __name__ == "__main__":
+    main()

@@ -124,6 +124,7 @@ egs_status check_decode(const egs_decode_shape* s, DecodeDims* p) {
   if (s->cache_len > (1 << 26)) return fail(EGS_ENOTSUP, "cache_len above 2^26");
   if (s->n_q_heads / s->n_kv_heads > 16)
     return fail(EGS_ENOTSUP, "more than 16 query heads per KV head");
+  if (s->n_obs > 128) return fail(EGS_ENOTSUP, "n_obs above 128 is not supported");
   p->B = s->batch;
   p->Hq = s->n_q_heads;
   p->Hkv = s->n_kv_heads;

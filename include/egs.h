@@ -198,8 +198,8 @@ egs_status egs_sparse_prefill_attn(const egs_prefill_shape* shape,
  * regularized head weights w_h = zeta/r + (1-zeta) softmax_h(-H_h/tau)),
  * Sec. 8.1 (compaction keeps token order).
  *
- * Valid shapes: W = n_obs, 1 <= W <= cache_len, n_sink, n_recent, n_keep >= 0,
- * n_recent >= W is not required; head_dim in {64, 128}; cache_len <= 2^26.
+ * Valid shapes: W = n_obs, 1 <= W <= min(cache_len, 128); n_sink, n_recent,
+ * n_keep >= 0; head_dim in {64, 128}; Hq / Hkv <= 16; cache_len <= 2^26.
  * n_total = cache_len if n_sink + n_recent + n_keep >= cache_len, else
  * n_sink + n_keep + n_recent (see egs_kv_retain_total()).
  * ------------------------------------------------------------------------- */

@@ -1,0 +1,182 @@
+"""GPU parity of decode-time KV retention (kv_retain) and decode attention
+(sparse_decode_attn) against the float64 oracle, through the C ABI."""
+import numpy as np
+import pytest
+import torch
+
+from _parity import ATTN_MAX_ABS, ATTN_REL_L2, ENTROPY_ATOL, attn_errors, dev_tensor, log
+from entropy_guided_sparse_amd import synth
+from oracle import egs_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+# Retention band: the group score mu is a probability over the cache, so it is
+# compared on the uniform-normalised scale L * mu (1 = uniform); entries this
+# close to the cutoff may swap.  Raw-mode scores are compared on the scale of
+# the largest |score|.
+RETAIN_BAND = 1e-4
+# mu comes from fp32 logits of exact bf16 products (|z| <= ~50 here, so
+# |dz| ~ 1e-5) and exp2 / fp32 sums: its relative error is ~2e-5 where the
+# mass is concentrated.  Bound: |d mu| <= MU_RTOL * mu + MU_ATOL_NORM / L.
+MU_RTOL = 1e-4
+MU_ATOL_NORM = 1e-5
+
+
+@pytest.fixture(scope="module")
+def api():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    from entropy_guided_sparse_amd import api as A
+    return A
+
+
+def _cfg(B=2, Hq=8, Hkv=2, d=128, L=4096, W=64, n_sink=4, n_recent=256, n_keep=512):
+    return synth.DecodeConfig("decode-small", B, Hq, Hkv, d, L, W, n_sink, n_recent, n_keep)
+
+
+def _keep_band_ok(keep, mu_ref, n_sink, n_recent, n_keep, band):
+    L = mu_ref.size
+    if n_sink + n_recent + n_keep >= L:
+        return keep.tolist() == list(range(L))
+    got = set(keep.tolist())
+    if len(got) != n_sink + n_recent + n_keep or list(keep) != sorted(keep):
+        return False
+    if not set(range(n_sink)) <= got or not set(range(L - n_recent, L)) <= got:
+        return False
+    cand = np.arange(n_sink, L - n_recent)
+    sel = np.isin(cand, list(got))
+    if n_keep == 0:
+        return not sel.any()
+    sc = mu_ref[cand]
+    c = np.sort(sc)[::-1][n_keep - 1]
+    return not (np.any((sc > c + band) & ~sel) or np.any((sc < c - band) & sel))
+
+
+def run_retain(api, cfg, seed=0, kind=0, alpha=2.0, zeta=0.5, tau=1.0, raw=0, info_alpha=1.0,
+               with_entropy=False, slices=None, inp=None):
+    log(f"[retain parity] B={cfg.batch} Hq={cfg.n_q_heads} Hkv={cfg.n_kv_heads} d={cfg.head_dim} "
+        f"L={cfg.cache_len} W={cfg.n_obs} sink={cfg.n_sink} recent={cfg.n_recent} "
+        f"keep={cfg.n_keep} kind={kind} raw={raw} info={info_alpha} seed={seed}")
+    if inp is None:
+        inp = synth.make_decode(cfg, seed)
+    B, Hq, Hkv, L = cfg.batch, cfg.n_q_heads, cfg.n_kv_heads, cfg.cache_len
+    r = Hq // Hkv
+    shape = api.DecodeShape(B, Hq, Hkv, cfg.head_dim, L, cfg.n_obs, cfg.n_sink, cfg.n_recent,
+                            cfg.n_keep)
+    prm = api.RetainParams(entropy_kind=kind, renyi_alpha=alpha, zeta=zeta, tau=tau,
+                           raw_logit_mode=raw, info_alpha=info_alpha)
+    qo, k, v, qn = (dev_tensor(x, "bf16") for x in (inp.q_obs_store, inp.k_store, inp.v_store,
+                                                   inp.q_new_store))
+    te = None
+    te_np = None
+    if with_entropy:
+        te_np = (np.random.default_rng(seed + 100).random((B, L)) * 4.0).astype(np.float32)
+        te = torch.from_numpy(te_np).cuda()
+    res = api.kv_retain(shape, prm, qo, k, v, token_entropy=te, want_scores=True)
+    out = api.sparse_decode_attn(shape, qn, res["k_out"], res["v_out"])
+    torch.cuda.synchronize()
+    keep = res["keep_idx"].cpu().numpy()
+    mu = res["scores"].cpu().numpy()
+    H = res["head_entropy"].cpu().numpy()
+    k_out = res["k_out"].cpu()
+    todo = slices if slices is not None else [(b, g) for b in range(B) for g in range(Hkv)]
+    worst_mu = worst_H = 0.0
+    for (b, g) in todo:
+        o_keep, o_mu, o_H = O.kv_retain_slice(
+            inp.q_obs[b, g * r:(g + 1) * r], inp.k[b, g], cfg.n_sink, cfg.n_recent, cfg.n_keep,
+            kind=kind, alpha=alpha, zeta=zeta, tau=tau, raw=bool(raw), info_alpha=info_alpha,
+            token_entropy=None if te_np is None else te_np[b])
+        if raw:
+            scale = np.abs(o_mu).max()
+            dmu = np.abs(mu[b, g] - o_mu).max() / scale
+            band = RETAIN_BAND * scale
+            assert dmu <= 1e-5, dmu
+        else:
+            err = np.abs(mu[b, g] - o_mu)
+            dmu = float((err / (MU_RTOL * np.abs(o_mu) + MU_ATOL_NORM / L)).max())
+            band = RETAIN_BAND / L
+            assert dmu <= 1.0, dmu
+            dH = np.abs(H[b, g * r:(g + 1) * r] - o_H).max()
+            worst_H = max(worst_H, dH)
+            assert dH <= ENTROPY_ATOL, dH
+        worst_mu = max(worst_mu, dmu)
+        # bit-exact selection on the GPU's own scores, band rule on the oracle's
+        g_keep = keep[b, g]
+        sel_on_gpu_mu = _select_on(mu[b, g].astype(np.float64), cfg)
+        np.testing.assert_array_equal(g_keep, sel_on_gpu_mu)
+        assert _keep_band_ok(g_keep, o_mu, cfg.n_sink, cfg.n_recent, cfg.n_keep, band)
+        # gather is a pure copy
+        assert torch.equal(k_out[b, g], torch.from_numpy(inp.k_store[b, g][g_keep]).view(torch.bfloat16))
+    log(f"  mu error / bound={worst_mu:.3e}  head entropy max|d|={worst_H:.3e}")
+    # decode attention on the GPU's own kept entries
+    kk = res["k_out"].float().cpu().numpy()
+    vv = res["v_out"].float().cpu().numpy()
+    ref = O.sparse_decode_attn(inp.q_new, kk, vv)
+    ma, rel = attn_errors(out.float().cpu().numpy(), ref)
+    log(f"  decode attention max|d|={ma:.3e} relL2={rel:.3e}")
+    assert ma <= ATTN_MAX_ABS and rel <= ATTN_REL_L2
+    return dict(inp=inp, keep=keep, mu=mu, H=H, out=out)
+
+
+def _select_on(mu, cfg):
+    L = mu.size
+    if cfg.n_sink + cfg.n_recent + cfg.n_keep >= L:
+        return np.arange(L)
+    top = O.select_topk(mu[cfg.n_sink:L - cfg.n_recent], cfg.n_keep)
+    keep = list(range(cfg.n_sink)) + [cfg.n_sink + t for t in top] + \
+        list(range(L - cfg.n_recent, L))
+    return np.asarray(sorted(keep))
+
+
+def test_retain_small_default(api):
+    res = run_retain(api, _cfg())
+    inp = res["inp"]
+    for b in range(2):
+        for g in range(2):
+            assert set(inp.planted[b, g].tolist()) <= set(res["keep"][b, g].tolist())
+
+
+def test_retain_renyi2(api):
+    run_retain(api, _cfg(), seed=1, kind=api.L.EGS_RENYI, alpha=2.0)
+
+
+def test_retain_zeta_one_tau(api):
+    run_retain(api, _cfg(), seed=2, zeta=1.0, tau=0.3)
+
+
+def test_retain_raw_mode(api):
+    run_retain(api, _cfg(), seed=3, raw=1)
+
+
+def test_retain_infokv_fusion(api):
+    run_retain(api, _cfg(), seed=4, info_alpha=0.9, with_entropy=True)
+
+
+def test_retain_keep_all(api):
+    run_retain(api, _cfg(L=700, n_keep=600), seed=5)
+
+
+def test_retain_no_top_entries(api):
+    run_retain(api, _cfg(L=2048, n_keep=0, n_recent=64, n_sink=0), seed=6)
+
+
+@pytest.mark.parametrize("W", [1, 40, 128])
+def test_retain_observer_windows(api, W):
+    run_retain(api, _cfg(W=W, L=3000, n_recent=max(W, 16), n_keep=300), seed=7)
+
+
+def test_retain_wide_group_d64(api):
+    # 7 query heads per KV head (two 4-head groups per workgroup row)
+    run_retain(api, _cfg(B=1, Hq=14, Hkv=2, d=64, L=5000, n_keep=700), seed=8)
+
+
+def test_decode_attention_keep_all_is_dense(api):
+    cfg = _cfg(B=2, L=1500, n_keep=2000)
+    res = run_retain(api, cfg, seed=9)
+    inp = res["inp"]
+    ref = torch.nn.functional.scaled_dot_product_attention(
+        torch.from_numpy(inp.q_new.astype(np.float64))[:, :, None],
+        torch.from_numpy(np.repeat(inp.k, 4, axis=1).astype(np.float64)),
+        torch.from_numpy(np.repeat(inp.v, 4, axis=1).astype(np.float64)))[:, :, 0].numpy()
+    ma, rel = attn_errors(res["out"].float().cpu().numpy(), ref)
+    assert ma <= ATTN_MAX_ABS and rel <= ATTN_REL_L2
