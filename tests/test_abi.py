@@ -1,0 +1,196 @@
+"""Host-side checks of the C ABI (no GPU needed): libegs.so loads, exports every
+entry point include/egs.h declares, and rejects invalid arguments on the host
+with a status and a message before anything is launched."""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "egs.h")
+
+
+def _declared():
+    txt = open(HEADER).read()
+    txt = re.sub(r"/\*.*?\*/", "", txt, flags=re.S)
+    return sorted(set(re.findall(r"\b(egs_[a-z0-9_]+)\s*\(", txt)))
+
+
+@pytest.fixture(scope="module")
+def L():
+    from entropy_guided_sparse_amd import _lib
+    return _lib
+
+
+def test_header_declares_the_boundary():
+    names = _declared()
+    for n in ["egs_entropy_score", "egs_allocate_budget", "egs_select_blocks",
+              "egs_sparse_prefill_attn", "egs_kv_retain", "egs_sparse_decode_attn"]:
+        assert n in names
+
+
+def test_library_exports_every_declared_symbol(L):
+    lib = ctypes.CDLL(L.LIB_PATH)
+    missing = [n for n in _declared() if not hasattr(lib, n)]
+    assert not missing, missing
+    # the binding mirrors the header one to one
+    assert sorted(L.SIGNATURES) == _declared()
+
+
+def test_abi_version_and_status_strings(L):
+    assert L.LIB.egs_abi_version() == 1
+    for st in range(5):
+        assert L.LIB.egs_status_string(st).decode().startswith("EGS_")
+
+
+def _shape(L, **kw):
+    base = dict(n_q_heads=4, n_kv_heads=2, head_dim=64, seq_len=2048, block_size=64,
+                segment_size=512, probe_len=64, dtype=L.EGS_BF16, sm_scale=0.0)
+    base.update(kw)
+    return L.PrefillShapeC(**base)
+
+
+FAKE = ctypes.c_void_p(1 << 20)   # never dereferenced: every call below fails first
+
+
+@pytest.fixture(autouse=True)
+def _no_device(request):
+    # The error-path calls pass placeholder pointers.  They are rejected on the
+    # host, but a mistake in a case would launch a kernel on them: never run
+    # these where a HIP device is visible.
+    if request.node.name.startswith(("test_header", "test_library", "test_abi_version")):
+        return
+    import torch
+    if torch.cuda.device_count() > 0:
+        pytest.skip("host-only error-path checks do not run where a device is visible")
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(seq_len=2000), "EINVAL"),          # N % L_S != 0
+    (dict(segment_size=500), "EINVAL"),      # L_S % L_B != 0
+    (dict(probe_len=0), "EINVAL"),
+    (dict(probe_len=1024), "EINVAL"),        # P > L_S
+    (dict(n_q_heads=5), "EINVAL"),           # Hq % Hkv != 0
+    (dict(dtype=7), "EINVAL"),
+    (dict(sm_scale=-1.0), "EINVAL"),
+    (dict(head_dim=96), "ENOTSUP"),
+    (dict(block_size=40, segment_size=480, seq_len=1920), "ENOTSUP"),
+    (dict(block_size=512, segment_size=1024), "ENOTSUP"),
+])
+def test_prefill_shape_errors(L, kw, status):
+    sc = _shape(L, **kw)
+    st = L.LIB.egs_entropy_score(ctypes.byref(sc), 0, 0, 2.0, FAKE, FAKE, FAKE, FAKE, FAKE,
+                                 1 << 30, None)
+    assert st == getattr(L, "EGS_" + status)
+    assert L.LIB.egs_last_error().decode()
+    assert L.LIB.egs_entropy_score_workspace(ctypes.byref(sc)) == 0
+
+
+def test_entropy_score_argument_errors(L):
+    sc = _shape(L)
+    ws = L.LIB.egs_entropy_score_workspace(ctypes.byref(sc))
+    assert ws > 0
+    call = lambda pool=0, kind=0, alpha=2.0, q=FAKE, wsb=ws: L.LIB.egs_entropy_score(
+        ctypes.byref(sc), pool, kind, alpha, q, FAKE, FAKE, FAKE, FAKE, wsb, None)
+    assert call(pool=1) == L.EGS_ENOTSUP          # max/min pooling not on the GPU path
+    assert call(pool=9) == L.EGS_EINVAL
+    assert call(kind=5) == L.EGS_EINVAL
+    assert call(kind=1, alpha=0.0) == L.EGS_EINVAL
+    assert call(kind=1, alpha=float("inf")) == L.EGS_EINVAL
+    assert call(q=None) == L.EGS_EINVAL
+    assert "q is NULL" in L.LIB.egs_last_error().decode()
+    assert call(q=ctypes.c_void_p((1 << 20) + 2)) == L.EGS_EINVAL   # misaligned
+    assert call(wsb=ws - 1) == L.EGS_EWORKSPACE
+
+
+def test_budget_and_select_errors(L):
+    sc = _shape(L)
+    pol = L.BudgetPolicyC(mode=9)
+    assert L.LIB.egs_allocate_budget(ctypes.byref(sc), ctypes.byref(pol), FAKE, FAKE, FAKE,
+                                     None) == L.EGS_EINVAL
+    pol = L.BudgetPolicyC(mode=L.EGS_BUDGET_ALG3, base_tokens=0.0, entropy_threshold=1e-5)
+    assert L.LIB.egs_allocate_budget(ctypes.byref(sc), ctypes.byref(pol), FAKE, FAKE, FAKE,
+                                     None) == L.EGS_EINVAL
+    pol = L.BudgetPolicyC(mode=L.EGS_BUDGET_PROPORTIONAL, frac_min=0.5, frac_max=0.1)
+    assert L.LIB.egs_allocate_budget(ctypes.byref(sc), ctypes.byref(pol), FAKE, FAKE, FAKE,
+                                     None) == L.EGS_EINVAL
+    pol = L.BudgetPolicyC(mode=L.EGS_BUDGET_FIXED, frac=0.25)
+    assert L.LIB.egs_allocate_budget(ctypes.byref(sc), None, FAKE, FAKE, FAKE,
+                                     None) == L.EGS_EINVAL
+    assert L.LIB.egs_allocate_budget(ctypes.byref(sc), ctypes.byref(pol), None, FAKE, FAKE,
+                                     None) == L.EGS_EINVAL
+    CB = 2048 // 64
+    for kmax in (0, CB + 1):
+        assert L.LIB.egs_select_blocks(ctypes.byref(sc), FAKE, FAKE, kmax, FAKE, FAKE,
+                                       None) == L.EGS_EINVAL
+    assert L.LIB.egs_sparse_prefill_attn(ctypes.byref(sc), FAKE, FAKE, FAKE, FAKE, FAKE, 0,
+                                         FAKE, None, None) == L.EGS_EINVAL
+    # out aliasing q
+    assert L.LIB.egs_sparse_prefill_attn(ctypes.byref(sc), FAKE, ctypes.c_void_p(2 << 20),
+                                         ctypes.c_void_p(3 << 20), FAKE, FAKE, 4, FAKE, None,
+                                         None) == L.EGS_EINVAL
+
+
+def _dshape(L, **kw):
+    base = dict(batch=2, n_q_heads=8, n_kv_heads=2, head_dim=128, cache_len=4096, n_obs=64,
+                n_sink=4, n_recent=256, n_keep=512, dtype=L.EGS_BF16, sm_scale=0.0)
+    base.update(kw)
+    return L.DecodeShapeC(**base)
+
+
+def test_decode_totals_and_workspace(L):
+    sc = _dshape(L)
+    assert L.LIB.egs_kv_retain_total(ctypes.byref(sc)) == 4 + 256 + 512
+    sc = _dshape(L, n_keep=8000)
+    assert L.LIB.egs_kv_retain_total(ctypes.byref(sc)) == 4096   # keep everything
+    assert L.LIB.egs_kv_retain_workspace(ctypes.byref(sc)) > 0
+
+
+@pytest.mark.parametrize("kw,status", [
+    (dict(n_q_heads=7), "EINVAL"),
+    (dict(n_obs=0), "EINVAL"),
+    (dict(n_obs=5000), "EINVAL"),
+    (dict(n_sink=-1), "EINVAL"),
+    (dict(dtype=1), "ENOTSUP"),          # f32 decode
+    (dict(head_dim=96), "ENOTSUP"),
+    (dict(n_obs=129), "ENOTSUP"),
+    (dict(n_q_heads=68, n_kv_heads=2), "ENOTSUP"),
+])
+def test_decode_shape_errors(L, kw, status):
+    sc = _dshape(L, **kw)
+    prm = L.RetainParamsC(0, 2.0, 0.5, 1.0, 0, 1.0)
+    st = L.LIB.egs_kv_retain(ctypes.byref(sc), ctypes.byref(prm), FAKE, FAKE, FAKE, None, FAKE,
+                             FAKE, FAKE, None, None, FAKE, 1 << 40, None)
+    assert st == getattr(L, "EGS_" + status)
+    assert L.LIB.egs_kv_retain_total(ctypes.byref(sc)) == -1
+
+
+def test_retain_param_errors(L):
+    sc = _dshape(L)
+    ws = L.LIB.egs_kv_retain_workspace(ctypes.byref(sc))
+
+    def call(prm, k_out=FAKE, v_out=FAKE, wsb=ws):
+        return L.LIB.egs_kv_retain(ctypes.byref(sc), ctypes.byref(prm), FAKE, FAKE, FAKE, None,
+                                   FAKE, k_out, v_out, None, None, FAKE, wsb, None)
+
+    P = lambda **kw: L.RetainParamsC(**{**dict(entropy_kind=0, renyi_alpha=2.0, zeta=0.5,
+                                                 tau=1.0, raw_logit_mode=0, info_alpha=1.0),
+                                        **kw})
+    assert call(P(zeta=0.0)) == L.EGS_EINVAL
+    assert call(P(zeta=1.5)) == L.EGS_EINVAL
+    assert call(P(tau=0.0)) == L.EGS_EINVAL
+    assert call(P(info_alpha=1.5)) == L.EGS_EINVAL
+    assert call(P(entropy_kind=1, renyi_alpha=-1.0)) == L.EGS_EINVAL
+    assert call(P(raw_logit_mode=2)) == L.EGS_EINVAL
+    assert call(P(), v_out=None) == L.EGS_EINVAL
+    assert call(P(), wsb=ws - 1) == L.EGS_EWORKSPACE
+    # decode attention
+    assert L.LIB.egs_sparse_decode_attn(ctypes.byref(sc), FAKE, FAKE, FAKE, 0, FAKE, FAKE,
+                                        1 << 30, None) == L.EGS_EINVAL
+    assert L.LIB.egs_sparse_decode_attn(ctypes.byref(sc), FAKE, FAKE, FAKE, 5000, FAKE, FAKE,
+                                        1 << 30, None) == L.EGS_EINVAL
+    aws = L.LIB.egs_sparse_decode_attn_workspace(ctypes.byref(sc), 772)
+    if aws > 0:
+        assert L.LIB.egs_sparse_decode_attn(ctypes.byref(sc), FAKE, FAKE, FAKE, 772, FAKE, FAKE,
+                                            aws - 1, None) == L.EGS_EWORKSPACE
