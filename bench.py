@@ -163,6 +163,8 @@ def main():
     sc = shape.c()
     ws = torch.empty(L.LIB.egs_entropy_score_workspace(ctypes.byref(sc)), dtype=torch.uint8,
                      device=dev)
+    attn_ws = torch.empty(max(256, L.LIB.egs_sparse_prefill_attn_workspace(ctypes.byref(sc))),
+                          dtype=torch.uint8, device=dev)
 
     def prefill(evs):
         evs[0].record()
@@ -173,7 +175,7 @@ def main():
         evs[2].record()
         api.select_blocks(shape, scores, budget, k_max, block_idx=idx, block_cnt=cnt)
         evs[3].record()
-        api.sparse_prefill_attn(shape, q, k, v, idx, cnt, out=out)
+        api.sparse_prefill_attn(shape, q, k, v, idx, cnt, out=out, workspace=attn_ws)
         evs[4].record()
 
     # ------------------------------------------------------------------ decode

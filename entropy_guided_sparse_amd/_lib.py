@@ -62,7 +62,9 @@ SIGNATURES = {
                                 _P, _P, _P, ctypes.c_size_t, _P]),
     "egs_allocate_budget": (_ST, [_PS, ctypes.POINTER(BudgetPolicyC), _P, _P, _P, _P]),
     "egs_select_blocks": (_ST, [_PS, _P, _P, ctypes.c_int32, _P, _P, _P]),
-    "egs_sparse_prefill_attn": (_ST, [_PS, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P]),
+    "egs_sparse_prefill_attn_workspace": (ctypes.c_size_t, [_PS]),
+    "egs_sparse_prefill_attn": (_ST, [_PS, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P,
+                                      ctypes.c_size_t, _P]),
     "egs_kv_retain_total": (ctypes.c_int32, [_DS]),
     "egs_kv_retain_workspace": (ctypes.c_size_t, [_DS]),
     "egs_kv_retain": (_ST, [_DS, ctypes.POINTER(RetainParamsC), _P, _P, _P, _P, _P, _P, _P,
@@ -92,7 +94,7 @@ def _load():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    if lib.egs_abi_version() != 1:
+    if lib.egs_abi_version() != 2:
         raise ImportError("libegs.so ABI version mismatch")
     return lib
 

@@ -204,7 +204,7 @@ def select_blocks(shape: PrefillShape, block_scores: torch.Tensor, budget: torch
 
 def sparse_prefill_attn(shape: PrefillShape, q, k, v, block_idx, block_cnt,
                         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
-                        return_lse: bool = False):
+                        return_lse: bool = False, workspace: Optional[torch.Tensor] = None):
     """Block-sparse causal GQA attention output [Hq, N, d] (and lse [Hq, N])."""
     s = shape
     dev = q.device
@@ -222,9 +222,13 @@ def sparse_prefill_attn(shape: PrefillShape, q, k, v, block_idx, block_cnt,
     if lse is not None:
         _need(lse, "lse", (s.n_q_heads, s.seq_len), torch.float32, dev)
     sc = s.c()
+    wsb = L.LIB.egs_sparse_prefill_attn_workspace(ctypes.byref(sc))
+    if workspace is None:
+        workspace = _workspace(wsb, dev)
     L.check(L.LIB.egs_sparse_prefill_attn(ctypes.byref(sc), _ptr(q), _ptr(k), _ptr(v),
                                           _ptr(block_idx), _ptr(block_cnt), k_max, _ptr(out),
-                                          _ptr(lse), _stream(dev)))
+                                          _ptr(lse), _ptr(workspace), workspace.numel(),
+                                          _stream(dev)))
     return (out, lse) if (return_lse or lse is not None) else out
 
 

@@ -7,21 +7,27 @@
 // under the causal mask, so a full budget reproduces dense causal attention.
 //
 // gfx950 design (bf16, head_dim 64/128, block 64/128):
-//  * One workgroup per (head, query block), L_B/32 wavefronts of 32 query rows.
-//    Workgroups are ordered heaviest (latest) query block first, and the r
-//    heads of one KV group for the same query block are dispatched to the same
-//    XCD so their shared K/V blocks meet in that XCD's L2.
-//  * The "transposed" flash formulation keeps every operand in the layout the
-//    next MFMA wants, with no cross-lane shuffles:
+//  * A pre-pass (vt_pack) rewrites V once per call into 64-key tiles stored
+//    d-major ("V^T") with the keys of every 16-key group permuted into the
+//    order in which the softmax probabilities leave the accumulator.  Every
+//    MFMA operand of the main kernel is then one 16-byte LDS read, and no
+//    transposition is repeated by the many query blocks that select a block.
+//  * One workgroup per (head, query block), L_B/32 wavefronts of 32 query
+//    rows.  Workgroups run heaviest (latest) query block first, and the r
+//    heads of a KV group for the same query block go to the same XCD so their
+//    shared K/V blocks meet in that XCD's L2.
+//  * Transposed flash formulation, no cross-lane shuffles:
 //        S^T = K Q^T     (A = K tile from LDS, B = Q^T held in registers)
-//        P^T  = exp2(S^T - m)   (a lane owns one query row -> row statistics
-//                                are lane-local plus one xor-32 exchange)
-//        O^T += V^T P^T  (A = V^T tile from LDS, B = P^T straight from the
-//                         accumulator registers)
-//    using v_mfma_f32_32x32x16_bf16, fp32 accumulation and online softmax.
-//  * K/V sub-tiles of 64 keys are double-buffered in LDS; the next sub-tile's
-//    global loads are issued before the current one is computed.  V is stored
-//    transposed (d-major) so the A operand of O^T is two 8-byte LDS reads.
+//        P^T = exp2(S^T - m)   (a lane owns one query row)
+//        O^T += V^T P^T  (A = V^T tile from LDS, B = P^T from the accumulator)
+//    on v_mfma_f32_32x32x16_bf16 with fp32 accumulation.  The running maximum
+//    is only raised (and O rescaled) when some row's maximum grows by more
+//    than 2^8 in probability; otherwise probabilities up to 2^8 accumulate
+//    against the stale maximum, which fp32 and bf16 hold exactly enough.
+//  * 64-key K and V^T stages are double-buffered in LDS behind XOR-swizzled
+//    16-byte chunks (conflict-free ds_read_b128); the next stage's global
+//    loads are in flight while the current stage is computed.  The block list
+//    of the (head, segment) is staged in LDS once.
 //
 // Generic path: a VALU kernel (one thread per query row, fp32 math) serves
 // fp32 inputs and shapes outside the MFMA kernel's range.
@@ -30,29 +36,74 @@
 
 namespace egs {
 
+constexpr int AT_KT = 64;     // keys per LDS stage and per V^T tile
+constexpr int AT_LCAP = 512;  // block-list entries staged in LDS at a time
+
+// Key order inside a 16-key group of a V^T tile: the k-slot order of the P^T
+// operand as it leaves the S^T accumulator.  Keys 0-3 sit at positions 0-3,
+// keys 8-11 at 4-7, keys 4-7 at 8-11 and keys 12-15 at 12-15 (bits 2 and 3
+// swapped), so the map is its own inverse.
+__device__ __forceinline__ int vt_swap23(int x16) {
+  return (x16 & 3) | ((x16 & 4) << 1) | ((x16 & 8) >> 1);
+}
+
+// ---------------------------------------------------------------------------
+// vt_pack: V [Hkv, N, D] -> Vt [Hkv, N/64, D, 64] with permuted keys.
+// One workgroup per (64-key tile, KV head); coalesced 16-byte loads and stores.
+// ---------------------------------------------------------------------------
+template <int D>
+__global__ __launch_bounds__(256) void vt_pack_kernel(const bf16* __restrict__ V, int N,
+                                                      bf16* __restrict__ Vt) {
+  constexpr int VP = D + 2;   // padded row (bf16) to spread the column reads
+  __shared__ bf16 tile[AT_KT * VP];
+  const int t = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+  const bf16* src = V + ((size_t)g * N + (size_t)t * AT_KT) * D;
+  constexpr int CH = AT_KT * D / 8;
+  for (int q = tid; q < CH; q += 256) {
+    const int row = q / (D / 8), c8 = q % (D / 8);
+    const bf16x8 v = load8(src + (size_t)row * D + c8 * 8);
+#pragma unroll
+    for (int e = 0; e < 8; ++e) tile[row * VP + c8 * 8 + e] = v[e];
+  }
+  __syncthreads();
+  bf16* dst = Vt + ((size_t)g * (N / AT_KT) + t) * (size_t)(D * AT_KT);
+  for (int q = tid; q < CH; q += 256) {
+    const int d = q / (AT_KT / 8), c8 = q % (AT_KT / 8);   // 8 positions per chunk
+    bf16x8 v;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) {
+      const int pos = c8 * 8 + e;
+      const int grp = pos >> 4;
+      v[e] = tile[(grp * 16 + vt_swap23(pos & 15)) * VP + d];
+    }
+    store8(dst + (size_t)d * AT_KT + c8 * 8, v);
+  }
+}
+
 // ---------------------------------------------------------------------------
 // MFMA kernel
 // ---------------------------------------------------------------------------
 template <int D, int LB>
-__global__ __launch_bounds__(LB * 2) void sparse_attn_mfma_kernel(
-    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ V,
+__global__ __launch_bounds__(LB * 2) __attribute__((amdgpu_waves_per_eu(2)))
+void sparse_attn_mfma_kernel(
+    const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ Vt,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt, int k_max,
     bf16* __restrict__ O, float* __restrict__ lse, int Hkv, int r, int N, int LS, int CS,
     int CB, float scale_log2, int xcd_remap) {
   constexpr int NW = LB / 32;
   constexpr int NT = NW * 64;
-  constexpr int KT = 64;              // keys per LDS sub-tile
+  constexpr int KT = AT_KT;
   constexpr int SUB = LB / KT;
-  constexpr int KPAD = D + 8;         // K row pitch (bf16 elements)
-  constexpr int VPAD = KT + 4;        // V^T row pitch (bf16 elements)
-  constexpr int NC = D / 16;
-  constexpr int ND = D / 32;
-  constexpr int KCT = KT * D / 8;     // 16-byte K chunks per sub-tile
-  constexpr int KI = (KCT + NT - 1) / NT;
-  constexpr int VUT = (KT / 4) * (D / 8);   // (4 keys x 8 d) V units per sub-tile
-  constexpr int VI = (VUT + NT - 1) / NT;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][KT * KPAD];
-  __shared__ __attribute__((aligned(16))) bf16 Vt[2][D * VPAD];
+  constexpr int NC = D / 16;          // 16-wide d chunks of Q / K
+  constexpr int ND = D / 32;          // 32-row d tiles of O^T
+  constexpr int KCH = D / 8;          // 16-byte chunks per K row
+  constexpr int STAGE_CH = KT * D / 8;          // 16-byte chunks per K (or V^T) stage
+  constexpr int PER_T = STAGE_CH / NT;          // chunks per thread per stage
+  static_assert(STAGE_CH % NT == 0, "stage must split evenly over the threads");
+  constexpr float kRescale = 8.0f;    // log2 of the largest unnormalised probability
+  __shared__ __attribute__((aligned(16))) bf16 Ks[2][KT * D];
+  __shared__ __attribute__((aligned(16))) bf16 Vs[2][D * KT];
+  __shared__ int lst[AT_LCAP];
 
   // ---- work item: (KV group, query block) pair, head within group ----
   const int bid = blockIdx.x;
@@ -74,6 +125,12 @@ __global__ __launch_bounds__(LB * 2) void sparse_attn_mfma_kernel(
   const int l32 = lane & 31, hg = lane >> 5;
   const size_t qrow0 = (size_t)b * LB + w * 32;
 
+  // block list of (h, s): staged in LDS, AT_LCAP entries at a time
+  const int32_t* sel = idx + ((size_t)h * CS + s) * k_max;
+  const int n = min(max(cnt[(size_t)h * CS + s], 0), k_max);
+  int lbase = 0;
+  for (int e = tid; e < min(n, AT_LCAP); e += NT) lst[e] = sel[e];
+
   bf16x8 qf[NC];
   {
     const bf16* qp = Q + ((size_t)h * N + qrow0 + l32) * D + 8 * hg;
@@ -85,80 +142,55 @@ __global__ __launch_bounds__(LB * 2) void sparse_attn_mfma_kernel(
   for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
     for (int i = 0; i < 16; ++i) o[dt][i] = 0.f;
-  float m_run = kNegBig, l_run = 0.f;
+  float m_run = kNegBig, l_run = 0.f;   // m_run in raw (unscaled) logit units
 
-  const int32_t* sel = idx + ((size_t)h * CS + s) * k_max;
-  const int n = min(max(cnt[(size_t)h * CS + s], 0), k_max);
+  __syncthreads();   // lst ready
   int p = 0;
   auto next_sel = [&]() -> int {
     while (p < n) {
-      const int j = sel[p++];
+      if (p == lbase + AT_LCAP) {   // uniform: refill the staged list
+        __syncthreads();
+        lbase += AT_LCAP;
+        for (int e = tid; e < AT_LCAP && lbase + e < n; e += NT) lst[e] = sel[lbase + e];
+        __syncthreads();
+      }
+      const int j = lst[p - lbase];
+      ++p;
       if (j >= 0 && j < b) return j;
     }
     return -1;
   };
 
   const bf16* Kg = K + (size_t)g * N * D;
-  const bf16* Vg = V + (size_t)g * N * D;
-  u32x4 kreg[KI];
-  u32x4 vreg[VI][4];
+  const bf16* Vg = Vt + (size_t)g * N * D;
+  u32x4 kreg[PER_T], vreg[PER_T];
 
   auto gload = [&](int blk, int sub) {
     const size_t key0 = (size_t)blk * LB + sub * KT;
+    const bf16* ksrc = Kg + key0 * D;
+    const bf16* vsrc = Vg + key0 * D;   // tile (key0 / 64) of V^T: D x 64 contiguous
 #pragma unroll
-    for (int ii = 0; ii < KI; ++ii) {
+    for (int ii = 0; ii < PER_T; ++ii) {
       const int q = tid + ii * NT;
-      if (q < KCT) {
-        const int row = q / (D / 8), c8 = q % (D / 8);
-        kreg[ii] = *reinterpret_cast<const u32x4*>(Kg + (key0 + row) * D + c8 * 8);
-      }
-    }
-#pragma unroll
-    for (int ii = 0; ii < VI; ++ii) {
-      const int u = tid + ii * NT;
-      if (u < VUT) {
-        const int k4 = u / (D / 8), c8 = u % (D / 8);
-#pragma unroll
-        for (int kk = 0; kk < 4; ++kk)
-          vreg[ii][kk] =
-              *reinterpret_cast<const u32x4*>(Vg + (key0 + 4 * k4 + kk) * D + c8 * 8);
-      }
+      kreg[ii] = *reinterpret_cast<const u32x4*>(ksrc + (size_t)q * 8);
+      vreg[ii] = *reinterpret_cast<const u32x4*>(vsrc + (size_t)q * 8);
     }
   };
   auto lstore = [&](int buf) {
 #pragma unroll
-    for (int ii = 0; ii < KI; ++ii) {
+    for (int ii = 0; ii < PER_T; ++ii) {
       const int q = tid + ii * NT;
-      if (q < KCT) {
-        const int row = q / (D / 8), c8 = q % (D / 8);
-        *reinterpret_cast<u32x4*>(&Ks[buf][row * KPAD + c8 * 8]) = kreg[ii];
-      }
-    }
-#pragma unroll
-    for (int ii = 0; ii < VI; ++ii) {
-      const int u = tid + ii * NT;
-      if (u < VUT) {
-        const int k4 = u / (D / 8), c8 = u % (D / 8);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) {
-          const int wd = e >> 1, sh = 16 * (e & 1);
-          const uint32_t a0 = (vreg[ii][0][wd] >> sh) & 0xFFFFu;
-          const uint32_t a1 = (vreg[ii][1][wd] >> sh) & 0xFFFFu;
-          const uint32_t a2 = (vreg[ii][2][wd] >> sh) & 0xFFFFu;
-          const uint32_t a3 = (vreg[ii][3][wd] >> sh) & 0xFFFFu;
-          u32x2 pk;
-          pk[0] = a0 | (a1 << 16);
-          pk[1] = a2 | (a3 << 16);
-          *reinterpret_cast<u32x2*>(&Vt[buf][(c8 * 8 + e) * VPAD + 4 * k4]) = pk;
-        }
-      }
+      const int krow = q / KCH, kc = q % KCH;
+      *reinterpret_cast<u32x4*>(&Ks[buf][krow * D + ((kc ^ (krow & 7)) * 8)]) = kreg[ii];
+      const int vrow = q / (KT / 8), vc = q % (KT / 8);
+      *reinterpret_cast<u32x4*>(&Vs[buf][vrow * KT + ((vc ^ (vrow & 7)) * 8)]) = vreg[ii];
     }
   };
 
   auto compute = [&](int buf, bool diag, int sub) {
     if (diag && sub * KT > w * 32 + 31) return;   // wave-uniform: all keys in the future
     const bf16* ks = Ks[buf];
-    const bf16* vt = Vt[buf];
+    const bf16* vs = Vs[buf];
     floatx16 st[2];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -168,53 +200,54 @@ __global__ __launch_bounds__(LB * 2) void sparse_attn_mfma_kernel(
     for (int c = 0; c < NC; ++c) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) {
-        const bf16x8 a = load8(ks + (kt * 32 + l32) * KPAD + 16 * c + 8 * hg);
+        const int row = kt * 32 + l32;
+        const bf16x8 a = load8(ks + row * D + (((2 * c + hg) ^ (row & 7)) * 8));
         st[kt] = mfma32(a, qf[c], st[kt]);
       }
     }
-    const bool need_mask = diag && (sub * KT + KT - 1 > w * 32);
-    const int row_local = w * 32 + l32;
-    float mx = m_run;
+    if (diag && (sub * KT + KT - 1 > w * 32)) {
+      const int row_local = w * 32 + l32;
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
+      for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        float v = st[kt][i] * scale_log2;
-        if (need_mask) {
-          const int key_local = sub * KT + kt * 32 + acc_row(i, lane);
-          if (key_local > row_local) v = -INFINITY;
-        }
-        st[kt][i] = v;
-        mx = fmaxf(mx, v);
-      }
+        for (int i = 0; i < 16; ++i)
+          if (sub * KT + kt * 32 + acc_row(i, lane) > row_local) st[kt][i] = -INFINITY;
     }
+    float mx = st[0][0];
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[kt][i]);
     mx = fmaxf(mx, __shfl_xor(mx, 32));
-    const float alpha = exp2f(m_run - mx);
-    m_run = mx;
-    l_run *= alpha;
+    // raise the running maximum only when a row grew by more than 2^kRescale
+    const bool grow = (mx - m_run) * scale_log2 > kRescale;
+    if (__any(grow)) {
+      const float m_new = fmaxf(m_run, mx);
+      const float alpha = exp2f((m_run - m_new) * scale_log2);
+      m_run = m_new;
+      l_run *= alpha;
 #pragma unroll
-    for (int dt = 0; dt < ND; ++dt)
+      for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
-      for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+        for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+    }
+    const float moff = m_run * scale_log2;
     bf16x8 pb[4];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float pv = exp2f(st[kt][i] - mx);
+        const float pv = exp2f(__builtin_fmaf(st[kt][i], scale_log2, -moff));
         l_run += pv;
         pb[kt * 2 + (i >> 3)][i & 7] = f2bf(pv);
       }
     }
 #pragma unroll
     for (int dt = 0; dt < ND; ++dt) {
+      const int row = dt * 32 + l32;
 #pragma unroll
       for (int ch = 0; ch < 4; ++ch) {
-        const int base = (ch >> 1) * 32 + 16 * (ch & 1);
-        const bf16* vrow = vt + (dt * 32 + l32) * VPAD + base + 4 * hg;
-        const bf16x4 lo4 = *reinterpret_cast<const bf16x4*>(vrow);
-        const bf16x4 hi4 = *reinterpret_cast<const bf16x4*>(vrow + 8);
-        const bf16x8 a = __builtin_shufflevector(lo4, hi4, 0, 1, 2, 3, 4, 5, 6, 7);
+        const bf16x8 a = load8(vs + row * KT + (((2 * ch + hg) ^ (row & 7)) * 8));
         o[dt] = mfma32(a, pb[ch], o[dt]);
       }
     }
@@ -267,7 +300,8 @@ __global__ __launch_bounds__(LB * 2) void sparse_attn_mfma_kernel(
       *reinterpret_cast<bf16x4*>(op + dt * 32 + 8 * i4 + 4 * hg) = v;
     }
   }
-  if (lse != nullptr && hg == 0) lse[(size_t)h * N + qrow0 + l32] = m_run * kLn2 + logf(lt);
+  if (lse != nullptr && hg == 0)
+    lse[(size_t)h * N + qrow0 + l32] = (m_run * scale_log2 + log2f(lt)) * kLn2;
 }
 
 // ---------------------------------------------------------------------------
@@ -383,22 +417,36 @@ static hipError_t generic_dispatch(const PrefillDims& p, const void* q, const vo
   return hipGetLastError();
 }
 
+static bool mfma_path(const PrefillDims& p) {
+  return p.dtype == EGS_BF16 && (p.D == 64 || p.D == 128) && (p.LB == 64 || p.LB == 128);
+}
+
+size_t sparse_attn_workspace_bytes(const PrefillDims& p) {
+  // V^T tiles for the MFMA path; nothing otherwise
+  return mfma_path(p) ? (size_t)p.Hkv * p.N * p.D * sizeof(bf16) : 0;
+}
+
 hipError_t launch_sparse_attn(const PrefillDims& p, const void* q, const void* k,
                               const void* v, const int32_t* idx, const int32_t* cnt,
-                              int k_max, void* out, float* lse, hipStream_t st) {
+                              int k_max, void* out, float* lse, void* ws, hipStream_t st) {
   if (p.dtype == EGS_F32) return generic_dispatch<float>(p, q, k, v, idx, cnt, k_max, out, lse, st);
-  const bool mfma_ok = (p.D == 64 || p.D == 128) && (p.LB == 64 || p.LB == 128);
-  if (!mfma_ok) return generic_dispatch<bf16>(p, q, k, v, idx, cnt, k_max, out, lse, st);
-  const int grid = p.Hq * p.CB;
-  const int remap = ((p.Hkv * p.CB) % 8 == 0) ? 1 : 0;
-  const float sl2 = p.sm_scale * kLog2e;
+  if (!mfma_path(p)) return generic_dispatch<bf16>(p, q, k, v, idx, cnt, k_max, out, lse, st);
   const bf16* Q = static_cast<const bf16*>(q);
   const bf16* K = static_cast<const bf16*>(k);
   const bf16* V = static_cast<const bf16*>(v);
+  bf16* Vt = static_cast<bf16*>(ws);
   bf16* O = static_cast<bf16*>(out);
+  const dim3 pgrid(p.N / AT_KT, p.Hkv);
+  if (p.D == 128) vt_pack_kernel<128><<<pgrid, 256, 0, st>>>(V, p.N, Vt);
+  else vt_pack_kernel<64><<<pgrid, 256, 0, st>>>(V, p.N, Vt);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int grid = p.Hq * p.CB;
+  const int remap = ((p.Hkv * p.CB) % 8 == 0) ? 1 : 0;
+  const float sl2 = p.sm_scale * kLog2e;
 #define EGS_MF(DD, BB)                                                                    \
   sparse_attn_mfma_kernel<DD, BB><<<grid, BB * 2, 0, st>>>(                               \
-      Q, K, V, idx, cnt, k_max, O, lse, p.Hkv, p.r, p.N, p.LS, p.CS, p.CB, sl2, remap)
+      Q, K, Vt, idx, cnt, k_max, O, lse, p.Hkv, p.r, p.N, p.LS, p.CS, p.CB, sl2, remap)
   if (p.D == 128 && p.LB == 128) EGS_MF(128, 128);
   else if (p.D == 128 && p.LB == 64) EGS_MF(128, 64);
   else if (p.D == 64 && p.LB == 128) EGS_MF(64, 128);

@@ -263,10 +263,17 @@ egs_status egs_select_blocks(const egs_prefill_shape* shape, const float* block_
                     "select launch");
 }
 
+size_t egs_sparse_prefill_attn_workspace(const egs_prefill_shape* shape) {
+  PrefillDims p;
+  if (check_prefill(shape, &p) != EGS_OK) return 0;
+  return round_up(egs::sparse_attn_workspace_bytes(p), kWsAlign);
+}
+
 egs_status egs_sparse_prefill_attn(const egs_prefill_shape* shape, const void* q, const void* k,
                                    const void* v, const int32_t* block_idx,
                                    const int32_t* block_cnt, int32_t k_max, void* out,
-                                   float* lse, hipStream_t stream) {
+                                   float* lse, void* workspace, size_t workspace_bytes,
+                                   hipStream_t stream) {
   PrefillDims p;
   egs_status st = check_prefill(shape, &p);
   if (st != EGS_OK) return st;
@@ -280,8 +287,15 @@ egs_status egs_sparse_prefill_attn(const egs_prefill_shape* shape, const void* q
   if ((st = need(block_cnt, "block_cnt", 4)) != EGS_OK) return st;
   if (lse != nullptr && !aligned(lse, 4)) return fail(EGS_EINVAL, "lse is not 4-byte aligned");
   if (out == q || out == k || out == v) return fail(EGS_EINVAL, "out aliases an input");
+  const size_t wsb = egs::sparse_attn_workspace_bytes(p);
+  if (wsb > 0) {
+    if ((st = need(workspace, "workspace", kWsAlign)) != EGS_OK) return st;
+    if (workspace_bytes < wsb)
+      return fail(EGS_EWORKSPACE, "workspace of %zu bytes is below the %zu required",
+                  workspace_bytes, wsb);
+  }
   return hip_status(egs::launch_sparse_attn(p, q, k, v, block_idx, block_cnt, k_max, out, lse,
-                                            stream),
+                                            workspace, stream),
                     "sparse_attn launch");
 }
 

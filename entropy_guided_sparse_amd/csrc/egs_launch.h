@@ -35,10 +35,11 @@ hipError_t launch_budget(const PrefillDims& p, const egs_budget_policy& pol,
 hipError_t launch_select(const PrefillDims& p, const float* scores,
                          const int32_t* budget, int k_max, int32_t* idx,
                          int32_t* cnt, hipStream_t st);
-// K5: block-sparse causal GQA attention.
+// K5: block-sparse causal GQA attention (workspace: the packed V^T tiles).
+size_t sparse_attn_workspace_bytes(const PrefillDims& p);
 hipError_t launch_sparse_attn(const PrefillDims& p, const void* q, const void* k,
                               const void* v, const int32_t* idx, const int32_t* cnt,
-                              int k_max, void* out, float* lse, hipStream_t st);
+                              int k_max, void* out, float* lse, void* ws, hipStream_t st);
 
 // K6/K7: decode retention.  Workspace layout is owned by retain.hip.
 size_t retain_workspace_bytes(const DecodeDims& p);

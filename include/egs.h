@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define EGS_ABI_VERSION 1
+#define EGS_ABI_VERSION 2
 
 typedef enum {
   EGS_OK = 0,
@@ -177,17 +177,22 @@ egs_status egs_select_blocks(const egs_prefill_shape* shape,
  * Query block b (rows b*L_B .. (b+1)*L_B-1) of segment s = b*L_B / L_S attends
  * the blocks L(h, b) = { j in block_idx[h, s, 0 .. cnt-1] : 0 <= j < b } U { b },
  * the own block b causally masked (key t <= row i).  Entries outside 0..b-1
- * are skipped, so any list is safe; lists from egs_select_blocks are
- * ascending.
+ * are skipped, so any list is safe; a block listed twice is attended twice
+ * (egs_select_blocks writes ascending lists without repeats).
  *   out[h, i, :] = sum_t softmax_t(sm_scale * q[h,i] . k[g,t]) v[g,t]
  *   lse[h, i]    = ln sum_t exp(sm_scale * q[h,i] . k[g,t])   (nullable)
  *   q: [Hq, N, d], k, v: [Hkv, N, d], out: [Hq, N, d] (dtype); lse [Hq, N] f32.
+ *   workspace: >= egs_sparse_prefill_attn_workspace(shape) bytes, 256-byte
+ *   aligned (the bf16 MFMA path packs V into d-major tiles there: Hkv*N*d*2
+ *   bytes; other paths need none and accept NULL).
  * ------------------------------------------------------------------------- */
+size_t egs_sparse_prefill_attn_workspace(const egs_prefill_shape* shape);
 egs_status egs_sparse_prefill_attn(const egs_prefill_shape* shape,
                                    const void* q, const void* k, const void* v,
                                    const int32_t* block_idx,
                                    const int32_t* block_cnt, int32_t k_max,
-                                   void* out, float* lse, hipStream_t stream);
+                                   void* out, float* lse, void* workspace,
+                                   size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Decode-time KV retention.

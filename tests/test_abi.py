@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.LIB.egs_abi_version() == 1
+    assert L.LIB.egs_abi_version() == 2
     for st in range(5):
         assert L.LIB.egs_status_string(st).decode().startswith("EGS_")
 
@@ -125,11 +125,20 @@ def test_budget_and_select_errors(L):
         assert L.LIB.egs_select_blocks(ctypes.byref(sc), FAKE, FAKE, kmax, FAKE, FAKE,
                                        None) == L.EGS_EINVAL
     assert L.LIB.egs_sparse_prefill_attn(ctypes.byref(sc), FAKE, FAKE, FAKE, FAKE, FAKE, 0,
-                                         FAKE, None, None) == L.EGS_EINVAL
+                                         FAKE, None, FAKE, 1 << 30, None) == L.EGS_EINVAL
     # out aliasing q
     assert L.LIB.egs_sparse_prefill_attn(ctypes.byref(sc), FAKE, ctypes.c_void_p(2 << 20),
                                          ctypes.c_void_p(3 << 20), FAKE, FAKE, 4, FAKE, None,
-                                         None) == L.EGS_EINVAL
+                                         FAKE, 1 << 30, None) == L.EGS_EINVAL
+    # the bf16 MFMA path needs the packed-V workspace: Hkv * N * d * 2 bytes
+    aws = L.LIB.egs_sparse_prefill_attn_workspace(ctypes.byref(sc))
+    assert aws == 2 * 2048 * 64 * 2
+    assert L.LIB.egs_sparse_prefill_attn(ctypes.byref(sc), FAKE, ctypes.c_void_p(2 << 20),
+                                         ctypes.c_void_p(3 << 20), FAKE, FAKE, 4,
+                                         ctypes.c_void_p(4 << 20), None, FAKE, aws - 1,
+                                         None) == L.EGS_EWORKSPACE
+    sc32 = _shape(L, dtype=L.EGS_F32)
+    assert L.LIB.egs_sparse_prefill_attn_workspace(ctypes.byref(sc32)) == 0
 
 
 def _dshape(L, **kw):
