@@ -24,10 +24,12 @@
 //    is only raised (and O rescaled) when some row's maximum grows by more
 //    than 2^8 in probability; otherwise probabilities up to 2^8 accumulate
 //    against the stale maximum, which fp32 and bf16 hold exactly enough.
-//  * 64-key K and V^T stages are double-buffered in LDS behind XOR-swizzled
-//    16-byte chunks (conflict-free ds_read_b128); the next stage's global
-//    loads are in flight while the current stage is computed.  The block list
-//    of the (head, segment) is staged in LDS once.
+//  * 64-key K and V^T stages are copied straight from global memory into LDS
+//    (global_load_lds_dwordx4, no register staging) behind XOR-swizzled
+//    16-byte chunks (conflict-free ds_read_b128), double-buffered and
+//    software-pipelined so that the S^T MFMAs of the next stage overlap the
+//    softmax of the current one.  The block list of the (head, segment) is
+//    staged in LDS once.
 //
 // Generic path: a VALU kernel (one thread per query row, fp32 math) serves
 // fp32 inputs and shapes outside the MFMA kernel's range.
@@ -83,6 +85,20 @@ __global__ __launch_bounds__(256) void vt_pack_kernel(const bf16* __restrict__ V
 // ---------------------------------------------------------------------------
 // MFMA kernel
 // ---------------------------------------------------------------------------
+// Stage n of a workgroup is one 64-key piece of its key list: the selected
+// blocks j < b in list order, then the own block b (each L_B / 64 stages).
+// Iteration n overlaps, per wavefront,
+//   direct LDS copies of K(n+2) and V^T(n+1),
+//   the MFMAs of S^T(n+1),
+//   the softmax of S^T(n) and the MFMAs of O^T += V^T(n) P^T(n),
+// and ends with one barrier.  K(n) and V^T(n) each live in one of two LDS
+// buffers; the buffer a copy overwrites was last read before the previous
+// barrier.
+struct AtItem {
+  int blk, sub;
+  bool diag, valid;
+};
+
 template <int D, int LB>
 __global__ __launch_bounds__(LB * 2) __attribute__((amdgpu_waves_per_eu(2)))
 void sparse_attn_mfma_kernel(
@@ -94,15 +110,16 @@ void sparse_attn_mfma_kernel(
   constexpr int NT = NW * 64;
   constexpr int KT = AT_KT;
   constexpr int SUB = LB / KT;
-  constexpr int NC = D / 16;          // 16-wide d chunks of Q / K
-  constexpr int ND = D / 32;          // 32-row d tiles of O^T
-  constexpr int KCH = D / 8;          // 16-byte chunks per K row
-  constexpr int STAGE_CH = KT * D / 8;          // 16-byte chunks per K (or V^T) stage
-  constexpr int PER_T = STAGE_CH / NT;          // chunks per thread per stage
-  static_assert(STAGE_CH % NT == 0, "stage must split evenly over the threads");
-  constexpr float kRescale = 8.0f;    // log2 of the largest unnormalised probability
-  __shared__ __attribute__((aligned(16))) bf16 Ks[2][KT * D];
-  __shared__ __attribute__((aligned(16))) bf16 Vs[2][D * KT];
+  constexpr int NC = D / 16;            // 16-wide d chunks of Q / K
+  constexpr int ND = D / 32;            // 32-row d tiles of O^T
+  constexpr int KCH = D / 8;            // 16-byte chunks per K row
+  constexpr int PIECES = KT * D * 2 / 1024;   // 1-KB wave copies per K (or V^T) stage
+  constexpr int PER_W = PIECES / NW;
+  static_assert(PIECES % NW == 0, "stage copies must split evenly over the waves");
+  constexpr int KROWS = 1024 / (D * 2);       // K rows per 1-KB piece
+  constexpr float kRescale = 8.0f;      // log2 of the largest unnormalised probability
+  __shared__ __attribute__((aligned(1024))) bf16 Ks[2][KT * D];
+  __shared__ __attribute__((aligned(1024))) bf16 Vs[2][D * KT];
   __shared__ int lst[AT_LCAP];
 
   // ---- work item: (KV group, query block) pair, head within group ----
@@ -124,6 +141,7 @@ void sparse_attn_mfma_kernel(
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hg = lane >> 5;
   const size_t qrow0 = (size_t)b * LB + w * 32;
+  const int row_local = w * 32 + l32;
 
   // block list of (h, s): staged in LDS, AT_LCAP entries at a time
   const int32_t* sel = idx + ((size_t)h * CS + s) * k_max;
@@ -160,38 +178,50 @@ void sparse_attn_mfma_kernel(
     }
     return -1;
   };
+  auto gen = [&](const AtItem& prev) -> AtItem {
+    AtItem it{prev.blk, prev.sub + 1, prev.diag, prev.valid};
+    if (!prev.valid || it.sub < SUB) return it;
+    it.sub = 0;
+    if (prev.diag) {
+      it.valid = false;
+      return it;
+    }
+    const int j = __builtin_amdgcn_readfirstlane(next_sel());
+    it.diag = j < 0;
+    it.blk = it.diag ? b : j;
+    return it;
+  };
+  // a wave whose rows all precede the piece's first key has nothing to do
+  auto active = [&](const AtItem& it) { return !(it.diag && it.sub * KT > w * 32 + 31); };
 
   const bf16* Kg = K + (size_t)g * N * D;
   const bf16* Vg = Vt + (size_t)g * N * D;
-  u32x4 kreg[PER_T], vreg[PER_T];
 
-  auto gload = [&](int blk, int sub) {
-    const size_t key0 = (size_t)blk * LB + sub * KT;
-    const bf16* ksrc = Kg + key0 * D;
-    const bf16* vsrc = Vg + key0 * D;   // tile (key0 / 64) of V^T: D x 64 contiguous
+  // per-lane byte offsets of the 16-byte chunks this lane copies (the XOR
+  // swizzle is a function of the row only, so they are the same every stage)
+  uint32_t koff[PER_W], voff[PER_W];
 #pragma unroll
-    for (int ii = 0; ii < PER_T; ++ii) {
-      const int q = tid + ii * NT;
-      kreg[ii] = *reinterpret_cast<const u32x4*>(ksrc + (size_t)q * 8);
-      vreg[ii] = *reinterpret_cast<const u32x4*>(vsrc + (size_t)q * 8);
-    }
-  };
-  auto lstore = [&](int buf) {
+  for (int ii = 0; ii < PER_W; ++ii) {
+    const int pc = w * PER_W + ii;
+    const int krow = pc * KROWS + lane / KCH;
+    koff[ii] = (uint32_t)((krow * D + ((lane % KCH) ^ (krow & 7)) * 8) * sizeof(bf16));
+    const int vrow = pc * 8 + (lane >> 3);
+    voff[ii] = (uint32_t)((vrow * KT + ((lane & 7) ^ (vrow & 7)) * 8) * sizeof(bf16));
+  }
+  auto load_k = [&](const AtItem& it, bf16* kbuf) {
+    const bf16* src = Kg + ((size_t)it.blk * LB + it.sub * KT) * D;
 #pragma unroll
-    for (int ii = 0; ii < PER_T; ++ii) {
-      const int q = tid + ii * NT;
-      const int krow = q / KCH, kc = q % KCH;
-      *reinterpret_cast<u32x4*>(&Ks[buf][krow * D + ((kc ^ (krow & 7)) * 8)]) = kreg[ii];
-      const int vrow = q / (KT / 8), vc = q % (KT / 8);
-      *reinterpret_cast<u32x4*>(&Vs[buf][vrow * KT + ((vc ^ (vrow & 7)) * 8)]) = vreg[ii];
-    }
+    for (int ii = 0; ii < PER_W; ++ii)
+      copy16_to_lds(src, koff[ii], kbuf + (w * PER_W + ii) * 512);
   };
-
-  auto compute = [&](int buf, bool diag, int sub) {
-    if (diag && sub * KT > w * 32 + 31) return;   // wave-uniform: all keys in the future
-    const bf16* ks = Ks[buf];
-    const bf16* vs = Vs[buf];
-    floatx16 st[2];
+  auto load_v = [&](const AtItem& it, bf16* vbuf) {
+    // V^T tile of the piece: D rows of 64 keys, contiguous
+    const bf16* src = Vg + ((size_t)it.blk * LB + it.sub * KT) * D;
+#pragma unroll
+    for (int ii = 0; ii < PER_W; ++ii)
+      copy16_to_lds(src, voff[ii], vbuf + (w * PER_W + ii) * 512);
+  };
+  auto mma_s = [&](const bf16* ks, floatx16 (&st)[2]) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
@@ -205,25 +235,25 @@ void sparse_attn_mfma_kernel(
         st[kt] = mfma32(a, qf[c], st[kt]);
       }
     }
-    if (diag && (sub * KT + KT - 1 > w * 32)) {
-      const int row_local = w * 32 + l32;
+  };
+  auto softmax_pv = [&](floatx16 (&st)[2], const AtItem& it, const bf16* vs) {
+    if (it.diag && (it.sub * KT + KT - 1 > w * 32)) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
         for (int i = 0; i < 16; ++i)
-          if (sub * KT + kt * 32 + acc_row(i, lane) > row_local) st[kt][i] = -INFINITY;
+          if (it.sub * KT + kt * 32 + acc_row(i, lane) > row_local) st[kt][i] = -INFINITY;
     }
     float mx = st[0][0];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) mx = fmaxf(mx, st[kt][i]);
-    mx = fmaxf(mx, __shfl_xor(mx, 32));
+    mx = xhalf_max(mx);
     // raise the running maximum only when a row grew by more than 2^kRescale
-    const bool grow = (mx - m_run) * scale_log2 > kRescale;
-    if (__any(grow)) {
+    if (__any((mx - m_run) * scale_log2 > kRescale)) {
       const float m_new = fmaxf(m_run, mx);
-      const float alpha = exp2f((m_run - m_new) * scale_log2);
+      const float alpha = fast_exp2((m_run - m_new) * scale_log2);
       m_run = m_new;
       l_run *= alpha;
 #pragma unroll
@@ -237,7 +267,7 @@ void sparse_attn_mfma_kernel(
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
-        const float pv = exp2f(__builtin_fmaf(st[kt][i], scale_log2, -moff));
+        const float pv = fast_exp2(__builtin_fmaf(st[kt][i], scale_log2, -moff));
         l_run += pv;
         pb[kt * 2 + (i >> 3)][i & 7] = f2bf(pv);
       }
@@ -253,41 +283,46 @@ void sparse_attn_mfma_kernel(
     }
   };
 
-  int cur = next_sel();
-  bool cur_diag = false;
-  if (cur < 0) {
-    cur = b;
-    cur_diag = true;
+  // ---- prologue: K(0), V^T(0), K(1) in flight; S^T(0) ----
+  AtItem it0;
+  {
+    const int j = __builtin_amdgcn_readfirstlane(next_sel());
+    it0.diag = j < 0;
+    it0.blk = it0.diag ? b : j;
+    it0.sub = 0;
+    it0.valid = true;
   }
-  int sub = 0, buf = 0;
-  gload(cur, 0);
-  lstore(0);
+  AtItem it1 = gen(it0);
+  AtItem it2 = gen(it1);
+  load_k(it0, Ks[0]);
+  load_v(it0, Vs[0]);
+  if (it1.valid) load_k(it1, Ks[1]);
+  wait_vmem();
   __syncthreads();
-  while (true) {
-    int nblk = cur, nsub = sub + 1;
-    bool ndiag = cur_diag, has_next = true;
-    if (nsub == SUB) {
-      nsub = 0;
-      if (cur_diag) {
-        has_next = false;
-      } else {
-        nblk = next_sel();
-        ndiag = nblk < 0;
-        if (ndiag) nblk = b;
-      }
-    }
-    if (has_next) gload(nblk, nsub);
-    compute(buf, cur_diag, sub);
-    if (!has_next) break;
-    lstore(buf ^ 1);
+  floatx16 sa[2], sb[2];
+  if (active(it0)) mma_s(Ks[0], sa);
+  __syncthreads();   // every wave is done with K(0): its buffer takes K(2)
+
+  // one pipeline step over buffers fixed at compile time (even / odd stage);
+  // returns false after the last piece
+  auto step = [&](floatx16 (&s_cur)[2], floatx16 (&s_nxt)[2], bf16* k_cur, bf16* k_nxt,
+                  bf16* v_cur, bf16* v_nxt) -> bool {
+    if (it2.valid) load_k(it2, k_cur);
+    if (it1.valid) load_v(it1, v_nxt);
+    if (it1.valid && active(it1)) mma_s(k_nxt, s_nxt);
+    if (active(it0)) softmax_pv(s_cur, it0, v_cur);
+    if (!it1.valid) return false;
+    wait_vmem();
     __syncthreads();
-    buf ^= 1;
-    cur = nblk;
-    sub = nsub;
-    cur_diag = ndiag;
+    it0 = it1;
+    it1 = it2;
+    it2 = gen(it2);
+    return true;
+  };
+  while (step(sa, sb, Ks[0], Ks[1], Vs[0], Vs[1]) && step(sb, sa, Ks[1], Ks[0], Vs[1], Vs[0])) {
   }
 
-  const float lt = l_run + __shfl_xor(l_run, 32);
+  const float lt = xhalf_sum(l_run);
   const float inv = 1.0f / lt;
   bf16* op = O + ((size_t)h * N + qrow0 + l32) * D;
 #pragma unroll
@@ -369,13 +404,13 @@ __global__ __launch_bounds__(256) void sparse_attn_generic_kernel(
           sc[kk] = v;
           mx = fmaxf(mx, v);
         }
-        const float alpha = exp2f(m - mx);
+        const float alpha = fast_exp2(m - mx);
         l *= alpha;
 #pragma unroll
         for (int d = 0; d < D; ++d) o[d] *= alpha;
         m = mx;
         for (int kk = 0; kk < KT; ++kk) {
-          const float pv = exp2f(sc[kk] - mx);
+          const float pv = fast_exp2(sc[kk] - mx);
           l += pv;
 #pragma unroll
           for (int d = 0; d < D; ++d) o[d] += pv * Vs[kk][d];

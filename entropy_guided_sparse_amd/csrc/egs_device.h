@@ -31,6 +31,12 @@ __device__ __forceinline__ int acc_row(int i, int lane) {
   return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
 }
 
+// 2^x with one v_exp_f32.  Results below 2^-126 may flush to zero: every
+// caller exponentiates a logit minus a running maximum, where such terms are
+// far below the fp32 resolution of the sum they join.  exp2f() would add a
+// denormal-preserving range reduction (five more VALU operations).
+__device__ __forceinline__ float fast_exp2(float x) { return __builtin_amdgcn_exp2f(x); }
+
 __device__ __forceinline__ float bf2f(bf16 x) { return (float)x; }
 __device__ __forceinline__ bf16 f2bf(float x) { return (bf16)x; }   // RNE
 
@@ -63,6 +69,39 @@ __device__ __forceinline__ void split8(const float* x, bf16x8& hi, bf16x8& lo) {
     lo[e] = (bf16)(x[e] - (float)h);
   }
 }
+
+// Combine a value with the one held by lane l ^ 32 (v_permlane32_swap: the two
+// halves of the wave trade places without going through LDS).
+__device__ __forceinline__ float xhalf_max(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  return fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1]));
+}
+__device__ __forceinline__ float xhalf_sum(float v) {
+  const auto r = __builtin_amdgcn_permlane32_swap(__float_as_uint(v), __float_as_uint(v),
+                                                  false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+
+// Direct global -> LDS copy of 16 bytes per lane (global_load_lds_dwordx4):
+// lane i's bytes land at lds_base + 16 * i, lds_base being wave-uniform (M0).
+// Issued through inline assembly so that the compiler does not track the copy
+// as an LDS write: it would otherwise wait for every copy in flight before any
+// later LDS read, including reads of other buffers.  Callers order reads of
+// the destination with wait_vmem() and a workgroup barrier.
+typedef __attribute__((address_space(3))) void lds_void_t;
+__device__ __forceinline__ void copy16_to_lds(const void* sbase, uint32_t voff, void* lds_base) {
+  // sbase: wave-uniform global base; voff: this lane's byte offset from it
+  const uint32_t lds_addr = (uint32_t)(uintptr_t)(lds_void_t*)lds_base;
+  asm volatile(
+      "s_mov_b32 m0, %2\n\t"
+      "global_load_lds_dwordx4 %0, %1"
+      :
+      : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+      : "memory", "m0");
+}
+// Wait for this wave's outstanding vector-memory loads (direct LDS copies included).
+__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll

@@ -179,8 +179,8 @@ __global__ __launch_bounds__(256) void obs_stats_kernel(
         const float mn = fmaxf(m[rt], tmax);
         float sum = 0.f;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sum += exp2f(st[rt][i] - mn);
-        l[rt] = l[rt] * exp2f(m[rt] - mn) + sum;
+        for (int i = 0; i < 16; ++i) sum += fast_exp2(st[rt][i] - mn);
+        l[rt] = l[rt] * fast_exp2(m[rt] - mn) + sum;
         m[rt] = mn;
       }
     }
@@ -190,7 +190,7 @@ __global__ __launch_bounds__(256) void obs_stats_kernel(
   for (int rt = 0; rt < RT; ++rt) {
     const float m2 = __shfl_xor(m[rt], 32), l2 = __shfl_xor(l[rt], 32);
     const float M = fmaxf(m[rt], m2);
-    const float Lr = l[rt] * exp2f(m[rt] - M) + l2 * exp2f(m2 - M);
+    const float Lr = l[rt] * fast_exp2(m[rt] - M) + l2 * fast_exp2(m2 - M);
     const int u = rt * 32 + l32;
     if (hg == 0 && u < W) {
       const size_t o = (((size_t)b * Hq + h) * nch + chunk) * W + u;
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(256) void obs_combine_kernel(const float* __restric
   float Lr = 0.f;
   for (int c = 0; c < nch; ++c) {
     const size_t o = ((size_t)bh * nch + c) * W + u;
-    Lr += stat_l[o] * exp2f(stat_m[o] - M);
+    Lr += stat_l[o] * fast_exp2(stat_m[o] - M);
   }
   row_m[i] = M;
   row_inv[i] = Lr > 0.f ? 1.0f / Lr : 0.f;
@@ -283,7 +283,7 @@ __global__ __launch_bounds__(256) void obs_mass_kernel(
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-          float pv = exp2f(z[rt][i] * sl2 - rm[rt][i]) * ri[rt][i];
+          float pv = fast_exp2(z[rt][i] * sl2 - rm[rt][i]) * ri[rt][i];
           if (edge && t > pos0 + rt * 32 + acc_row(i, lane)) pv = 0.f;
           colsum += pv;
         }
@@ -720,7 +720,7 @@ __global__ __launch_bounds__(256) void decode_attn_split_kernel(
     mx = wave_max(mx);
     float sum = 0.f;
     for (int t = t_begin + lane; t < t_end; t += 64) {
-      const float pv = exp2f(pbuf[w][t - t_begin] - mx);
+      const float pv = fast_exp2(pbuf[w][t - t_begin] - mx);
       pbuf[w][t - t_begin] = pv;
       sum += pv;
     }
@@ -760,7 +760,7 @@ __global__ __launch_bounds__(64) void decode_attn_combine_kernel(const float* __
   for (int e = 0; e < DPL; ++e) o[e] = 0.f;
   for (int s = 0; s < nsplit; ++s) {
     const float* q = pp + (size_t)s * (D + 2);
-    const float f = exp2f(q[D] - M);
+    const float f = fast_exp2(q[D] - M);
     Lr += q[D + 1] * f;
 #pragma unroll
     for (int e = 0; e < DPL; ++e) o[e] += q[lane * DPL + e] * f;

@@ -178,14 +178,14 @@ __global__ __launch_bounds__(256) void probe_score_kernel(
       const float mn = fmaxf(m, tmax);
       float sum = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) sum += exp2f(zt[i] - mn);
-      l = l * exp2f(m - mn) + sum;
+      for (int i = 0; i < 16; ++i) sum += fast_exp2(zt[i] - mn);
+      l = l * fast_exp2(m - mn) + sum;
       m = mn;
     }
     {
       const float m2 = __shfl_xor(m, 32), l2 = __shfl_xor(l, 32);
       const float M = fmaxf(m, m2);
-      const float Lr = l * exp2f(m - M) + l2 * exp2f(m2 - M);
+      const float Lr = l * fast_exp2(m - M) + l2 * fast_exp2(m2 - M);
       if (hg == 0) {
         st_m[w][l32] = M;
         st_l[w][l32] = Lr;
@@ -198,7 +198,7 @@ __global__ __launch_bounds__(256) void probe_score_kernel(
       for (int q = 1; q < 4; ++q) M = fmaxf(M, st_m[q][tid]);
       float Lr = 0.f;
 #pragma unroll
-      for (int q = 0; q < 4; ++q) Lr += st_l[q][tid] * exp2f(st_m[q][tid] - M);
+      for (int q = 0; q < 4; ++q) Lr += st_l[q][tid] * fast_exp2(st_m[q][tid] - M);
       rowM[tid] = M;
       rowInvL[tid] = (rt * 32 + tid < P && Lr > 0.f) ? 1.0f / Lr : 0.f;
     }
@@ -228,7 +228,7 @@ __global__ __launch_bounds__(256) void probe_score_kernel(
       }
       float colsum = 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) colsum += exp2f(z[i] * scale_log2 - rm[i]) * ril[i];
+      for (int i = 0; i < 16; ++i) colsum += fast_exp2(z[i] * scale_log2 - rm[i]) * ril[i];
       colsum += __shfl_xor(colsum, 32);
       if (hg == 0 && bvalid) acc[blk] += colsum;
     }
