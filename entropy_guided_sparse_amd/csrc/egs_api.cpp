@@ -92,10 +92,6 @@ egs_status check_prefill(const egs_prefill_shape* s, PrefillDims* p) {
   return EGS_OK;
 }
 
-size_t kbar_plane_bytes(const PrefillDims& p) {
-  return round_up((size_t)p.Hkv * p.CB * p.D * 2, kWsAlign);
-}
-
 egs_status need(const void* ptr, const char* name, size_t align) {
   if (ptr == nullptr) return fail(EGS_EINVAL, "%s is NULL", name);
   if (!aligned(ptr, align)) return fail(EGS_EINVAL, "%s is not %zu-byte aligned", name, align);
@@ -168,7 +164,7 @@ const char* egs_last_error(void) {
 size_t egs_entropy_score_workspace(const egs_prefill_shape* shape) {
   PrefillDims p;
   if (check_prefill(shape, &p) != EGS_OK) return 0;
-  return 2 * kbar_plane_bytes(p);
+  return egs::score_workspace_bytes(p);
 }
 
 egs_status egs_entropy_score(const egs_prefill_shape* shape, int32_t pool_kind,
@@ -194,16 +190,13 @@ egs_status egs_entropy_score(const egs_prefill_shape* shape, int32_t pool_kind,
   if ((st = need(block_scores, "block_scores", 4)) != EGS_OK) return st;
   if ((st = need(entropy, "entropy", 4)) != EGS_OK) return st;
   if ((st = need(workspace, "workspace", kWsAlign)) != EGS_OK) return st;
-  const size_t plane = kbar_plane_bytes(p);
-  if (workspace_bytes < 2 * plane)
+  const size_t wsb = egs::score_workspace_bytes(p);
+  if (workspace_bytes < wsb)
     return fail(EGS_EWORKSPACE, "workspace of %zu bytes is below the %zu required",
-                workspace_bytes, 2 * plane);
-  char* ws = static_cast<char*>(workspace);
-  hipError_t e = egs::launch_pool_keys(p, k, ws, ws + plane, stream);
-  if (e != hipSuccess) return hip_status(e, "pool_keys launch");
-  e = egs::launch_probe_score(p, q, ws, ws + plane, kind, renyi_alpha, block_scores, entropy,
-                              stream);
-  return hip_status(e, "probe_score launch");
+                workspace_bytes, wsb);
+  return hip_status(egs::launch_entropy_score(p, q, k, kind, renyi_alpha, block_scores, entropy,
+                                              workspace, stream),
+                    "entropy_score launch");
 }
 
 egs_status egs_allocate_budget(const egs_prefill_shape* shape, const egs_budget_policy* policy,

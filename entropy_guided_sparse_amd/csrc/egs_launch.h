@@ -20,13 +20,12 @@ struct DecodeDims {
   float sm_scale;
 };
 
-// K1: mean of every key block, written as a bf16 hi/lo pair (kbar ~= hi + lo).
-hipError_t launch_pool_keys(const PrefillDims& p, const void* k, void* kb_hi,
-                            void* kb_lo, hipStream_t st);
-// K2: probe observation rows + per-(head, segment) entropy.
-hipError_t launch_probe_score(const PrefillDims& p, const void* q, const void* kb_hi,
-                              const void* kb_lo, int kind, float alpha,
-                              float* scores, float* entropy, hipStream_t st);
+// K1 + K2: key-block means (a bf16 hi/lo pair), probe observation rows and
+// per-(head, segment) entropy.  Workspace layout is owned by score.hip.
+size_t score_workspace_bytes(const PrefillDims& p);
+hipError_t launch_entropy_score(const PrefillDims& p, const void* q, const void* k, int kind,
+                                float alpha, float* scores, float* entropy, void* ws,
+                                hipStream_t st);
 // K3: head classes and budgets (float64 arithmetic).
 hipError_t launch_budget(const PrefillDims& p, const egs_budget_policy& pol,
                          const float* entropy, int8_t* rigid, int32_t* budget,
