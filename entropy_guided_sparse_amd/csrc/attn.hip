@@ -26,10 +26,12 @@
 //    against the stale maximum, which fp32 and bf16 hold exactly enough.
 //  * 64-key K and V^T stages are copied straight from global memory into LDS
 //    (global_load_lds_dwordx4, no register staging) behind XOR-swizzled
-//    16-byte chunks (conflict-free ds_read_b128), double-buffered and
-//    software-pipelined so that the S^T MFMAs of the next stage overlap the
-//    softmax of the current one.  The block list of the (head, segment) is
-//    staged in LDS once.
+//    16-byte chunks (conflict-free ds_read_b128), double-buffered: the copies
+//    of stage n+1 are in flight while stage n is computed.  Two workgroups
+//    share a CU, so one wavefront's softmax overlaps another's MFMAs.  (Also
+//    holding S^T of the next stage in registers to overlap it within a
+//    wavefront measured slower: the extra 32 registers cost LDS prefetch.)
+//    The block list of the (head, segment) is staged in LDS once.
 //
 // Generic path: a VALU kernel (one thread per query row, fp32 math) serves
 // fp32 inputs and shapes outside the MFMA kernel's range.
@@ -87,13 +89,10 @@ __global__ __launch_bounds__(256) void vt_pack_kernel(const bf16* __restrict__ V
 // ---------------------------------------------------------------------------
 // Stage n of a workgroup is one 64-key piece of its key list: the selected
 // blocks j < b in list order, then the own block b (each L_B / 64 stages).
-// Iteration n overlaps, per wavefront,
-//   direct LDS copies of K(n+2) and V^T(n+1),
-//   the MFMAs of S^T(n+1),
-//   the softmax of S^T(n) and the MFMAs of O^T += V^T(n) P^T(n),
-// and ends with one barrier.  K(n) and V^T(n) each live in one of two LDS
-// buffers; the buffer a copy overwrites was last read before the previous
-// barrier.
+// Iteration n issues the direct LDS copies of K(n+1) and V^T(n+1), computes
+// S^T(n), its softmax and O^T += V^T(n) P^T(n), and ends with one barrier.
+// K and V^T each live in two LDS buffers; the buffer a copy overwrites was
+// last read before the previous barrier.
 struct AtItem {
   int blk, sub;
   bool diag, valid;
@@ -221,22 +220,38 @@ void sparse_attn_mfma_kernel(
     for (int ii = 0; ii < PER_W; ++ii)
       copy16_to_lds(src, voff[ii], vbuf + (w * PER_W + ii) * 512);
   };
+  // LDS operand reads run two MFMA steps ahead of their use (fragments
+  // rotate through three register slots; the loops unroll fully, so every
+  // slot index is a compile-time constant)
+  auto kfrag = [&](const bf16* ks, int c, bf16x8 (&f)[2]) {
+#pragma unroll
+    for (int kt = 0; kt < 2; ++kt) {
+      const int row = kt * 32 + l32;
+      f[kt] = load8(ks + row * D + (((2 * c + hg) ^ (row & 7)) * 8));
+    }
+  };
   auto mma_s = [&](const bf16* ks, floatx16 (&st)[2]) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) st[kt][i] = 0.f;
+    bf16x8 fa[3][2];
+    kfrag(ks, 0, fa[0]);
+    if (NC > 1) kfrag(ks, 1, fa[1]);
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
+      if (c + 2 < NC) kfrag(ks, c + 2, fa[(c + 2) % 3]);
 #pragma unroll
-      for (int kt = 0; kt < 2; ++kt) {
-        const int row = kt * 32 + l32;
-        const bf16x8 a = load8(ks + row * D + (((2 * c + hg) ^ (row & 7)) * 8));
-        st[kt] = mfma32(a, qf[c], st[kt]);
-      }
+      for (int kt = 0; kt < 2; ++kt) st[kt] = mfma32(fa[c % 3][kt], qf[c], st[kt]);
     }
   };
-  auto softmax_pv = [&](floatx16 (&st)[2], const AtItem& it, const bf16* vs) {
+  // V^T fragment f = (d tile f / 4, 16-key group f % 4)
+  auto vfrag = [&](const bf16* vs, int f) -> bf16x8 {
+    const int row = (f >> 2) * 32 + l32, ch = f & 3;
+    return load8(vs + row * KT + (((2 * ch + hg) ^ (row & 7)) * 8));
+  };
+  // causal mask of the own block, row maximum and (rarely) a raised maximum
+  auto softmax_max = [&](floatx16 (&st)[2], const AtItem& it) {
     if (it.diag && (it.sub * KT + KT - 1 > w * 32)) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -261,8 +276,10 @@ void sparse_attn_mfma_kernel(
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
     }
+  };
+  // P^T = exp2(S^T - m) as the bf16 B operand, and its row sums
+  auto softmax_exp = [&](const floatx16 (&st)[2], bf16x8 (&pb)[4]) {
     const float moff = m_run * scale_log2;
-    bf16x8 pb[4];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
 #pragma unroll
@@ -272,18 +289,18 @@ void sparse_attn_mfma_kernel(
         pb[kt * 2 + (i >> 3)][i & 7] = f2bf(pv);
       }
     }
+  };
+  // fv[0], fv[1] hold V^T fragments 0 and 1 on entry
+  auto mma_pv = [&](const bf16x8 (&pb)[4], const bf16* vs, bf16x8 (&fv)[3]) {
+    constexpr int NF = ND * 4;
 #pragma unroll
-    for (int dt = 0; dt < ND; ++dt) {
-      const int row = dt * 32 + l32;
-#pragma unroll
-      for (int ch = 0; ch < 4; ++ch) {
-        const bf16x8 a = load8(vs + row * KT + (((2 * ch + hg) ^ (row & 7)) * 8));
-        o[dt] = mfma32(a, pb[ch], o[dt]);
-      }
+    for (int f = 0; f < NF; ++f) {
+      if (f + 2 < NF) fv[(f + 2) % 3] = vfrag(vs, f + 2);
+      o[f >> 2] = mfma32(fv[f % 3], pb[f & 3], o[f >> 2]);
     }
   };
 
-  // ---- prologue: K(0), V^T(0), K(1) in flight; S^T(0) ----
+  // ---- prologue: K(0), V^T(0) ----
   AtItem it0;
   {
     const int j = __builtin_amdgcn_readfirstlane(next_sel());
@@ -293,33 +310,37 @@ void sparse_attn_mfma_kernel(
     it0.valid = true;
   }
   AtItem it1 = gen(it0);
-  AtItem it2 = gen(it1);
   load_k(it0, Ks[0]);
   load_v(it0, Vs[0]);
-  if (it1.valid) load_k(it1, Ks[1]);
   wait_vmem();
   __syncthreads();
-  floatx16 sa[2], sb[2];
-  if (active(it0)) mma_s(Ks[0], sa);
-  __syncthreads();   // every wave is done with K(0): its buffer takes K(2)
 
-  // one pipeline step over buffers fixed at compile time (even / odd stage);
-  // returns false after the last piece
-  auto step = [&](floatx16 (&s_cur)[2], floatx16 (&s_nxt)[2], bf16* k_cur, bf16* k_nxt,
-                  bf16* v_cur, bf16* v_nxt) -> bool {
-    if (it2.valid) load_k(it2, k_cur);
-    if (it1.valid) load_v(it1, v_nxt);
-    if (it1.valid && active(it1)) mma_s(k_nxt, s_nxt);
-    if (active(it0)) softmax_pv(s_cur, it0, v_cur);
+  // one pipeline step over buffers fixed at compile time (even / odd stage):
+  // the copies of stage n+1 fly while stage n is computed; returns false
+  // after the last piece
+  auto step = [&](bf16* k_cur, bf16* k_nxt, bf16* v_cur, bf16* v_nxt) -> bool {
+    if (it1.valid) {
+      load_k(it1, k_nxt);
+      load_v(it1, v_nxt);
+    }
+    if (active(it0)) {
+      floatx16 st[2];
+      bf16x8 pb[4], fv[3];
+      mma_s(k_cur, st);
+      fv[0] = vfrag(v_cur, 0);   // V^T reads in flight during the softmax
+      fv[1] = vfrag(v_cur, 1);
+      softmax_max(st, it0);
+      softmax_exp(st, pb);
+      mma_pv(pb, v_cur, fv);
+    }
     if (!it1.valid) return false;
     wait_vmem();
     __syncthreads();
     it0 = it1;
-    it1 = it2;
-    it2 = gen(it2);
+    it1 = gen(it1);
     return true;
   };
-  while (step(sa, sb, Ks[0], Ks[1], Vs[0], Vs[1]) && step(sb, sa, Ks[1], Ks[0], Vs[1], Vs[0])) {
+  while (step(Ks[0], Ks[1], Vs[0], Vs[1]) && step(Ks[1], Ks[0], Vs[1], Vs[0])) {
   }
 
   const float lt = xhalf_sum(l_run);
