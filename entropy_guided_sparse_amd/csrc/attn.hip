@@ -203,9 +203,10 @@ void sparse_attn_mfma_kernel(
   for (int ii = 0; ii < PER_W; ++ii) {
     const int pc = w * PER_W + ii;
     const int krow = pc * KROWS + lane / KCH;
-    koff[ii] = (uint32_t)((krow * D + ((lane % KCH) ^ (krow & 7)) * 8) * sizeof(bf16));
+    koff[ii] = (uint32_t)((krow * D + ((lane % KCH) ^ lds_swz<D * 2>(krow)) * 8) *
+                          sizeof(bf16));
     const int vrow = pc * 8 + (lane >> 3);
-    voff[ii] = (uint32_t)((vrow * KT + ((lane & 7) ^ (vrow & 7)) * 8) * sizeof(bf16));
+    voff[ii] = (uint32_t)((vrow * KT + ((lane & 7) ^ lds_swz<KT * 2>(vrow)) * 8) * sizeof(bf16));
   }
   auto load_k = [&](const AtItem& it, bf16* kbuf) {
     const bf16* src = Kg + ((size_t)it.blk * LB + it.sub * KT) * D;
@@ -227,7 +228,7 @@ void sparse_attn_mfma_kernel(
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
       const int row = kt * 32 + l32;
-      f[kt] = load8(ks + row * D + (((2 * c + hg) ^ (row & 7)) * 8));
+      f[kt] = load8(ks + row * D + (((2 * c + hg) ^ lds_swz<D * 2>(row)) * 8));
     }
   };
   auto mma_s = [&](const bf16* ks, floatx16 (&st)[2]) {
@@ -248,7 +249,7 @@ void sparse_attn_mfma_kernel(
   // V^T fragment f = (d tile f / 4, 16-key group f % 4)
   auto vfrag = [&](const bf16* vs, int f) -> bf16x8 {
     const int row = (f >> 2) * 32 + l32, ch = f & 3;
-    return load8(vs + row * KT + (((2 * ch + hg) ^ (row & 7)) * 8));
+    return load8(vs + row * KT + (((2 * ch + hg) ^ lds_swz<KT * 2>(row)) * 8));
   };
   // causal mask of the own block, row maximum and (rarely) a raised maximum
   auto softmax_max = [&](floatx16 (&st)[2], const AtItem& it) {

@@ -102,6 +102,14 @@ __device__ __forceinline__ void copy16_to_lds(const void* sbase, uint32_t voff, 
 }
 // Wait for this wave's outstanding vector-memory loads (direct LDS copies included).
 __device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
+// Wait until at most N of this wave's vector-memory operations are in flight.
+// Loads retire in issue order, so with only direct LDS copies outstanding this
+// waits for every copy except the N issued last.
+template <int N>
+__device__ __forceinline__ void wait_vmem_upto() {
+  static_assert(N >= 0 && N <= 63, "vmcnt range");
+  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+}
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
@@ -132,6 +140,20 @@ __device__ __forceinline__ int wave_incl_scan(int v) {
     if (lane >= o) v += t;
   }
   return v;
+}
+
+// XOR swizzle of the 16-byte chunks of LDS rows of ROW_BYTES bytes.  The LDS
+// serves 256 bytes (16 chunks) per cycle, i.e. the 16 lanes of a quarter
+// wave per ds_read_b128; operand reads have those lanes on 16 consecutive
+// rows at one logical chunk.  Rows sharing a 256-byte window are told apart
+// by their offset in it, rows in different windows by the XOR, so the 16
+// reads land in 16 distinct chunk slots.
+template <int ROW_BYTES>
+__device__ __forceinline__ int lds_swz(int row) {
+  constexpr int CPR = ROW_BYTES / 16;               // chunks per row
+  constexpr int RPW = CPR >= 16 ? 1 : 16 / CPR;     // rows per 256-byte window
+  constexpr int MASK = (CPR >= 16 ? 16 : CPR) - 1;
+  return (row / RPW) & MASK;
 }
 
 // Order-preserving map of float bits onto unsigned integers.

@@ -34,12 +34,12 @@
 namespace egs {
 
 constexpr int RT_CK = 1024;   // keys per chunk (pass 1 / pass 2 work unit)
-constexpr int RT_KS = 128;    // keys per LDS stage
+constexpr int RT_KT = 64;     // keys per LDS stage
 constexpr int SEL_T = 1024;   // threads of the select kernel
 constexpr int DA_SPL = 512;   // keys per decode-attention split
 
 struct RetainLayout {
-  size_t stat_m, stat_l, row_m, row_inv, mass, ent, weight, mu, qsum, total;
+  size_t stat_m, stat_l, row_m, row_inv, mass, ent, weight, mu, qsum, tstats, total;
   int nch;
 };
 
@@ -66,6 +66,7 @@ static RetainLayout retain_layout(const DecodeDims& p) {
   o.weight = take((size_t)p.B * p.Hq * 4);
   o.mu = take((size_t)p.B * p.Hkv * p.L * 4);
   o.qsum = take((size_t)p.B * p.Hkv * p.D * 4);
+  o.tstats = take((size_t)p.B * 2 * 4);
   o.total = off;
   return o;
 }
@@ -77,19 +78,31 @@ size_t retain_workspace_bytes(const DecodeDims& p) {
 // ---------------------------------------------------------------------------
 // shared pieces of pass 1 / pass 2
 // ---------------------------------------------------------------------------
+// 64-key K stages copied straight into LDS (global_load_lds_dwordx4) by the
+// four wavefronts, 16-byte chunks XOR-swizzled by row; rows past the chunk's
+// last key repeat that key (in bounds) and are masked by the consumer.
 template <int D>
-struct KStage {
-  static constexpr int KPAD = D + 8;
-  static constexpr int CH = RT_KS * D / 8;   // 16-byte chunks per stage
-  // cooperative copy of keys [t0, t0 + RT_KS) (zero past t_end) into LDS
-  __device__ static void load(bf16* Ks, const bf16* Kg, int t0, int t_end) {
-    for (int q = threadIdx.x; q < CH; q += 256) {
-      const int row = q / (D / 8), c8 = q % (D / 8);
-      const int t = t0 + row;
-      u32x4 v = {0u, 0u, 0u, 0u};
-      if (t < t_end) v = *reinterpret_cast<const u32x4*>(Kg + (size_t)t * D + c8 * 8);
-      *reinterpret_cast<u32x4*>(Ks + row * KPAD + c8 * 8) = v;
+struct KPipe {
+  static constexpr int PIECES = RT_KT * D * 2 / 1024;   // 1-KB wave copies per stage
+  static constexpr int PER_W = PIECES / 4;
+  static constexpr int KROWS = 1024 / (D * 2);          // K rows per piece
+  static constexpr int KCH = D / 8;
+  static_assert(PIECES % 4 == 0, "stage copies must split evenly over four waves");
+  __device__ static void copy(bf16* kbuf, const bf16* Kg, int t0, int t_last, int w,
+                              int lane) {
+    const bf16* src = Kg + (size_t)t0 * D;
+#pragma unroll
+    for (int ii = 0; ii < PER_W; ++ii) {
+      const int pc = w * PER_W + ii;
+      const int row = pc * KROWS + lane / KCH;
+      const int c = (lane % KCH) ^ lds_swz<D * 2>(row);
+      const int t = min(t0 + row, t_last);
+      copy16_to_lds(src, (uint32_t)(((t - t0) * D + c * 8) * sizeof(bf16)), kbuf + pc * 512);
     }
+  }
+  // the 8 bf16 of key row `row` (0..63 in the stage), d chunk (2c + hg)
+  __device__ static bf16x8 frag(const bf16* kbuf, int row, int c, int hg) {
+    return load8(kbuf + row * D + (((2 * c + hg) ^ lds_swz<D * 2>(row)) * 8));
   }
 };
 
@@ -115,15 +128,28 @@ __device__ __forceinline__ void load_obs_q(bf16x8 (&qf)[RT][D / 16], const bf16*
 }
 
 // ---------------------------------------------------------------------------
-// pass 1: per-chunk running max / sum of every observer row
+// pass 1 (MASS = false): per-chunk running max / sum of every observer row.
+// pass 2 (MASS = true): per-head window-mean mass of every key and the
+// chunk's sink-isolated entropy partial sums.
+// Workgroup = (1024-key chunk, batch x KV group, 4-head group); the four
+// wavefronts (one query head each) share every K stage.  Stages are copied
+// RT_DEPTH - 1 ahead of the one being computed (four LDS buffers), so each
+// workgroup keeps three 16-KB copies in flight against HBM latency; the pass-2
+// masses collect in LDS and leave after the loop, so that only the copies
+// are outstanding while the loop waits on them.
 // ---------------------------------------------------------------------------
-template <int D, int RT>
-__global__ __launch_bounds__(256) void obs_stats_kernel(
+constexpr int RT_DEPTH = 4;
+
+template <int D, int RT, bool MASS>
+__global__ __launch_bounds__(256) void obs_pass_kernel(
     const bf16* __restrict__ Qo, const bf16* __restrict__ K, int Hq, int Hkv, int r, int L,
-    int W, int nch, float sl2, float* __restrict__ stat_m, float* __restrict__ stat_l) {
+    int W, int nch, float sl2, float* __restrict__ stat_m, float* __restrict__ stat_l,
+    const float* __restrict__ row_m, const float* __restrict__ row_inv, int n_sink, int kind,
+    float alpha, float* __restrict__ mass, float* __restrict__ ent) {
   constexpr int NC = D / 16;
-  constexpr int KPAD = KStage<D>::KPAD;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[RT_KS * KPAD];
+  constexpr int PW = KPipe<D>::PER_W;
+  __shared__ __attribute__((aligned(1024))) bf16 Ks[RT_DEPTH][RT_KT * D];
+  __shared__ float mbuf[MASS ? 4 * RT_CK : 1];
   const int chunk = blockIdx.x, bg = blockIdx.y;
   const int b = bg / Hkv, g = bg % Hkv;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -131,6 +157,11 @@ __global__ __launch_bounds__(256) void obs_stats_kernel(
   const int hl = blockIdx.z * 4 + w;
   const bool hvalid = hl < r;
   const int h = g * r + (hvalid ? hl : 0);
+  const int t_begin = chunk * RT_CK, t_end = min(L, t_begin + RT_CK);
+  const int nst = (t_end - t_begin + RT_KT - 1) / RT_KT;
+  const bf16* Kg = K + (size_t)bg * L * D;
+  const int pos0 = L - W;   // observer u sits at pos0 + u
+
   bf16x8 qf[RT][NC];
   load_obs_q<D, RT>(qf, Qo, b, h, Hq, W, hvalid, lane);
   float m[RT], l[RT];
@@ -139,172 +170,176 @@ __global__ __launch_bounds__(256) void obs_stats_kernel(
     m[rt] = kNegBig;
     l[rt] = 0.f;
   }
-  const int t_begin = chunk * RT_CK, t_end = min(L, t_begin + RT_CK);
-  const bf16* Kg = K + (size_t)bg * L * D;
-  const int pos0 = L - W;   // observer u sits at pos0 + u
-  for (int t0 = t_begin; t0 < t_end; t0 += RT_KS) {
-    __syncthreads();
-    KStage<D>::load(Ks, Kg, t0, t_end);
-    __syncthreads();
-    if (!hvalid) continue;
-    for (int kt = 0; kt < RT_KS / 32; ++kt) {
-      const int tk = t0 + kt * 32;
-      if (tk >= t_end) break;
-      floatx16 st[RT];
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) st[rt][i] = 0.f;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const bf16x8 a = load8(Ks + (kt * 32 + l32) * KPAD + 16 * c + 8 * hg);
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) st[rt] = mfma32(a, qf[rt][c], st[rt]);
-      }
-      const bool edge = (tk + 31 >= t_end) || (tk + 31 > pos0);
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const int u = rt * 32 + l32;
-        float tmax = kNegBig;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float v = st[rt][i] * sl2;
-          if (edge) {
-            const int t = tk + acc_row(i, lane);
-            if (t >= t_end || t > pos0 + u) v = -INFINITY;
-          }
-          st[rt][i] = v;
-          tmax = fmaxf(tmax, v);
-        }
-        const float mn = fmaxf(m[rt], tmax);
-        float sum = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) sum += fast_exp2(st[rt][i] - mn);
-        l[rt] = l[rt] * fast_exp2(m[rt] - mn) + sum;
-        m[rt] = mn;
-      }
-    }
-  }
-  if (!hvalid) return;
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const float m2 = __shfl_xor(m[rt], 32), l2 = __shfl_xor(l[rt], 32);
-    const float M = fmaxf(m[rt], m2);
-    const float Lr = l[rt] * fast_exp2(m[rt] - M) + l2 * fast_exp2(m2 - M);
-    const int u = rt * 32 + l32;
-    if (hg == 0 && u < W) {
-      const size_t o = (((size_t)b * Hq + h) * nch + chunk) * W + u;
-      stat_m[o] = M;
-      stat_l[o] = Lr;
-    }
-  }
-}
-
-__global__ __launch_bounds__(256) void obs_combine_kernel(const float* __restrict__ stat_m,
-                                                          const float* __restrict__ stat_l,
-                                                          int rows, int nch, int W,
-                                                          float* __restrict__ row_m,
-                                                          float* __restrict__ row_inv) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= rows) return;
-  const int bh = i / W, u = i % W;
-  float M = kNegBig;
-  for (int c = 0; c < nch; ++c) M = fmaxf(M, stat_m[((size_t)bh * nch + c) * W + u]);
-  float Lr = 0.f;
-  for (int c = 0; c < nch; ++c) {
-    const size_t o = ((size_t)bh * nch + c) * W + u;
-    Lr += stat_l[o] * fast_exp2(stat_m[o] - M);
-  }
-  row_m[i] = M;
-  row_inv[i] = Lr > 0.f ? 1.0f / Lr : 0.f;
-}
-
-// ---------------------------------------------------------------------------
-// pass 2: per-head window-mean mass and sink-isolated entropy partial sums
-// ---------------------------------------------------------------------------
-template <int D, int RT>
-__global__ __launch_bounds__(256) void obs_mass_kernel(
-    const bf16* __restrict__ Qo, const bf16* __restrict__ K, int Hq, int Hkv, int r, int L,
-    int W, int nch, float sl2, const float* __restrict__ row_m,
-    const float* __restrict__ row_inv, int n_sink, int kind, float alpha,
-    float* __restrict__ mass, float* __restrict__ ent) {
-  constexpr int NC = D / 16;
-  constexpr int KPAD = KStage<D>::KPAD;
-  __shared__ __attribute__((aligned(16))) bf16 Ks[RT_KS * KPAD];
-  const int chunk = blockIdx.x, bg = blockIdx.y;
-  const int b = bg / Hkv, g = bg % Hkv;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int l32 = lane & 31, hg = lane >> 5;
-  const int hl = blockIdx.z * 4 + w;
-  const bool hvalid = hl < r;
-  const int h = g * r + (hvalid ? hl : 0);
-  bf16x8 qf[RT][NC];
-  load_obs_q<D, RT>(qf, Qo, b, h, Hq, W, hvalid, lane);
-  float rm[RT][16], ri[RT][16];
-  const size_t rbase = ((size_t)b * Hq + h) * W;
-#pragma unroll
-  for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-    for (int i = 0; i < 16; ++i) {
-      const int u = rt * 32 + acc_row(i, lane);
-      const bool ok = hvalid && u < W;
-      rm[rt][i] = ok ? row_m[rbase + u] : 0.f;
-      ri[rt][i] = ok ? row_inv[rbase + u] : 0.f;
-    }
-  const float invW = 1.0f / (float)W;
+  // pass 2: the final statistics of the rows this lane's registers hold
+  float rm[RT][16];
   float s1 = 0.f, s2 = 0.f;
-  const int t_begin = chunk * RT_CK, t_end = min(L, t_begin + RT_CK);
-  const bf16* Kg = K + (size_t)bg * L * D;
-  float* mrow = mass + ((size_t)b * Hq + h) * L;
-  const int pos0 = L - W;
-  for (int t0 = t_begin; t0 < t_end; t0 += RT_KS) {
-    __syncthreads();
-    KStage<D>::load(Ks, Kg, t0, t_end);
-    __syncthreads();
-    if (!hvalid) continue;
-    for (int kt = 0; kt < RT_KS / 32; ++kt) {
+  const float invW = 1.0f / (float)W;
+  if (MASS) {
+    const size_t rbase = ((size_t)b * Hq + h) * W;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const int u = rt * 32 + acc_row(i, lane);
+        const bool ok = hvalid && u < W;
+        // exp2(z sl2 - M) / L = exp2(z sl2 - (M + log2 L)); rows past the
+        // window get an infinite offset, i.e. probability 0
+        const float inv = ok ? row_inv[rbase + u] : 0.f;
+        rm[rt][i] = ok && inv > 0.f ? row_m[rbase + u] - __log2f(inv) : INFINITY;
+      }
+  }
+  wait_vmem();   // only the copies below are in flight from here on
+#pragma unroll
+  for (int d = 0; d < RT_DEPTH - 1; ++d)
+    if (d < nst) KPipe<D>::copy(Ks[d], Kg, t_begin + d * RT_KT, t_end - 1, w, lane);
+
+  auto compute = [&](const bf16* ks, int t0) {
+#pragma unroll
+    for (int kt = 0; kt < RT_KT / 32; ++kt) {
       const int tk = t0 + kt * 32;
       if (tk >= t_end) break;
+      // keys past the chunk or after an observer's position are masked
+      const bool edge = (tk + 31 >= t_end) || (tk + 31 > pos0);
       floatx16 z[RT];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) z[rt][i] = 0.f;
+      if (!MASS) {
+        // S^T: lane owns observer row (rt*32 + l32), registers hold keys
 #pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const bf16x8 bk = load8(Ks + (kt * 32 + l32) * KPAD + 16 * c + 8 * hg);
+        for (int c = 0; c < NC; ++c) {
+          const bf16x8 a = KPipe<D>::frag(ks, kt * 32 + l32, c, hg);
 #pragma unroll
-        for (int rt = 0; rt < RT; ++rt) z[rt] = mfma32(qf[rt][c], bk, z[rt]);
-      }
-      const int t = tk + l32;            // this lane's key
-      const bool edge = tk + 31 > pos0;  // causal mask only near the end
-      float colsum = 0.f;
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          float pv = fast_exp2(z[rt][i] * sl2 - rm[rt][i]) * ri[rt][i];
-          if (edge && t > pos0 + rt * 32 + acc_row(i, lane)) pv = 0.f;
-          colsum += pv;
+          for (int rt = 0; rt < RT; ++rt) z[rt] = mfma32(a, qf[rt][c], z[rt]);
         }
-      colsum += __shfl_xor(colsum, 32);
-      if (hg == 0 && t < t_end) {
-        const float a = colsum * invW;
-        mrow[t] = a;
-        if (t >= n_sink && a > 0.f) {
-          s1 += a;
-          s2 += (kind == EGS_SHANNON) ? a * logf(a) : powf(a, alpha);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          const int u = rt * 32 + l32;
+          if (edge) {
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              const int t = tk + acc_row(i, lane);
+              if (t >= t_end || t > pos0 + u) z[rt][i] = -INFINITY;
+            }
+          }
+          float tmax = z[rt][0];
+#pragma unroll
+          for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, z[rt][i]);
+          // m is kept in log2 units (logit * sl2); sl2 > 0 commutes with max
+          const float mn = fmaxf(m[rt], tmax * sl2);
+          float sum = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sum += fast_exp2(__builtin_fmaf(z[rt][i], sl2, -mn));
+          l[rt] = l[rt] * fast_exp2(m[rt] - mn) + sum;
+          m[rt] = mn;
+        }
+      } else {
+        // Z: lane owns key (tk + l32), registers hold observer rows
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const bf16x8 bk = KPipe<D>::frag(ks, kt * 32 + l32, c, hg);
+#pragma unroll
+          for (int rt = 0; rt < RT; ++rt) z[rt] = mfma32(qf[rt][c], bk, z[rt]);
+        }
+        const int t = tk + l32;
+        float colsum = 0.f;
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            float pv = fast_exp2(__builtin_fmaf(z[rt][i], sl2, -rm[rt][i]));
+            if (edge && t > pos0 + rt * 32 + acc_row(i, lane)) pv = 0.f;
+            colsum += pv;
+          }
+        colsum = xhalf_sum(colsum);
+        if (hg == 0 && t < t_end) {
+          const float a = colsum * invW;
+          mbuf[w * RT_CK + (t - t_begin)] = a;
+          if (t >= n_sink && a > 0.f) {
+            s1 += a;
+            s2 += (kind == EGS_SHANNON) ? a * logf(a) : powf(a, alpha);
+          }
         }
       }
     }
+  };
+  // stage st sits in buffer st % RT_DEPTH; iteration st copies stage
+  // st + RT_DEPTH - 1 into the buffer stage st - 1 used
+  for (int st = 0; st < nst; ++st) {
+    const int ahead = min(RT_DEPTH - 2, nst - 1 - st);   // copies issued after stage st's
+    if (ahead >= 2) wait_vmem_upto<2 * PW>();
+    else if (ahead == 1) wait_vmem_upto<PW>();
+    else wait_vmem();
+    __syncthreads();
+    if (st + RT_DEPTH - 1 < nst)
+      KPipe<D>::copy(Ks[(st + RT_DEPTH - 1) % RT_DEPTH], Kg, t_begin + (st + RT_DEPTH - 1) * RT_KT,
+                     t_end - 1, w, lane);
+    if (hvalid) compute(Ks[st % RT_DEPTH], t_begin + st * RT_KT);
   }
   if (!hvalid) return;
-  s1 = wave_sum(s1);
-  s2 = wave_sum(s2);
-  if (lane == 0) {
-    float* e = ent + (((size_t)b * Hq + h) * nch + chunk) * 2;
-    e[0] = s1;
-    e[1] = s2;
+  if (!MASS) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const float M = xhalf_max(m[rt]);
+      const float Lr = xhalf_sum(l[rt] * fast_exp2(m[rt] - M));
+      const int u = rt * 32 + l32;
+      if (hg == 0 && u < W) {
+        const size_t o = (((size_t)b * Hq + h) * nch + chunk) * W + u;
+        stat_m[o] = M;
+        stat_l[o] = Lr;
+      }
+    }
+  } else {
+    // this wave's own masses: written and read by the same wavefront
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+    float* mrow = mass + ((size_t)b * Hq + h) * L;
+    for (int t = t_begin + lane; t < t_end; t += 64) mrow[t] = mbuf[w * RT_CK + (t - t_begin)];
+    s1 = wave_sum(s1);
+    s2 = wave_sum(s2);
+    if (lane == 0) {
+      float* e = ent + (((size_t)b * Hq + h) * nch + chunk) * 2;
+      e[0] = s1;
+      e[1] = s2;
+    }
+  }
+}
+
+// the rows' final maximum and 1/sum: one workgroup per (batch, head); the
+// W rows of the head each get 256 / W threads that split the chunks
+__global__ __launch_bounds__(256) void obs_combine_kernel(const float* __restrict__ stat_m,
+                                                          const float* __restrict__ stat_l,
+                                                          int nch, int W,
+                                                          float* __restrict__ row_m,
+                                                          float* __restrict__ row_inv) {
+  __shared__ float pm[256], pl[256];
+  const int bh = blockIdx.x, tid = threadIdx.x;
+  const int parts = max(1, 256 / W);
+  const int u = tid % W, part = tid / W;
+  const bool on = tid < parts * W;
+  float M = kNegBig, Lr = 0.f;
+  if (on) {
+    const float* sm = stat_m + (size_t)bh * nch * W + u;
+    const float* sl = stat_l + (size_t)bh * nch * W + u;
+    for (int c = part; c < nch; c += parts) {
+      const float mc = sm[(size_t)c * W], lc = sl[(size_t)c * W];
+      const float mn = fmaxf(M, mc);
+      Lr = Lr * fast_exp2(M - mn) + lc * fast_exp2(mc - mn);
+      M = mn;
+    }
+  }
+  pm[tid] = M;
+  pl[tid] = Lr;
+  __syncthreads();
+  if (tid < W) {
+    float Mt = kNegBig;
+    for (int q = 0; q < parts; ++q) Mt = fmaxf(Mt, pm[q * W + tid]);
+    float Lt = 0.f;
+    for (int q = 0; q < parts; ++q) Lt += pl[q * W + tid] * fast_exp2(pm[q * W + tid] - Mt);
+    row_m[(size_t)bh * W + tid] = Mt;
+    row_inv[(size_t)bh * W + tid] = Lt > 0.f ? 1.0f / Lt : 0.f;
   }
 }
 
@@ -368,7 +403,8 @@ __global__ __launch_bounds__(256) void raw_qsum_kernel(const bf16* __restrict__ 
 template <int D>
 __global__ __launch_bounds__(256) void raw_score_kernel(const bf16* __restrict__ K,
                                                         const float* __restrict__ qsum, int L,
-                                                        float* __restrict__ mu) {
+                                                        float* __restrict__ mu,
+                                                        float* __restrict__ scores) {
   __shared__ float qs[D];
   const int bg = blockIdx.y;
   for (int d = threadIdx.x; d < D; d += 256) qs[d] = qsum[(size_t)bg * D + d];
@@ -385,6 +421,7 @@ __global__ __launch_bounds__(256) void raw_score_kernel(const bf16* __restrict__
     for (int e = 0; e < 8; ++e) acc += x[e] * qs[8 * c + e];
   }
   mu[(size_t)bg * L + t] = acc;
+  if (scores != nullptr) scores[(size_t)bg * L + t] = acc;
 }
 
 // ---------------------------------------------------------------------------
@@ -435,46 +472,69 @@ __device__ __forceinline__ int block_excl_scan_1024(int v, int* red) {
   return base + incl - v;
 }
 
-__global__ __launch_bounds__(SEL_T) void retain_select_kernel(
-    const float* __restrict__ mass, const float* __restrict__ weight,
-    const float* __restrict__ token_entropy, int raw, float info_alpha, int Hq, int Hkv, int r,
-    int L, int n_sink, int n_recent, int n_keep, int n_total, float* __restrict__ mu,
-    float* __restrict__ scores, int32_t* __restrict__ keep_idx) {
-  __shared__ int hist[4096];
-  __shared__ int ired[SEL_T / 64];
+// InfoKV fusion input: per batch, the maximum of the token entropies and the
+// sum of exp(E - max) over the cache (one workgroup per batch)
+__global__ __launch_bounds__(SEL_T) void token_softmax_stats_kernel(const float* __restrict__ E,
+                                                                    int L,
+                                                                    float* __restrict__ stats) {
   __shared__ float fred[SEL_T / 64];
-  __shared__ int sh_digit, sh_above;
-  const int bg = blockIdx.x, b = bg / Hkv, g = bg % Hkv;
-  const int tid = threadIdx.x;
-  float* mu_row = mu + (size_t)bg * L;
-
-  // ---- mu_t ----
-  if (!raw) {
-    __shared__ float wv[16];
-    if (tid < r) wv[tid] = weight[(size_t)b * Hq + g * r + tid];
-    __syncthreads();
-    const float* mrow = mass + ((size_t)b * Hq + g * r) * L;
-    for (int t = tid; t < L; t += SEL_T) {
-      float acc = 0.f;
-      for (int hl = 0; hl < r; ++hl) acc += wv[hl] * mrow[(size_t)hl * L + t];
-      mu_row[t] = acc;
-    }
-    if (token_entropy != nullptr && info_alpha < 1.0f) {
-      const float* E = token_entropy + (size_t)b * L;
-      float mx = -INFINITY;
-      for (int t = tid; t < L; t += SEL_T) mx = fmaxf(mx, E[t]);
-      mx = block_max_1024f(mx, fred);
-      float se = 0.f;
-      for (int t = tid; t < L; t += SEL_T) se += expf(E[t] - mx);
-      se = block_sum_1024f(se, fred);
-      const float inv = 1.0f / se;
-      for (int t = tid; t < L; t += SEL_T)
-        mu_row[t] = info_alpha * mu_row[t] + (1.0f - info_alpha) * (expf(E[t] - mx) * inv);
-    }
+  const int b = blockIdx.x, tid = threadIdx.x;
+  const float* e = E + (size_t)b * L;
+  float mx = -INFINITY;
+  for (int t = tid; t < L; t += SEL_T) mx = fmaxf(mx, e[t]);
+  mx = block_max_1024f(mx, fred);
+  float se = 0.f;
+  for (int t = tid; t < L; t += SEL_T) se += expf(e[t] - mx);
+  se = block_sum_1024f(se, fred);
+  if (tid == 0) {
+    stats[2 * b] = mx;
+    stats[2 * b + 1] = 1.0f / se;
   }
-  __syncthreads();
-  if (scores != nullptr)
-    for (int t = tid; t < L; t += SEL_T) scores[(size_t)bg * L + t] = mu_row[t];
+}
+
+// group score mu_t = sum_{h in g} w_h a^h_t, optionally fused with the
+// softmax of the token entropies; one thread per (batch x KV group, key)
+__global__ __launch_bounds__(256) void retain_mu_kernel(
+    const float* __restrict__ mass, const float* __restrict__ weight,
+    const float* __restrict__ token_entropy, const float* __restrict__ tstats,
+    float info_alpha, int Hq, int Hkv, int r, int L, float* __restrict__ mu,
+    float* __restrict__ scores) {
+  const int bg = blockIdx.y, b = bg / Hkv, g = bg % Hkv;
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= L) return;
+  const float* mrow = mass + ((size_t)b * Hq + g * r) * L + t;
+  const float* wv = weight + (size_t)b * Hq + g * r;
+  float acc = 0.f;
+  for (int hl = 0; hl < r; ++hl) acc += wv[hl] * mrow[(size_t)hl * L];
+  if (token_entropy != nullptr) {
+    const float sm = expf(token_entropy[(size_t)b * L + t] - tstats[2 * b]) * tstats[2 * b + 1];
+    acc = info_alpha * acc + (1.0f - info_alpha) * sm;
+  }
+  mu[(size_t)bg * L + t] = acc;
+  if (scores != nullptr) scores[(size_t)bg * L + t] = acc;
+}
+
+// exact top-n_keep of mu over the candidates and ascending compaction of the
+// keep set; one workgroup per (batch, KV group).
+//   radix select: 12 / 12 / 8-bit digits of the order-preserving key, each
+//     pass a coalesced sweep over the candidates (eight loads in flight per
+//     thread) into an LDS histogram, then a scan that fixes the digit;
+//   compaction: rounds of SEL_R consecutive keys staged in LDS with coalesced
+//     loads; each thread takes SEL_R / SEL_T consecutive keys, one block scan
+//     of (selected, tied) counts places them, ties to T taken by lower index.
+constexpr int SEL_R = 16384;
+constexpr int SEL_U = 8;
+
+__global__ __launch_bounds__(SEL_T) void retain_select_kernel(
+    const float* __restrict__ mu, int L, int n_sink, int n_recent, int n_keep, int n_total,
+    int32_t* __restrict__ keep_idx) {
+  __shared__ int hist[4096];
+  __shared__ uint32_t keys[SEL_R];
+  __shared__ int ired[SEL_T / 64];
+  __shared__ int sh_digit, sh_above, tot_sel, tot_eq;
+  const int bg = blockIdx.x;
+  const int tid = threadIdx.x;
+  const float* mu_row = mu + (size_t)bg * L;
 
   const bool keep_all = (long long)n_sink + n_recent + n_keep >= L;
   const int c_lo = n_sink, c_hi = L - n_recent;   // candidates [c_lo, c_hi)
@@ -482,16 +542,25 @@ __global__ __launch_bounds__(SEL_T) void retain_select_kernel(
   int kr = n_keep;
   const bool partial = !keep_all && n_keep > 0;
   if (partial) {
-    // 12 / 12 / 8-bit radix select of the n_keep-th largest key
     const int shifts[3] = {20, 8, 0};
     const int bits[3] = {12, 12, 8};
     for (int ps = 0; ps < 3; ++ps) {
       const int sh = shifts[ps], nb = 1 << bits[ps];
       for (int i = tid; i < 4096; i += SEL_T) hist[i] = 0;
       __syncthreads();
-      for (int t = c_lo + tid; t < c_hi; t += SEL_T) {
-        const uint32_t key = orderable(mu_row[t]);
-        if ((key & mask) == prefix) atomicAdd(&hist[(key >> sh) & (uint32_t)(nb - 1)], 1);
+      for (int t0 = c_lo; t0 < c_hi; t0 += SEL_T * SEL_U) {
+        uint32_t kv[SEL_U];
+#pragma unroll
+        for (int u = 0; u < SEL_U; ++u) {
+          const int t = t0 + u * SEL_T + tid;
+          kv[u] = t < c_hi ? orderable(mu_row[t]) : 0u;
+        }
+#pragma unroll
+        for (int u = 0; u < SEL_U; ++u) {
+          const int t = t0 + u * SEL_T + tid;
+          if (t < c_hi && (kv[u] & mask) == prefix)
+            atomicAdd(&hist[(kv[u] >> sh) & (uint32_t)(nb - 1)], 1);
+        }
       }
       __syncthreads();
       // thread tid owns digits nb-1-4*tid .. nb-4-4*tid (descending)
@@ -525,34 +594,70 @@ __global__ __launch_bounds__(SEL_T) void retain_select_kernel(
       __syncthreads();
     }
   }
-  const uint32_t T = prefix;
+  const uint32_t T = prefix;   // key of the n_keep-th candidate; kr ties to T are kept
 
-  // ---- ascending compaction over [0, L): contiguous chunk per thread ----
-  const int E = (L + SEL_T - 1) / SEL_T;
-  const int j0 = min(L, tid * E), j1 = min(L, j0 + E);
-  int n_eq = 0;
-  if (partial)
-    for (int t = max(j0, c_lo); t < min(j1, c_hi); ++t) n_eq += (orderable(mu_row[t]) == T);
-  const int eq0 = block_excl_scan_1024(n_eq, ired);
-  auto take = [&](int t, int& es) -> bool {
-    if (keep_all || t < c_lo || t >= c_hi) return true;
-    if (!partial) return false;
-    const uint32_t key = orderable(mu_row[t]);
-    if (key > T) return true;
-    if (key == T) return (es++) < kr;
-    return false;
-  };
-  int n_sel = 0;
-  {
-    int es = eq0;
-    for (int t = j0; t < j1; ++t) n_sel += take(t, es) ? 1 : 0;
-  }
-  int pos = block_excl_scan_1024(n_sel, ired);
+  // ---- ascending compaction over [0, L) ----
+  constexpr int PER = SEL_R / SEL_T;
   int32_t* out = keep_idx + (size_t)bg * n_total;
-  {
-    int es = eq0;
-    for (int t = j0; t < j1; ++t)
-      if (take(t, es) && pos < n_total) out[pos++] = t;
+  int base_sel = 0, base_eq = 0;   // kept and tied entries before this round
+  for (int r0 = 0; r0 < L; r0 += SEL_R) {
+    const int rn = min(SEL_R, L - r0);
+    __syncthreads();   // the previous round's keys are consumed
+#pragma unroll 4
+    for (int i = tid; i < rn; i += SEL_T) keys[i] = orderable(mu_row[r0 + i]);
+    __syncthreads();
+    const int j0 = tid * PER;
+    int n_sel = 0, n_eq = 0;
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int j = j0 + e, t = r0 + j;
+      if (j < rn) {
+        const bool cand = t >= c_lo && t < c_hi;
+        if (!cand || keep_all) {
+          ++n_sel;
+        } else if (partial) {
+          n_sel += keys[j] > T;
+          n_eq += keys[j] == T;
+        }
+      }
+    }
+    // one scan of both counts (each below 2^16 per round); the ties kept
+    // before this thread are the first kr ties in index order
+    const int packed = block_excl_scan_1024((n_sel << 16) | n_eq, ired);
+    int es = base_eq + (packed & 0xFFFF);
+    int pos = base_sel + (packed >> 16) + min(es, kr);
+#pragma unroll
+    for (int e = 0; e < PER; ++e) {
+      const int j = j0 + e, t = r0 + j;
+      if (j < rn) {
+        const bool cand = t >= c_lo && t < c_hi;
+        bool take;
+        if (!cand || keep_all) {
+          take = true;
+        } else if (!partial) {
+          take = false;
+        } else if (keys[j] > T) {
+          take = true;
+        } else if (keys[j] == T) {
+          take = es < kr;
+          ++es;
+        } else {
+          take = false;
+        }
+        if (take) {
+          if (pos < n_total) out[pos] = t;
+          ++pos;
+        }
+      }
+    }
+    // round totals: the last thread's exclusive prefix plus its own counts
+    if (tid == SEL_T - 1) {
+      tot_sel = (packed >> 16) + n_sel;
+      tot_eq = (packed & 0xFFFF) + n_eq;
+    }
+    __syncthreads();
+    base_sel += tot_sel;
+    base_eq += tot_eq;
   }
 }
 
@@ -598,17 +703,18 @@ static hipError_t retain_passes(const DecodeDims& p, const RetainLayout& lay, ch
   float* stat_l = reinterpret_cast<float*>(ws + lay.stat_l);
   float* row_m = reinterpret_cast<float*>(ws + lay.row_m);
   float* row_inv = reinterpret_cast<float*>(ws + lay.row_inv);
-  obs_stats_kernel<D, RT><<<grid, 256, 0, st>>>(Qo, K, p.Hq, p.Hkv, p.r, p.L, p.W, lay.nch, sl2,
-                                                stat_m, stat_l);
+  float* mass = reinterpret_cast<float*>(ws + lay.mass);
+  float* ent = reinterpret_cast<float*>(ws + lay.ent);
+  obs_pass_kernel<D, RT, false><<<grid, 256, 0, st>>>(Qo, K, p.Hq, p.Hkv, p.r, p.L, p.W, lay.nch,
+                                                      sl2, stat_m, stat_l, row_m, row_inv,
+                                                      p.n_sink, kind, alpha, mass, ent);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int rows = p.B * p.Hq * p.W;
-  obs_combine_kernel<<<(rows + 255) / 256, 256, 0, st>>>(stat_m, stat_l, rows, lay.nch, p.W,
-                                                         row_m, row_inv);
+  obs_combine_kernel<<<p.B * p.Hq, 256, 0, st>>>(stat_m, stat_l, lay.nch, p.W, row_m, row_inv);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  obs_mass_kernel<D, RT><<<grid, 256, 0, st>>>(
-      Qo, K, p.Hq, p.Hkv, p.r, p.L, p.W, lay.nch, sl2, row_m, row_inv, p.n_sink, kind, alpha,
-      reinterpret_cast<float*>(ws + lay.mass), reinterpret_cast<float*>(ws + lay.ent));
+  obs_pass_kernel<D, RT, true><<<grid, 256, 0, st>>>(Qo, K, p.Hq, p.Hkv, p.r, p.L, p.W, lay.nch,
+                                                     sl2, stat_m, stat_l, row_m, row_inv,
+                                                     p.n_sink, kind, alpha, mass, ent);
   return hipGetLastError();
 }
 
@@ -650,9 +756,11 @@ hipError_t launch_kv_retain(const DecodeDims& p, const egs_retain_params& prm, c
     dim3 grid((p.L + 255) / 256, p.B * p.Hkv);
     float* mu = reinterpret_cast<float*>(ws + lay.mu);
     if (p.D == 128)
-      raw_score_kernel<128><<<grid, 256, 0, st>>>(static_cast<const bf16*>(k), qsum, p.L, mu);
+      raw_score_kernel<128><<<grid, 256, 0, st>>>(static_cast<const bf16*>(k), qsum, p.L, mu,
+                                                  scores);
     else
-      raw_score_kernel<64><<<grid, 256, 0, st>>>(static_cast<const bf16*>(k), qsum, p.L, mu);
+      raw_score_kernel<64><<<grid, 256, 0, st>>>(static_cast<const bf16*>(k), qsum, p.L, mu,
+                                                 scores);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (head_entropy != nullptr) {
       const int n = p.B * p.Hq;
@@ -660,10 +768,23 @@ hipError_t launch_kv_retain(const DecodeDims& p, const egs_retain_params& prm, c
       if ((e = hipGetLastError()) != hipSuccess) return e;
     }
   }
-  retain_select_kernel<<<p.B * p.Hkv, SEL_T, 0, st>>>(
-      reinterpret_cast<const float*>(ws + lay.mass), reinterpret_cast<const float*>(ws + lay.weight),
-      raw ? nullptr : token_entropy, raw, (float)prm.info_alpha, p.Hq, p.Hkv, p.r, p.L, p.n_sink,
-      p.n_recent, p.n_keep, p.n_total, reinterpret_cast<float*>(ws + lay.mu), scores, keep_idx);
+  float* mu = reinterpret_cast<float*>(ws + lay.mu);
+  if (!raw) {
+    const bool fuse = token_entropy != nullptr && prm.info_alpha < 1.0;
+    float* tstats = reinterpret_cast<float*>(ws + lay.tstats);
+    if (fuse) {
+      token_softmax_stats_kernel<<<p.B, SEL_T, 0, st>>>(token_entropy, p.L, tstats);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+    dim3 grid((p.L + 255) / 256, p.B * p.Hkv);
+    retain_mu_kernel<<<grid, 256, 0, st>>>(
+        reinterpret_cast<const float*>(ws + lay.mass),
+        reinterpret_cast<const float*>(ws + lay.weight), fuse ? token_entropy : nullptr, tstats,
+        (float)prm.info_alpha, p.Hq, p.Hkv, p.r, p.L, mu, scores);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  retain_select_kernel<<<p.B * p.Hkv, SEL_T, 0, st>>>(mu, p.L, p.n_sink, p.n_recent, p.n_keep,
+                                                       p.n_total, keep_idx);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   if (k_out != nullptr) {
     const long long units = (long long)p.B * p.Hkv * p.n_total * (p.D / 8);

@@ -175,12 +175,10 @@ struct QFrag<float> {
   __device__ static void split(const raw_t& v, bf16x8& hi, bf16x8& lo) { split8(v.x, hi, lo); }
 };
 
-// XOR mask of the row-swizzled 16-byte chunks of a D-wide bf16 row: rows
-// with at least 8 chunks swizzle over 8, narrower rows over all their chunks.
+// XOR swizzle of the 16-byte chunks of a D-wide bf16 row in LDS
 template <int D>
 __device__ __forceinline__ int kbar_swz(int row) {
-  constexpr int KCH = D / 8;
-  return row & (KCH >= 8 ? 7 : KCH - 1);
+  return lds_swz<D * 2>(row);
 }
 
 // Stage the hi / lo pooled keys of blocks c0 .. c0 + nb - 1 (zero beyond) in

@@ -180,3 +180,27 @@ def test_decode_attention_keep_all_is_dense(api):
         torch.from_numpy(np.repeat(inp.v, 4, axis=1).astype(np.float64)))[:, :, 0].numpy()
     ma, rel = attn_errors(res["out"].float().cpu().numpy(), ref)
     assert ma <= ATTN_MAX_ABS and rel <= ATTN_REL_L2
+
+
+def test_retain_all_scores_tied(api):
+    """Zero keys make every observer's attention uniform over its visible keys,
+    so all candidates (all visible to every observer) tie exactly: the keep set
+    is the first n_keep candidates by index, on the GPU as in the oracle."""
+    B, Hq, Hkv, d, L, W = 1, 4, 1, 128, 4096, 64
+    n_sink, n_recent, n_keep = 4, 256, 300
+    log(f"[retain ties] L={L} keep={n_keep}")
+    rng = np.random.default_rng(11)
+    q_obs = synth.round_to_bf16(rng.standard_normal((B, Hq, W, d)).astype(np.float32))
+    k = np.zeros((B, Hkv, L, d), dtype=np.int16)
+    v = synth.round_to_bf16(rng.standard_normal((B, Hkv, L, d)).astype(np.float32))
+    shape = api.DecodeShape(B, Hq, Hkv, d, L, W, n_sink, n_recent, n_keep)
+    res = api.kv_retain(shape, api.RetainParams(), dev_tensor(q_obs, "bf16"),
+                        dev_tensor(k, "bf16"), dev_tensor(v, "bf16"), want_scores=True)
+    torch.cuda.synchronize()
+    keep = res["keep_idx"].cpu().numpy()[0, 0]
+    want = np.array(list(range(n_sink)) + list(range(n_sink, n_sink + n_keep)) +
+                    list(range(L - n_recent, L)))
+    np.testing.assert_array_equal(keep, want)
+    o_keep, o_mu, _ = O.kv_retain_slice(synth.bf16_bits_to_f32(q_obs)[0], np.zeros((L, d)),
+                                        n_sink, n_recent, n_keep)
+    np.testing.assert_array_equal(o_keep, want)
