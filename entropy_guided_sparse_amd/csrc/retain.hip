@@ -36,7 +36,7 @@ namespace egs {
 constexpr int RT_CK = 1024;   // keys per chunk (pass 1 / pass 2 work unit)
 constexpr int RT_KT = 64;     // keys per LDS stage
 constexpr int SEL_T = 1024;   // threads of the select kernel
-constexpr int DA_SPL = 512;   // keys per decode-attention split
+constexpr int DA_SPL = 256;   // kept entries per decode-attention split
 
 struct RetainLayout {
   size_t stat_m, stat_l, row_m, row_inv, mass, ent, weight, mu, qsum, tstats, total;
@@ -805,66 +805,111 @@ hipError_t launch_kv_retain(const DecodeDims& p, const egs_retain_params& prm, c
 // ---------------------------------------------------------------------------
 // K8: decode attention over the kept entries
 // ---------------------------------------------------------------------------
+// One workgroup per (split of DA_SPL kept entries, batch x KV group); the GQA
+// group's query heads (one per wavefront, four at a time) share every 64-entry
+// K / V stage, copied straight into LDS two stages deep.
+//   QK: a lane owns one entry of the stage; the head's query is broadcast from
+//       LDS; the entry's K row is read as swizzled 16-byte chunks.
+//   softmax: online per head over the split (wave max / sum per stage).
+//   PV: a lane owns D/64 output dims; the probabilities come from LDS.
+// Each split leaves its unnormalised output, maximum and sum for the combine.
 template <int D>
 __global__ __launch_bounds__(256) void decode_attn_split_kernel(
     const bf16* __restrict__ Qn, const bf16* __restrict__ K, const bf16* __restrict__ V,
     int Hq, int Hkv, int r, int n, int nsplit, float sl2, float* __restrict__ part) {
-  constexpr int DPL = D / 64;    // output dims per lane
-  __shared__ float pbuf[4][DA_SPL];
+  constexpr int DPL = D / 64;          // output dims per lane
+  constexpr int KCH = D / 8;           // 16-byte chunks per row
+  constexpr int ST = 64;               // entries per stage
+  constexpr int PIECES = ST * D * 2 / 1024;
+  constexpr int PER_W = PIECES / 4;
+  constexpr int KROWS = 1024 / (D * 2);
+  static_assert(PIECES % 4 == 0, "stage copies must split over four waves");
+  __shared__ __attribute__((aligned(1024))) bf16 Ks[2][ST * D];
+  __shared__ __attribute__((aligned(1024))) bf16 Vs[2][ST * D];
+  __shared__ float qsh[4][D];
+  __shared__ float psh[4][ST];
   const int sp = blockIdx.x, bg = blockIdx.y, b = bg / Hkv, g = bg % Hkv;
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int t_begin = sp * DA_SPL, t_end = min(n, t_begin + DA_SPL);
+  const int nst = (t_end - t_begin + ST - 1) / ST;
   const bf16* Kg = K + (size_t)bg * n * D;
   const bf16* Vg = V + (size_t)bg * n * D;
-  for (int hl = w; hl < r; hl += 4) {
-    const int h = g * r + hl;
-    const bf16* q = Qn + ((size_t)b * Hq + h) * D;
-    float qv[D];
+  // K and V rows share one layout: swizzled 16-byte chunks
+  auto copy_stage = [&](int st, int buf) {
+    const int t0 = t_begin + st * ST;
 #pragma unroll
-    for (int c = 0; c < D / 8; ++c) load8f(q + 8 * c, qv + 8 * c);
-    // logits: lane owns keys t_begin + lane + 64 j
-    float mx = kNegBig;
-    for (int t = t_begin + lane; t < t_end; t += 64) {
-      const bf16* kr = Kg + (size_t)t * D;
-      float acc = 0.f;
-#pragma unroll
-      for (int c = 0; c < D / 8; ++c) {
-        float x[8];
-        load8f(kr + 8 * c, x);
-#pragma unroll
-        for (int e = 0; e < 8; ++e) acc += qv[8 * c + e] * x[e];
-      }
-      const float s = acc * sl2;
-      pbuf[w][t - t_begin] = s;
-      mx = fmaxf(mx, s);
+    for (int ii = 0; ii < PER_W; ++ii) {
+      const int pc = w * PER_W + ii;
+      const int row = pc * KROWS + lane / KCH;
+      const int c = (lane % KCH) ^ lds_swz<D * 2>(row);
+      const int t = min(t0 + row, t_end - 1);   // past the split: a repeated row, masked
+      const uint32_t off = (uint32_t)(((t - t0) * D + c * 8) * sizeof(bf16));
+      copy16_to_lds(Kg + (size_t)t0 * D, off, Ks[buf] + pc * 512);
+      copy16_to_lds(Vg + (size_t)t0 * D, off, Vs[buf] + pc * 512);
     }
-    mx = wave_max(mx);
-    float sum = 0.f;
-    for (int t = t_begin + lane; t < t_end; t += 64) {
-      const float pv = fast_exp2(pbuf[w][t - t_begin] - mx);
-      pbuf[w][t - t_begin] = pv;
-      sum += pv;
+  };
+  for (int hl0 = 0; hl0 < r; hl0 += 4) {
+    const int hl = hl0 + w;
+    const bool hv = hl < r;
+    const int h = g * r + (hv ? hl : 0);
+    {
+      const bf16* q = Qn + ((size_t)b * Hq + h) * D;
+      for (int d = lane; d < D; d += 64) qsh[w][d] = hv ? bf2f(q[d]) * sl2 : 0.f;
     }
-    sum = wave_sum(sum);
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
-    float o[DPL];
+    copy_stage(0, 0);
+    float m = kNegBig, l = 0.f, o[DPL];
 #pragma unroll
     for (int e = 0; e < DPL; ++e) o[e] = 0.f;
-    for (int t = t_begin; t < t_end; ++t) {
-      const float pv = pbuf[w][t - t_begin];
-      const bf16* vr = Vg + (size_t)t * D + lane * DPL;
+    for (int st = 0; st < nst; ++st) {
+      wait_vmem();
+      __syncthreads();   // stage st landed; every wave is done with stage st-1
+      if (st + 1 < nst) copy_stage(st + 1, (st + 1) & 1);
+      const bf16* ks = Ks[st & 1];
+      const bf16* vs = Vs[st & 1];
+      const int t = t_begin + st * ST + lane;
+      // logit of this lane's entry (log2 units)
+      float z = 0.f;
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) o[e] += pv * bf2f(vr[e]);
-    }
-    float* pp = part + (((size_t)b * Hq + h) * nsplit + sp) * (D + 2);
+      for (int c = 0; c < KCH; ++c) {
+        float x[8];
+        const bf16x8 kv = load8(ks + lane * D + ((c ^ lds_swz<D * 2>(lane)) * 8));
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) pp[lane * DPL + e] = o[e];
-    if (lane == 0) {
-      pp[D] = mx;
-      pp[D + 1] = sum;
+        for (int e = 0; e < 8; ++e) x[e] = (float)kv[e];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) z = __builtin_fmaf(qsh[w][8 * c + e], x[e], z);
+      }
+      if (t >= t_end) z = -INFINITY;
+      const float mx = fmaxf(m, wave_max(z));
+      const float pz = fast_exp2(z - mx);
+      const float alpha = fast_exp2(m - mx);
+      l = l * alpha + wave_sum(pz);
+      m = mx;
+      psh[w][lane] = pz;
+      __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+      __builtin_amdgcn_wave_barrier();
+      __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) o[e] *= alpha;
+      // dims DPL*lane .. : chunk (DPL*lane)/8 of every V row
+      const int d0 = DPL * lane, c = d0 / 8, off = d0 % 8;
+#pragma unroll 8
+      for (int k = 0; k < ST; ++k) {
+        const float pk = psh[w][k];
+        const bf16* vr = vs + k * D + ((c ^ lds_swz<D * 2>(k)) * 8) + off;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) o[e] = __builtin_fmaf(pk, bf2f(vr[e]), o[e]);
+      }
     }
-    __builtin_amdgcn_wave_barrier();
+    if (hv) {
+      float* pp = part + (((size_t)b * Hq + h) * nsplit + sp) * (D + 2);
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) pp[DPL * lane + e] = o[e];
+      if (lane == 0) {
+        pp[D] = m;
+        pp[D + 1] = l;
+      }
+    }
+    __syncthreads();   // the stage buffers are reused by the next head group
   }
 }
 
