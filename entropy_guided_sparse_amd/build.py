@@ -24,6 +24,8 @@ COMMON = [
     "-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",
     # no packed-fp32 instructions anywhere in device code
     "-Xclang", "-target-feature", "-Xclang", "-packed-fp32-ops",
+    # MFMA results stay in VGPRs (no accumulator-register copies before VALU use)
+    "-mllvm", "-amdgpu-mfma-vgpr-form",
     "-Wno-unused-command-line-argument",
     "-I", os.path.join(ROOT, "include"),
 ]

@@ -28,6 +28,8 @@
 //  * Decode attention splits the kept range in 512-key chunks (one wavefront
 //    per query head, lane-per-key dot products, LDS-broadcast probabilities)
 //    and combines the chunks with their log-sum-exp.
+#include <type_traits>
+
 #include "egs_device.h"
 #include "egs_launch.h"
 
@@ -193,13 +195,14 @@ __global__ __launch_bounds__(256) void obs_pass_kernel(
   for (int d = 0; d < RT_DEPTH - 1; ++d)
     if (d < nst) KPipe<D>::copy(Ks[d], Kg, t_begin + d * RT_KT, t_end - 1, w, lane);
 
-  auto compute = [&](const bf16* ks, int t0) {
+  // EDGE: the stage holds keys past the chunk or after an observer position
+  auto compute = [&](const bf16* ks, int t0, auto edge_tag) {
+    constexpr bool EDGE = decltype(edge_tag)::value;
 #pragma unroll
     for (int kt = 0; kt < RT_KT / 32; ++kt) {
       const int tk = t0 + kt * 32;
       if (tk >= t_end) break;
-      // keys past the chunk or after an observer's position are masked
-      const bool edge = (tk + 31 >= t_end) || (tk + 31 > pos0);
+      const bool edge = EDGE && ((tk + 31 >= t_end) || (tk + 31 > pos0));
       floatx16 z[RT];
 #pragma unroll
       for (int rt = 0; rt < RT; ++rt)
@@ -258,7 +261,9 @@ __global__ __launch_bounds__(256) void obs_pass_kernel(
           mbuf[w * RT_CK + (t - t_begin)] = a;
           if (t >= n_sink && a > 0.f) {
             s1 += a;
-            s2 += (kind == EGS_SHANNON) ? a * logf(a) : powf(a, alpha);
+            // one v_log_f32: a ln a, or a^alpha = 2^(alpha log2 a)
+            const float lg = __log2f(a);
+            s2 += (kind == EGS_SHANNON) ? a * lg * kLn2 : fast_exp2(alpha * lg);
           }
         }
       }
@@ -275,7 +280,13 @@ __global__ __launch_bounds__(256) void obs_pass_kernel(
     if (st + RT_DEPTH - 1 < nst)
       KPipe<D>::copy(Ks[(st + RT_DEPTH - 1) % RT_DEPTH], Kg, t_begin + (st + RT_DEPTH - 1) * RT_KT,
                      t_end - 1, w, lane);
-    if (hvalid) compute(Ks[st % RT_DEPTH], t_begin + st * RT_KT);
+    if (hvalid) {
+      const int t0 = t_begin + st * RT_KT;
+      if (t0 + RT_KT - 1 >= t_end || t0 + RT_KT - 1 > pos0)
+        compute(Ks[st % RT_DEPTH], t0, std::true_type{});
+      else
+        compute(Ks[st % RT_DEPTH], t0, std::false_type{});
+    }
   }
   if (!hvalid) return;
   if (!MASS) {
