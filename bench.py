@@ -39,6 +39,9 @@ def parse_args():
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time spent on the oracle sample")
     ap.add_argument("--json-out", default=None)
+    ap.add_argument("--calib-copy-mib", type=int, default=0,
+                    help="also run one plain copy of this many MiB (a known-size kernel "
+                         "that scales HBM byte counters taken under a profiler)")
     return ap.parse_args()
 
 
@@ -92,6 +95,48 @@ def scoring_bytes(cfg, k_max, elt):
             + Hq * CS * CB * 4                # observation rows written
             + Hq * CS * 4 * 2                 # entropy, budgets
             + Hq * CS * k_max * 4 + Hq * CS * 4)  # block lists, counts
+
+
+TRAFFIC_FILE = "traffic_sparse_attn_llama3-8b-128k.txt"
+ATTN_SOURCES = ("entropy_guided_sparse_amd/csrc/attn.hip", "entropy_guided_sparse_amd/csrc/egs_device.h")
+
+
+def attn_source_hash():
+    import hashlib
+    root = os.path.dirname(os.path.abspath(__file__))
+    h = hashlib.sha256()
+    for rel in ATTN_SOURCES:
+        with open(os.path.join(root, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(cfg_name):
+    """HBM bytes per launch of the attention kernel from the stored counter summary,
+    or None if there is none or the kernel's source has changed since it was taken."""
+    path = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles", TRAFFIC_FILE)
+    if cfg_name != "llama3-8b-128k" or not os.path.exists(path):
+        return None
+    rec = {}
+    for line in open(path):
+        m = line.strip().strip("`").split(":", 1)
+        if len(m) == 2 and m[0].strip() in ("bytes_per_launch", "source_sha256_16"):
+            rec[m[0].strip()] = m[1].strip()
+    if rec.get("source_sha256_16") != attn_source_hash() or "bytes_per_launch" not in rec:
+        return None
+    return int(rec["bytes_per_launch"])
+
+
+def calib_copy(torch, dev, mib):
+    """One elementwise copy of `mib` MiB (read mib, write mib): torch.neg on fp32."""
+    n = mib * (1 << 20) // 4
+    x = torch.ones(n, dtype=torch.float32, device=dev)
+    y = torch.empty_like(x)
+    torch.cuda.synchronize()
+    torch.neg(x, out=y)
+    torch.cuda.synchronize()
+    log(f"calibration copy: {mib} MiB read + {mib} MiB written by one torch.neg kernel")
+    del x, y
 
 
 def cpu_baseline(cfg, inp, idx, cnt, seconds):
@@ -258,14 +303,9 @@ def main():
     eff_tflops = exec_flops / (t_prefill * 1e-3) / 1e12
     dense_equiv = dense_tiles * tile_flops / (t_prefill * 1e-3) / 1e12
 
-    traffic = None
-    prof = os.path.join(os.path.dirname(os.path.abspath(__file__)), "profiles",
-                        "traffic_sparse_attn_llama3-8b-128k.json")
-    if os.path.exists(prof) and cfg.name == "llama3-8b-128k":
-        try:
-            traffic = json.load(open(prof)).get("bytes_per_launch")
-        except Exception:
-            traffic = None
+    traffic = measured_traffic(cfg.name)
+    if args.calib_copy_mib > 0:
+        calib_copy(torch, dev, args.calib_copy_mib)
 
     res = {
         "metric": "sparse prefill ms/layer + effective TFLOP/s at 128k; scoring-pass GB/s",

@@ -13,21 +13,24 @@
 // always kept; compaction preserves token order (EntroPrefill Sec. 8.1).
 //
 // gfx950 design:
-//  * Pass 1 (obs_stats): one workgroup per (1024-key chunk, batch x KV group,
-//    4-head group).  128-key K stages are staged in LDS and shared by the four
-//    wavefronts (one query head each); S^T = K Q^T on v_mfma_f32_32x32x16_bf16
-//    gives every lane one observer row: running max / sum in registers.
-//  * A combine kernel folds the per-chunk statistics into each row's final
-//    max and 1/sum.
-//  * Pass 2 (obs_mass) recomputes the logits with keys as the N dimension, so
-//    a lane owns one key and the window mean is a register sum; it writes the
-//    per-head mass and the per-chunk sink-isolated entropy partial sums.
-//  * head_weight turns the partial sums into H_h and w_h; retain_select forms
-//    mu_t, runs an exact 12/12/8-bit radix select over the candidates in LDS
-//    and compacts the kept indices in ascending order; gather copies K/V rows.
-//  * Decode attention splits the kept range in 512-key chunks (one wavefront
-//    per query head, lane-per-key dot products, LDS-broadcast probabilities)
-//    and combines the chunks with their log-sum-exp.
+//  * Both passes run obs_pass_kernel: one workgroup per (1024-key chunk,
+//    batch x KV group, 4-head group).  64-key K stages are copied straight
+//    into LDS, four deep, and shared by the four wavefronts (one query head
+//    each); the logits of a stage take v_mfma_f32_32x32x16_bf16.
+//    Pass 1 (keys as M: a lane owns an observer row) keeps the chunk's
+//    running max / sum of every row; a combine kernel folds the chunks into
+//    each row's final max and 1/sum.  Pass 2 recomputes the logits with keys
+//    as N, so a lane owns one key and the window mean is a register sum; it
+//    writes the per-head mass and the chunk's sink-isolated entropy partial
+//    sums.
+//  * head_weight turns the partial sums into H_h and w_h; retain_mu forms
+//    mu_t; retain_select runs an exact 12/12/8-bit radix select over the
+//    candidates and compacts the kept indices in ascending order through LDS;
+//    gather copies the kept K/V rows.
+//  * Decode attention splits the kept range into 256-entry chunks; the GQA
+//    group's heads share each 64-entry K / V stage in LDS (lane-per-entry dot
+//    products, lane-per-dim PV) and a combine kernel merges the chunks with
+//    their log-sum-exp.
 #include <type_traits>
 
 #include "egs_device.h"

@@ -14,12 +14,21 @@
 //  * K1 streams K once from HBM (16-byte loads along d, fp32 sums) and writes
 //    the block means as a bf16 hi/lo pair, so the probe logits can run on
 //    bf16 MFMA with ~2^-17 relative error (two MFMAs per product).
-//  * K2 runs one workgroup per (head, segment), heaviest segments first.  Each
-//    32-row probe tile is scored against 32-block tiles with
-//    v_mfma_f32_32x32x16_bf16 twice: pass 1 with blocks as the M dimension
-//    (a lane owns a probe row: running max / sum in registers), pass 2 with
-//    blocks as the N dimension (a lane owns a block: the probe average is a
-//    register sum).  No logits are stored.
+//  * K2 splits the causal blocks of every (segment, KV group) into chunks of
+//    64 blocks; a workgroup stages one chunk's hi/lo block means in LDS once
+//    and scores the probe rows of all r heads of the group against it on
+//    v_mfma_f32_32x32x16_bf16.  Four kernels, no logits stored:
+//      probe_stats   blocks as M: a lane owns a probe row; the chunk's row
+//                    maximum and sum of exponentials;
+//      probe_combine the chunks' (max, sum) pairs folded into each row's
+//                    maximum and 1/sum;
+//      probe_mass    blocks as N: a lane owns a block; the probe-averaged mass
+//                    is a register sum, written as the block's score, with
+//                    the chunk's entropy partial sum;
+//      probe_entropy the partial sums of every (head, segment) added in chunk
+//                    order.
+//    Work items run on a 1-D grid with every chunk of a (segment, group) on
+//    one XCD, so its probe queries and block means are fetched into one L2.
 #include "egs_device.h"
 #include "egs_launch.h"
 
