@@ -100,16 +100,23 @@ __device__ __forceinline__ void copy16_to_lds(const void* sbase, uint32_t voff, 
       : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
       : "memory", "m0");
 }
-// Wait for this wave's outstanding vector-memory loads (direct LDS copies included).
-__device__ __forceinline__ void wait_vmem() { asm volatile("s_waitcnt vmcnt(0)" ::: "memory"); }
 // Wait until at most N of this wave's vector-memory operations are in flight.
 // Loads retire in issue order, so with only direct LDS copies outstanding this
-// waits for every copy except the N issued last.
+// waits for every copy except the N issued last.  The wait goes through the
+// s_waitcnt builtin (gfx9 encoding: vmcnt in bits 3:0 and 15:14, expcnt and
+// lgkmcnt left at their maxima) rather than inline assembly, so the compiler's
+// own wait tracking sees it: loads it issued earlier (e.g. register operands
+// fetched before a pipelined loop) are then known to be complete, and it does
+// not wait for them again inside the loop, where such a wait would also stall
+// on the copies in flight.
 template <int N>
 __device__ __forceinline__ void wait_vmem_upto() {
   static_assert(N >= 0 && N <= 63, "vmcnt range");
-  asm volatile("s_waitcnt vmcnt(%0)" ::"n"(N) : "memory");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
+// Wait for all of this wave's outstanding vector-memory loads (direct LDS
+// copies included).
+__device__ __forceinline__ void wait_vmem() { wait_vmem_upto<0>(); }
 
 __device__ __forceinline__ float wave_max(float v) {
 #pragma unroll
