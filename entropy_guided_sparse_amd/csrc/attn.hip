@@ -42,6 +42,10 @@ namespace egs {
 
 constexpr int AT_KT = 64;     // keys per LDS stage and per V^T tile
 constexpr int AT_LCAP = 512;  // block-list entries staged in LDS at a time
+constexpr int PV_AHEAD = 3;   // V^T fragments read ahead of their MFMA
+
+// The compiler schedules nothing across this point.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 
 // Key order inside a 16-key group of a V^T tile: the k-slot order of the P^T
 // operand as it leaves the S^T accumulator.  Keys 0-3 sit at positions 0-3,
@@ -137,7 +141,8 @@ void sparse_attn_mfma_kernel(
   const int h = g * r + hl;
   const int s = (b * LB) / LS;
 
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hg = lane >> 5;
   const size_t qrow0 = (size_t)b * LB + w * 32;
   const int row_local = w * 32 + l32;
@@ -210,20 +215,23 @@ void sparse_attn_mfma_kernel(
   }
   auto load_k = [&](const AtItem& it, bf16* kbuf) {
     const bf16* src = Kg + ((size_t)it.blk * LB + it.sub * KT) * D;
+    const uint32_t dst = lds_u32(kbuf) + w * PER_W * 1024;
 #pragma unroll
-    for (int ii = 0; ii < PER_W; ++ii)
-      copy16_to_lds(src, koff[ii], kbuf + (w * PER_W + ii) * 512);
+    for (int ii = 0; ii < PER_W; ++ii) copy16_to_lds_at(src, koff[ii], dst + ii * 1024);
   };
   auto load_v = [&](const AtItem& it, bf16* vbuf) {
     // V^T tile of the piece: D rows of 64 keys, contiguous
     const bf16* src = Vg + ((size_t)it.blk * LB + it.sub * KT) * D;
+    const uint32_t dst = lds_u32(vbuf) + w * PER_W * 1024;
 #pragma unroll
-    for (int ii = 0; ii < PER_W; ++ii)
-      copy16_to_lds(src, voff[ii], vbuf + (w * PER_W + ii) * 512);
+    for (int ii = 0; ii < PER_W; ++ii) copy16_to_lds_at(src, voff[ii], dst + ii * 1024);
   };
-  // LDS operand reads run two MFMA steps ahead of their use (fragments
-  // rotate through three register slots; the loops unroll fully, so every
-  // slot index is a compile-time constant)
+  // LDS operand reads run ahead of their use: K fragments two d chunks
+  // ahead (three register slots), V^T fragments PV_AHEAD MFMAs ahead.  The
+  // loops unroll fully, so every slot index is a compile-time constant, and a
+  // scheduling fence after each read group keeps the compiler from sinking
+  // the reads back next to their use (it does so to save registers, and
+  // every MFMA then waits out a full LDS latency).
   auto kfrag = [&](const bf16* ks, int c, bf16x8 (&f)[2]) {
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt) {
@@ -242,13 +250,15 @@ void sparse_attn_mfma_kernel(
 #pragma unroll
     for (int c = 0; c < NC; ++c) {
       if (c + 2 < NC) kfrag(ks, c + 2, fa[(c + 2) % 3]);
+      sched_fence();
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt) st[kt] = mfma32(fa[c % 3][kt], qf[c], st[kt]);
+      sched_fence();
     }
   };
-  // V^T fragment f = (d tile f / 4, 16-key group f % 4)
+  // V^T fragment f in PV order: 16-key group q = f / ND, d tile f % ND
   auto vfrag = [&](const bf16* vs, int f) -> bf16x8 {
-    const int row = (f >> 2) * 32 + l32, ch = f & 3;
+    const int row = (f % ND) * 32 + l32, ch = f / ND;
     return load8(vs + row * KT + (((2 * ch + hg) ^ lds_swz<KT * 2>(row)) * 8));
   };
   // causal mask of the own block, row maximum and (rarely) a raised maximum
@@ -278,27 +288,40 @@ void sparse_attn_mfma_kernel(
         for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
     }
   };
-  // P^T = exp2(S^T - m) as the bf16 B operand, and its row sums
-  auto softmax_exp = [&](const floatx16 (&st)[2], bf16x8 (&pb)[4]) {
-    const float moff = m_run * scale_log2;
+  // P^T of 16-key group q = exp2(S^T - m) as a bf16 B operand (accumulator
+  // tile q / 2, slots 8 (q % 2) .. 8 (q % 2) + 7), and its row sum
+  auto softmax_exp = [&](const floatx16 (&st)[2], int q, float moff) -> bf16x8 {
+    bf16x8 r;
+    float pv[8];
 #pragma unroll
-    for (int kt = 0; kt < 2; ++kt) {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) {
-        const float pv = fast_exp2(__builtin_fmaf(st[kt][i], scale_log2, -moff));
-        l_run += pv;
-        pb[kt * 2 + (i >> 3)][i & 7] = f2bf(pv);
-      }
+    for (int e = 0; e < 8; ++e) {
+      pv[e] = fast_exp2(__builtin_fmaf(st[q >> 1][8 * (q & 1) + e], scale_log2, -moff));
+      r[e] = f2bf(pv[e]);
     }
+    l_run += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+    return r;
   };
-  // fv[0], fv[1] hold V^T fragments 0 and 1 on entry
-  auto mma_pv = [&](const bf16x8 (&pb)[4], const bf16* vs, bf16x8 (&fv)[3]) {
+  // O^T += V^T P^T, 16-key group outer: the ND MFMAs of group q run while the
+  // VALU forms the probabilities of group q + 1.  fv[0 .. PV_AHEAD-1] hold
+  // the first V^T fragments on entry.
+  auto mma_pv = [&](const floatx16 (&st)[2], const bf16* vs, bf16x8 (&fv)[PV_AHEAD + 1]) {
     constexpr int NF = ND * 4;
+    const float moff = m_run * scale_log2;
+    bf16x8 pcur = softmax_exp(st, 0, moff);
 #pragma unroll
-    for (int f = 0; f < NF; ++f) {
-      if (f + 2 < NF) fv[(f + 2) % 3] = vfrag(vs, f + 2);
-      o[f >> 2] = mfma32(fv[f % 3], pb[f & 3], o[f >> 2]);
+    for (int q = 0; q < 4; ++q) {
+      sched_fence();
+      bf16x8 pnx;
+      if (q < 3) pnx = softmax_exp(st, q + 1, moff);
+#pragma unroll
+      for (int dt = 0; dt < ND; ++dt) {
+        const int f = q * ND + dt;
+        if (f + PV_AHEAD < NF) fv[(f + PV_AHEAD) % (PV_AHEAD + 1)] = vfrag(vs, f + PV_AHEAD);
+        o[dt] = mfma32(fv[f % (PV_AHEAD + 1)], pcur, o[dt]);
+      }
+      pcur = pnx;
     }
+    sched_fence();
   };
 
   // ---- prologue: K(0), V^T(0) ----
@@ -326,13 +349,13 @@ void sparse_attn_mfma_kernel(
     }
     if (active(it0)) {
       floatx16 st[2];
-      bf16x8 pb[4], fv[3];
+      bf16x8 fv[PV_AHEAD + 1];
       mma_s(k_cur, st);
-      fv[0] = vfrag(v_cur, 0);   // V^T reads in flight during the softmax
-      fv[1] = vfrag(v_cur, 1);
+#pragma unroll
+      for (int f = 0; f < PV_AHEAD; ++f) fv[f] = vfrag(v_cur, f);   // in flight during the max
+      sched_fence();
       softmax_max(st, it0);
-      softmax_exp(st, pb);
-      mma_pv(pb, v_cur, fv);
+      mma_pv(st, v_cur, fv);
     }
     if (!it1.valid) return false;
     wait_vmem();

@@ -90,15 +90,23 @@ __device__ __forceinline__ float xhalf_sum(float v) {
 // later LDS read, including reads of other buffers.  Callers order reads of
 // the destination with wait_vmem() and a workgroup barrier.
 typedef __attribute__((address_space(3))) void lds_void_t;
-__device__ __forceinline__ void copy16_to_lds(const void* sbase, uint32_t voff, void* lds_base) {
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_u32(const void* p) {
+  return (uint32_t)(uintptr_t)(const lds_void_t*)p;
+}
+// lds_addr must be wave-uniform (it goes to M0 through an SGPR).
+__device__ __forceinline__ void copy16_to_lds_at(const void* sbase, uint32_t voff,
+                                                 uint32_t lds_addr) {
   // sbase: wave-uniform global base; voff: this lane's byte offset from it
-  const uint32_t lds_addr = (uint32_t)(uintptr_t)(lds_void_t*)lds_base;
   asm volatile(
       "s_mov_b32 m0, %2\n\t"
       "global_load_lds_dwordx4 %0, %1"
       :
-      : "v"(voff), "s"(sbase), "s"(__builtin_amdgcn_readfirstlane(lds_addr))
+      : "v"(voff), "s"(sbase), "s"(lds_addr)
       : "memory", "m0");
+}
+__device__ __forceinline__ void copy16_to_lds(const void* sbase, uint32_t voff, void* lds_base) {
+  copy16_to_lds_at(sbase, voff, __builtin_amdgcn_readfirstlane(lds_u32(lds_base)));
 }
 // Wait until at most N of this wave's vector-memory operations are in flight.
 // Loads retire in issue order, so with only direct LDS copies outstanding this
