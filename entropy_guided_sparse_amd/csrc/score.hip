@@ -224,13 +224,16 @@ __device__ __forceinline__ void stage_kbar(bf16* kh, bf16* kl, const bf16* KH, c
 
 // 1-D grid -> (chunk, segment, KV group) with every chunk of one (segment,
 // group) pair on the same XCD (workgroup id mod 8), so the pair's probe
-// queries and pooled keys are fetched into one L2 only.  Returns false for
-// the padding ids of the last, partial group of eight pairs.
+// queries and pooled keys are fetched into one L2 only.  Within every run of
+// eight pairs XCD x takes pair 8m + ((x - m) mod 8), so the pairs rotate over
+// the XCDs and the causal segments' unequal work spreads evenly.  Returns
+// false for the padding ids of the last, partial group of eight pairs.
 __device__ __forceinline__ bool probe_item(int bid, int nch, int CS, int Hkv, int& ch, int& s,
                                            int& g) {
   const int xcd = bid & 7, k = bid >> 3;
   ch = k % nch;
-  const int pair = (k / nch) * 8 + xcd;
+  const int m = k / nch;
+  const int pair = 8 * m + ((xcd - m) & 7);
   if (pair >= CS * Hkv) return false;
   g = pair / CS;
   s = pair % CS;
