@@ -303,6 +303,24 @@ def main():
     eff_tflops = exec_flops / (t_prefill * 1e-3) / 1e12
     dense_equiv = dense_tiles * tile_flops / (t_prefill * 1e-3) / 1e12
 
+    # the paper-literal max / min observation rows ([EI] Alg. 1-2), timed on
+    # their own after the step loop (they are not part of the step)
+    mm_scores = torch.empty_like(scores)
+    mm_E = torch.empty_like(E)
+    for _ in range(2):
+        api.entropy_score(shape, q, k, kind=kind, renyi_alpha=2.0, pool=L.EGS_POOL_MAXMIN,
+                          block_scores=mm_scores, entropy=mm_E, workspace=ws)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    e0.record()
+    for _ in range(args.steps):
+        api.entropy_score(shape, q, k, kind=kind, renyi_alpha=2.0, pool=L.EGS_POOL_MAXMIN,
+                          block_scores=mm_scores, entropy=mm_E, workspace=ws)
+    e1.record()
+    torch.cuda.synchronize()
+    t_mm = e0.elapsed_time(e1) / args.steps
+    mm_bytes = (cfg.n_q_heads + cfg.n_kv_heads) * cfg.seq_len * d * elt + Hq * CS * CB * 4
+    del mm_scores, mm_E
+
     traffic = measured_traffic(cfg.name)
     if args.calib_copy_mib > 0:
         calib_copy(torch, dev, args.calib_copy_mib)
@@ -345,6 +363,12 @@ def main():
         "scoring_roofline": {"bound": "hbm", "achieved": round(scoring_gbs, 1),
                              "peak": PEAK_HBM_GBS, "unit": "GB/s",
                              "frac": round(scoring_gbs / PEAK_HBM_GBS, 4)},
+        "maxmin_scoring_us": round(t_mm * 1e3, 2),
+        "maxmin_scoring_roofline": {"bound": "hbm",
+                                    "achieved": round(mm_bytes / (t_mm * 1e-3) / 1e9, 1),
+                                    "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                                    "frac": round(mm_bytes / (t_mm * 1e-3) / 1e9 / PEAK_HBM_GBS,
+                                                  4)},
     }
     if decode is not None:
         dc = decode["cfg"]

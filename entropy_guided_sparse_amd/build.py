@@ -18,7 +18,7 @@ OBJ = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libegs.so")
 ARCH = os.environ.get("EGS_OFFLOAD_ARCH", "gfx950")
 
-SOURCES = ["egs_api.cpp", "score.hip", "budget_select.hip", "attn.hip", "retain.hip"]
+SOURCES = ["egs_api.cpp", "score.hip", "maxmin.hip", "budget_select.hip", "attn.hip", "retain.hip"]
 
 COMMON = [
     "-O3", "-fPIC", "-std=c++17", f"--offload-arch={ARCH}",

@@ -174,9 +174,8 @@ egs_status egs_entropy_score(const egs_prefill_shape* shape, int32_t pool_kind,
   PrefillDims p;
   egs_status st = check_prefill(shape, &p);
   if (st != EGS_OK) return st;
-  if (pool_kind == EGS_POOL_MAXMIN)
-    return fail(EGS_ENOTSUP, "EGS_POOL_MAXMIN is not available on the GPU path");
-  if (pool_kind != EGS_POOL_MEAN_PROBE) return fail(EGS_EINVAL, "unknown pool_kind %d", pool_kind);
+  if (pool_kind != EGS_POOL_MEAN_PROBE && pool_kind != EGS_POOL_MAXMIN)
+    return fail(EGS_EINVAL, "unknown pool_kind %d", pool_kind);
   int kind = entropy_kind;
   if (kind != EGS_SHANNON && kind != EGS_RENYI)
     return fail(EGS_EINVAL, "unknown entropy_kind %d", entropy_kind);
@@ -194,6 +193,10 @@ egs_status egs_entropy_score(const egs_prefill_shape* shape, int32_t pool_kind,
   if (workspace_bytes < wsb)
     return fail(EGS_EWORKSPACE, "workspace of %zu bytes is below the %zu required",
                 workspace_bytes, wsb);
+  if (pool_kind == EGS_POOL_MAXMIN)
+    return hip_status(egs::launch_entropy_score_maxmin(p, q, k, kind, renyi_alpha, block_scores,
+                                                       entropy, workspace, stream),
+                      "entropy_score (max/min) launch");
   return hip_status(egs::launch_entropy_score(p, q, k, kind, renyi_alpha, block_scores, entropy,
                                               workspace, stream),
                     "entropy_score launch");

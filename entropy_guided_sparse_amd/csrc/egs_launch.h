@@ -26,6 +26,12 @@ size_t score_workspace_bytes(const PrefillDims& p);
 hipError_t launch_entropy_score(const PrefillDims& p, const void* q, const void* k, int kind,
                                 float alpha, float* scores, float* entropy, void* ws,
                                 hipStream_t st);
+// The same outputs from the max / min representatives (maxmin.hip); its
+// workspace need is included in score_workspace_bytes.
+size_t maxmin_workspace_bytes(const PrefillDims& p);
+hipError_t launch_entropy_score_maxmin(const PrefillDims& p, const void* q, const void* k,
+                                       int kind, float alpha, float* scores, float* entropy,
+                                       void* ws, hipStream_t st);
 // K3: head classes and budgets (float64 arithmetic).
 hipError_t launch_budget(const PrefillDims& p, const egs_budget_policy& pol,
                          const float* entropy, int8_t* rigid, int32_t* budget,

@@ -29,6 +29,8 @@
 //                    order.
 //    Work items run on a 1-D grid with every chunk of a (segment, group) on
 //    one XCD, so its probe queries and block means are fetched into one L2.
+#include <algorithm>
+
 #include "egs_device.h"
 #include "egs_launch.h"
 
@@ -138,7 +140,7 @@ static ScoreLayout score_layout(const PrefillDims& p) {
 }
 
 size_t score_workspace_bytes(const PrefillDims& p) {
-  return score_layout(p).total;
+  return std::max(score_layout(p).total, maxmin_workspace_bytes(p));
 }
 
 template <typename TQ>

@@ -65,8 +65,8 @@ typedef enum { EGS_SHANNON = 0, EGS_RENYI = 1 } egs_entropy_kind;
 /* How key blocks are represented for the observation rows.
  * MEAN_PROBE: mean of every key block, scored against the last probe_len
  *   queries of each segment.
- * MAXMIN: the max / min representatives of [EI] Sec. 4.2 Alg. 1-2 (not
- *   available on the GPU yet: returns EGS_ENOTSUP). */
+ * MAXMIN: the max / min representatives of [EI] Sec. 4.2 Alg. 1-2 (whole
+ *   segments of queries, whole blocks of keys; probe_len is not used). */
 typedef enum { EGS_POOL_MEAN_PROBE = 0, EGS_POOL_MAXMIN = 1 } egs_pool_kind;
 
 /* Budget policy ([EI] Sec. 1: rigid heads get a fixed minimal budget, dynamic
@@ -122,6 +122,16 @@ typedef struct {
  *                      u in the last P positions of segment s, j < C_B(s)
  *   block_scores[h, s, j] = (1/P) * sum_u softmax_j(z[h, s, u, :])[j]
  *                           for j < C_B(s), and -1 for j >= C_B(s)
+ * With pool_kind EGS_POOL_MAXMIN ([EI] Sec. 4.2 Alg. 1-2) instead:
+ *   Qx[h, s] / Qn[h, s] = element-wise max / min of q[h, u] over the L_S
+ *                      positions u of segment s
+ *   Kx[g, j] / Kn[g, j] = element-wise max / min of the keys of block j
+ *   S1..S4           = softmax_j over j < C_B(s) of sm_scale * (Qx.Kx_j,
+ *                      Qx.Kn_j, Qn.Kx_j, Qn.Kn_j)
+ *   block_scores[h, s, j] = A_j / sum_j' A_j',
+ *                      A_j = max((S1_j + S2_j) / 2, (S3_j + S4_j) / 2)
+ *   (Alg. 2 leaves out sm_scale and the renormalisation; both are applied.)
+ *
  *   entropy[h, s]    = -sum_j a ln a        (EGS_SHANNON)
  *                    = ln(sum_j a^alpha)/(1-alpha)   (EGS_RENYI, alpha > 0,
  *                      alpha == 1 means Shannon)

@@ -93,7 +93,9 @@ def test_entropy_score_argument_errors(L):
     assert ws > 0
     call = lambda pool=0, kind=0, alpha=2.0, q=FAKE, wsb=ws: L.LIB.egs_entropy_score(
         ctypes.byref(sc), pool, kind, alpha, q, FAKE, FAKE, FAKE, FAKE, wsb, None)
-    assert call(pool=1) == L.EGS_ENOTSUP          # max/min pooling not on the GPU path
+    # max/min pooling is validated like the mean probe before anything launches
+    assert call(pool=1, q=None) == L.EGS_EINVAL
+    assert call(pool=1, wsb=ws - 1) == L.EGS_EWORKSPACE
     assert call(pool=9) == L.EGS_EINVAL
     assert call(kind=5) == L.EGS_EINVAL
     assert call(kind=1, alpha=0.0) == L.EGS_EINVAL

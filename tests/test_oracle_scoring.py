@@ -156,3 +156,51 @@ def test_planted_structure_eight_hot_blocks():
             assert E[h].max() < 1e-3
         else:
             assert np.all(np.abs(E[h] - math.log(8)) < 0.15), E[h]
+
+
+def test_maxmin_hand_example():
+    # EntropyInfer Sec. 4.2, Alg. 1-2 worked by hand (d = 1, scale 1, one
+    # segment of four queries, two key blocks of two keys):
+    #   queries 1, -2, 0.5, 0  ->  Q_max = 1, Q_min = -2
+    #   block 0 keys 0, 0      ->  K_max = K_min = 0
+    #   block 1 keys ln 3, 0   ->  K_max = ln 3, K_min = 0
+    #   S1 = softmax(0, ln 3) = (1/4, 3/4)     S2 = softmax(0, 0) = (1/2, 1/2)
+    #   S3 = softmax(0, -2 ln 3) = (9/10, 1/10)  S4 = (1/2, 1/2)
+    #   max((S1+S2)/2, (S3+S4)/2) = max((3/8, 5/8), (7/10, 3/10)) = (7/10, 5/8)
+    #   renormalised: (28/53, 25/53)
+    Q = np.array([[[1.0], [-2.0], [0.5], [0.0]]])
+    K = np.array([[[0.0], [0.0], [math.log(3.0)], [0.0]]])
+    a = O.observation_rows_maxmin(Q, K, 4, 2, sm_scale=1.0)
+    np.testing.assert_allclose(a[0, 0], [28 / 53, 25 / 53], atol=1e-15)
+
+
+def test_maxmin_matches_token_loop_brute_force():
+    # The representatives and the four softmaxes written out with plain loops
+    # over tokens, dimensions and blocks, on a tiny input with a group of two
+    # heads, several segments and non-trivial maxima.
+    hq, hkv, d, n, lb, ls = 2, 1, 3, 24, 3, 6
+    rng = np.random.default_rng(11)
+    Q = rng.standard_normal((hq, n, d))
+    K = rng.standard_normal((hkv, n, d))
+    sc = 1.0 / math.sqrt(d)
+    got = O.observation_rows_maxmin(Q, K, ls, lb)
+    for h in range(hq):
+        for s in range(n // ls):
+            qx = [max(Q[h, u, e] for u in range(s * ls, (s + 1) * ls)) for e in range(d)]
+            qn = [min(Q[h, u, e] for u in range(s * ls, (s + 1) * ls)) for e in range(d)]
+            cb = (s + 1) * ls // lb
+            kx = [[max(K[0, t, e] for t in range(j * lb, (j + 1) * lb)) for e in range(d)]
+                  for j in range(cb)]
+            kn = [[min(K[0, t, e] for t in range(j * lb, (j + 1) * lb)) for e in range(d)]
+                  for j in range(cb)]
+
+            def sm(qv, kk):
+                z = [sc * sum(qv[e] * kk[j][e] for e in range(d)) for j in range(cb)]
+                m = max(z)
+                w = [math.exp(x - m) for x in z]
+                return [x / sum(w) for x in w]
+            s1, s2, s3, s4 = sm(qx, kx), sm(qx, kn), sm(qn, kx), sm(qn, kn)
+            A = [max((s1[j] + s2[j]) / 2, (s3[j] + s4[j]) / 2) for j in range(cb)]
+            tot = sum(A)
+            np.testing.assert_allclose(got[h, s, :cb], [x / tot for x in A], atol=1e-14)
+            assert np.all(got[h, s, cb:] == -1.0)

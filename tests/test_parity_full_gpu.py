@@ -152,3 +152,23 @@ def test_full_decode_retention(api):
         ma, rel = attn_errors(out[b:b + 1].float().cpu().numpy(), ref)
         log(f"  decode attention batch {b}: max|d|={ma:.3e} relL2={rel:.3e}")
         assert ma <= ATTN_MAX_ABS and rel <= ATTN_REL_L2
+
+
+def test_full_maxmin_observation_rows(api):
+    """[EI] Alg. 1-2 representatives on the 128k layer: every observation row
+    and entropy against the oracle."""
+    cfg = synth.PREFILL_CONFIGS["llama3-8b-128k"]
+    log(f"[full maxmin parity] {cfg.name}")
+    inp = synth.make_prefill(cfg, seed=0)
+    shape = prefill_shape(api, cfg)
+    q = dev_tensor(inp.q_store, cfg.dtype)
+    k = dev_tensor(inp.k_store, cfg.dtype)
+    scores, E = api.entropy_score(shape, q, k, pool=api.L.EGS_POOL_MAXMIN)
+    torch.cuda.synchronize()
+    g_scores, g_E = scores.cpu().numpy(), E.cpu().numpy()
+    del q, k
+    r_scores, r_E = O.entropy_score(inp.q, inp.k, cfg.segment_size, cfg.block_size,
+                                    cfg.probe_len, pool="maxmin")
+    ds, dE = float(np.abs(g_scores - r_scores).max()), float(np.abs(g_E - r_E).max())
+    log(f"  scores max|d|={ds:.3e} entropy max|d|={dE:.3e}")
+    assert ds <= SCORE_ATOL and dE <= ENTROPY_ATOL

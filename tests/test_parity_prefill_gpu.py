@@ -265,3 +265,62 @@ def test_outputs_are_deterministic(api):
         outs.append([t.cpu() for t in (sc, E, bud, idx, cnt, o)])
     for a, b in zip(*outs):
         assert torch.equal(a, b)
+
+
+def run_maxmin(api, cfg, seed=0, kind=0, alpha=2.0):
+    """MAXMIN observation rows ([EI] Alg. 1-2) against the oracle, then the
+    budget and selection steps on them."""
+    log(f"[maxmin parity] {cfg.name} seed={seed} kind={kind} Hq={cfg.n_q_heads} "
+        f"Hkv={cfg.n_kv_heads} d={cfg.head_dim} N={cfg.seq_len} LB={cfg.block_size} "
+        f"LS={cfg.segment_size} {cfg.dtype}")
+    inp = synth.make_prefill(cfg, seed)
+    shape = prefill_shape(api, cfg)
+    q = dev_tensor(inp.q_store, cfg.dtype)
+    k = dev_tensor(inp.k_store, cfg.dtype)
+    LS, LB = cfg.segment_size, cfg.block_size
+    CB = cfg.seq_len // LB
+    scores, E = api.entropy_score(shape, q, k, kind=kind, renyi_alpha=alpha,
+                                  pool=api.L.EGS_POOL_MAXMIN)
+    pol = _policy(api, api.L.EGS_BUDGET_FIXED, frac=0.3)
+    rigid, budget = api.allocate_budget(shape, pol, E)
+    idx, cnt = api.select_blocks(shape, scores, budget, CB)
+    torch.cuda.synchronize()
+    g_scores, g_E = scores.cpu().numpy(), E.cpu().numpy()
+    r_scores, r_E = O.entropy_score(inp.q, inp.k, LS, LB, cfg.probe_len, kind=kind,
+                                    alpha=alpha, pool="maxmin")
+    ds = float(np.abs(g_scores - r_scores).max())
+    dE = float(np.abs(g_E - r_E).max())
+    log(f"  scores max|d|={ds:.3e}  entropy max|d|={dE:.3e}")
+    assert ds <= SCORE_ATOL and dE <= ENTROPY_ATOL
+    o_rigid, o_budget = _oracle_budget(g_E.astype(np.float64), cfg, pol)
+    np.testing.assert_array_equal(budget.cpu().numpy(), o_budget)
+    o_idx, o_cnt = O.select_blocks(g_scores.astype(np.float64), o_budget, LS, LB, k_max=CB)
+    np.testing.assert_array_equal(cnt.cpu().numpy(), o_cnt)
+    np.testing.assert_array_equal(idx.cpu().numpy(), o_idx)
+
+
+@pytest.mark.parametrize("case", ["tiny_f32", "tiny_f32_renyi", "d16_bf16", "d16_f32",
+                                  "d128_two_chunks", "d64_block64", "d32_ragged_chunk",
+                                  "one_block_segments"])
+def test_maxmin_observation_rows(api, case):
+    if case.startswith("tiny_f32"):
+        cfg = synth.PREFILL_CONFIGS["tiny-2k-f32"]
+    else:
+        kw = dict(d16_bf16=dict(head_dim=16, seq_len=256, block_size=16, segment_size=64),
+                  d16_f32=dict(head_dim=16, seq_len=256, block_size=16, segment_size=64,
+                               dtype="f32"),
+                  # L_S = 2048: two pooled query chunks of 1024 rows per segment
+                  d128_two_chunks=dict(n_q_heads=8, n_kv_heads=2, head_dim=128, seq_len=8192,
+                                       block_size=128, segment_size=2048,
+                                       head_types="fraction", hot_count="8",
+                                       hot_dist="zipf1.2"),
+                  d64_block64=dict(n_q_heads=6, n_kv_heads=3, head_dim=64, seq_len=4096,
+                                   block_size=64, segment_size=512,
+                                   head_types="per_segment", hot_count="poisson4"),
+                  # L_S / L_B = 3: query chunks of 48 rows, fewer than the row phases
+                  d32_ragged_chunk=dict(head_dim=32, seq_len=576, block_size=16,
+                                        segment_size=48, probe_len=16),
+                  one_block_segments=dict(segment_size=64, probe_len=16, seq_len=512))[case]
+        cfg = synth.small_prefill_config(**kw)
+    kind = api.L.EGS_RENYI if case.endswith("renyi") else api.L.EGS_SHANNON
+    run_maxmin(api, cfg, seed=7, kind=kind)
