@@ -133,7 +133,8 @@ __device__ __forceinline__ void load_obs_q(bf16x8 (&qf)[RT][D / 16], const bf16*
 }
 
 // ---------------------------------------------------------------------------
-// pass 1 (MASS = false): per-chunk running max / sum of every observer row.
+// pass 1 (MASS = false): per chunk and observer row, a reference m (at most
+// 64 below the row's maximum in log2 units) and the sum of exp2(z - m).
 // pass 2 (MASS = true): per-head window-mean mass of every key and the
 // chunk's sink-isolated entropy partial sums.
 // Workgroup = (1024-key chunk, batch x KV group, 4-head group); the four
@@ -229,16 +230,28 @@ __global__ __launch_bounds__(256) void obs_pass_kernel(
               if (t >= t_end || t > pos0 + u) z[rt][i] = -INFINITY;
             }
           }
-          float tmax = z[rt][0];
-#pragma unroll
-          for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, z[rt][i]);
-          // m is kept in log2 units (logit * sl2); sl2 > 0 commutes with max
-          const float mn = fmaxf(m[rt], tmax * sl2);
+          // The terms are taken against the running reference m (log2
+          // units), which is raised only when this tile would overflow
+          // against it (a term above 2^64, or the first tile, m = kNegBig).
+          // Otherwise m may sit below the true maximum: l then holds the sum
+          // relative to m, which is all the combine needs (it rescales every
+          // chunk's (m, l) to a common reference), and fp32 keeps the ratios.
           float sum = 0.f;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) sum += fast_exp2(__builtin_fmaf(z[rt][i], sl2, -mn));
-          l[rt] = l[rt] * fast_exp2(m[rt] - mn) + sum;
-          m[rt] = mn;
+          for (int i = 0; i < 16; ++i) sum += fast_exp2(__builtin_fmaf(z[rt][i], sl2, -m[rt]));
+          if (!(sum <= 0x1p64f)) {
+            float tmax = z[rt][0];
+#pragma unroll
+            for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, z[rt][i]);
+            // sl2 > 0 commutes with max
+            const float mn = fmaxf(m[rt], tmax * sl2);
+            sum = 0.f;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) sum += fast_exp2(__builtin_fmaf(z[rt][i], sl2, -mn));
+            l[rt] *= fast_exp2(m[rt] - mn);
+            m[rt] = mn;
+          }
+          l[rt] += sum;
         }
       } else {
         // Z: lane owns key (tk + l32), registers hold observer rows
@@ -321,8 +334,9 @@ __global__ __launch_bounds__(256) void obs_pass_kernel(
   }
 }
 
-// the rows' final maximum and 1/sum: one workgroup per (batch, head); the
-// W rows of the head each get 256 / W threads that split the chunks
+// the rows' common reference (the largest chunk reference) and 1/sum: one
+// workgroup per (batch, head); the W rows of the head each get 256 / W
+// threads that split the chunks
 __global__ __launch_bounds__(256) void obs_combine_kernel(const float* __restrict__ stat_m,
                                                           const float* __restrict__ stat_l,
                                                           int nch, int W,
