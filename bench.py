@@ -246,6 +246,14 @@ def main():
                           dtype=torch.uint8, device=dev)
         dout = torch.empty_like(dqn)
         decode = dict(cfg=dcfg, shape=dshape, n_total=n_total)
+        # page-level retention on the step's group scores: 16-token pages,
+        # 256 kept pages per group beyond the sink and recent pages
+        pg_S, pg_K = 16, 256
+        mu_buf = torch.empty((dcfg.batch, dcfg.n_kv_heads, dcfg.cache_len), dtype=torch.float32,
+                             device=dev)
+        pg_ws = torch.empty(max(256, L.LIB.egs_page_retain_workspace(
+            ctypes.byref(dsc), pg_S, pg_K, L.EGS_PAGE_LAYER_UNION)), dtype=torch.uint8,
+            device=dev)
 
         def decode_step(evs):
             res = api.kv_retain(dshape, prm, dq, dk, dv, workspace=dws)
@@ -321,6 +329,22 @@ def main():
     mm_bytes = (cfg.n_q_heads + cfg.n_kv_heads) * cfg.seq_len * d * elt + Hq * CS * CB * 4
     del mm_scores, mm_E
 
+    # page-level retention ([EP] Sec. 7) on the decode workload's group scores
+    page_us = {}
+    if decode is not None:
+        ds = decode["shape"]
+        kr = api.kv_retain(ds, prm, dq, dk, dv, workspace=dws, want_scores=True, gather=False)
+        mu_buf.copy_(kr["scores"])
+        for name, mode in (("group", L.EGS_PAGE_GROUP), ("layer_union", L.EGS_PAGE_LAYER_UNION)):
+            api.page_retain(ds, mu_buf, pg_S, pg_K, mode, workspace=pg_ws)
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for _ in range(args.steps):
+                api.page_retain(ds, mu_buf, pg_S, pg_K, mode, workspace=pg_ws)
+            e1.record()
+            torch.cuda.synchronize()
+            page_us[name] = round(e0.elapsed_time(e1) / args.steps * 1e3, 2)
+
     traffic = measured_traffic(cfg.name)
     if args.calib_copy_mib > 0:
         calib_copy(torch, dev, args.calib_copy_mib)
@@ -376,6 +400,9 @@ def main():
         res["decode_ms"] = round(t_decode, 4)
         res["decode_kv_retain_gbps"] = round(kv_bytes / (kernel_us["kv_retain"] * 1e-6) / 1e9, 1)
         res["decode_n_total"] = decode["n_total"]
+        res["page_retain_us"] = page_us
+        res["page_retain_config"] = {"page_size": pg_S, "n_keep_pages": pg_K,
+                                     "scores": "kv_retain group scores, batch 8, 8 groups, 128k"}
     if not args.no_cpu_baseline:
         res["cpu_baseline"] = cpu_baseline(cfg, inp, g_idx, g_cnt, args.cpu_seconds)
     line = json.dumps(res)

@@ -17,6 +17,8 @@ EGS_BF16, EGS_F32 = 0, 1
 EGS_SHANNON, EGS_RENYI = 0, 1
 EGS_POOL_MEAN_PROBE, EGS_POOL_MAXMIN = 0, 1
 EGS_BUDGET_FIXED, EGS_BUDGET_TWO_LEVEL, EGS_BUDGET_PROPORTIONAL, EGS_BUDGET_ALG3 = range(4)
+EGS_PAGE_GROUP, EGS_PAGE_LAYER_UNION, EGS_PAGE_HEAD_UNION = 0, 1, 2
+ABI_VERSION = 3
 
 
 class PrefillShapeC(ctypes.Structure):
@@ -72,6 +74,12 @@ SIGNATURES = {
     "egs_sparse_decode_attn_workspace": (ctypes.c_size_t, [_DS, ctypes.c_int32]),
     "egs_sparse_decode_attn": (_ST, [_DS, _P, _P, _P, ctypes.c_int32, _P, _P,
                                      ctypes.c_size_t, _P]),
+    "egs_page_retain_capacity": (ctypes.c_int32, [_DS, ctypes.c_int32, ctypes.c_int32,
+                                                  ctypes.c_int32]),
+    "egs_page_retain_workspace": (ctypes.c_size_t, [_DS, ctypes.c_int32, ctypes.c_int32,
+                                                    ctypes.c_int32]),
+    "egs_page_retain": (_ST, [_DS, ctypes.c_int32, ctypes.c_int32, ctypes.c_int32, _P, _P, _P,
+                              _P, ctypes.c_size_t, _P]),
     "egs_status_string": (ctypes.c_char_p, [ctypes.c_int32]),
     "egs_last_error": (ctypes.c_char_p, []),
     "egs_abi_version": (ctypes.c_int32, []),
@@ -94,7 +102,7 @@ def _load():
         fn = getattr(lib, name)
         fn.restype = res
         fn.argtypes = args
-    if lib.egs_abi_version() != 2:
+    if lib.egs_abi_version() != ABI_VERSION:
         raise ImportError("libegs.so ABI version mismatch")
     return lib
 

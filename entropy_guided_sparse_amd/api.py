@@ -274,6 +274,36 @@ def kv_retain(shape: DecodeShape, params: RetainParams, q_obs, k_cache, v_cache,
             "scores": sco}
 
 
+def page_retain(shape: DecodeShape, token_scores: torch.Tensor, page_size: int,
+                n_keep_pages: int, mode: int = L.EGS_PAGE_GROUP,
+                page_idx: Optional[torch.Tensor] = None,
+                page_cnt: Optional[torch.Tensor] = None,
+                workspace: Optional[torch.Tensor] = None):
+    """Kept pages [B, Y, cap] (ascending, -1 padded) and their counts [B, Y]."""
+    s = shape
+    dev = token_scores.device
+    sc = s.c()
+    X = s.n_q_heads if mode == L.EGS_PAGE_HEAD_UNION else s.n_kv_heads
+    Y = 1 if mode == L.EGS_PAGE_LAYER_UNION else s.n_kv_heads
+    _need(token_scores, "token_scores", (s.batch, X, s.cache_len), torch.float32)
+    cap = L.LIB.egs_page_retain_capacity(ctypes.byref(sc), page_size, n_keep_pages, mode)
+    if cap < 0:
+        raise L.EgsError(L.EGS_EINVAL, L.LIB.egs_last_error().decode())
+    if page_idx is None:
+        page_idx = _empty((s.batch, Y, max(cap, 1)), torch.int32, dev)
+    if page_cnt is None:
+        page_cnt = _empty((s.batch, Y), torch.int32, dev)
+    _need(page_idx, "page_idx", (s.batch, Y, max(cap, 1)), torch.int32, dev)
+    _need(page_cnt, "page_cnt", (s.batch, Y), torch.int32, dev)
+    wsb = L.LIB.egs_page_retain_workspace(ctypes.byref(sc), page_size, n_keep_pages, mode)
+    if workspace is None:
+        workspace = _workspace(wsb, dev)
+    L.check(L.LIB.egs_page_retain(ctypes.byref(sc), page_size, n_keep_pages, mode,
+                                  _ptr(token_scores), _ptr(page_idx), _ptr(page_cnt),
+                                  _ptr(workspace), workspace.numel(), _stream(dev)))
+    return page_idx, page_cnt
+
+
 def sparse_decode_attn(shape: DecodeShape, q_new, k_kept, v_kept,
                        out: Optional[torch.Tensor] = None,
                        workspace: Optional[torch.Tensor] = None):

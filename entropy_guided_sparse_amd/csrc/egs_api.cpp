@@ -388,4 +388,57 @@ egs_status egs_sparse_decode_attn(const egs_decode_shape* shape, const void* q_n
                     "decode_attn launch");
 }
 
+// page-level retention: shape checks shared by the queries and the call
+static egs_status check_pages(const egs_decode_shape* shape, int32_t page_size,
+                              int32_t n_keep_pages, int32_t mode, DecodeDims* p,
+                              egs::PageDims* q) {
+  egs_status st = check_decode(shape, p);
+  if (st != EGS_OK) return st;
+  if (page_size < 1) return fail(EGS_EINVAL, "page_size must be >= 1");
+  if (n_keep_pages < 0) return fail(EGS_EINVAL, "n_keep_pages must be >= 0");
+  if (mode != EGS_PAGE_GROUP && mode != EGS_PAGE_LAYER_UNION && mode != EGS_PAGE_HEAD_UNION)
+    return fail(EGS_EINVAL, "unknown page mode %d", mode);
+  if ((p->L + (long long)page_size - 1) / page_size > egs::kMaxPages)
+    return fail(EGS_ENOTSUP, "more than %d pages", egs::kMaxPages);
+  *q = egs::page_dims(*p, page_size, n_keep_pages, mode);
+  return EGS_OK;
+}
+
+int32_t egs_page_retain_capacity(const egs_decode_shape* shape, int32_t page_size,
+                                 int32_t n_keep_pages, int32_t mode) {
+  DecodeDims p;
+  egs::PageDims q;
+  if (check_pages(shape, page_size, n_keep_pages, mode, &p, &q) != EGS_OK) return -1;
+  return q.cap;
+}
+
+size_t egs_page_retain_workspace(const egs_decode_shape* shape, int32_t page_size,
+                                 int32_t n_keep_pages, int32_t mode) {
+  DecodeDims p;
+  egs::PageDims q;
+  if (check_pages(shape, page_size, n_keep_pages, mode, &p, &q) != EGS_OK) return 0;
+  return egs::page_retain_workspace_bytes(p, q);
+}
+
+egs_status egs_page_retain(const egs_decode_shape* shape, int32_t page_size,
+                           int32_t n_keep_pages, int32_t mode, const float* token_scores,
+                           int32_t* page_idx, int32_t* page_cnt, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  DecodeDims p;
+  egs::PageDims q;
+  egs_status st = check_pages(shape, page_size, n_keep_pages, mode, &p, &q);
+  if (st != EGS_OK) return st;
+  if ((st = need(token_scores, "token_scores", 4)) != EGS_OK) return st;
+  if ((st = need(page_idx, "page_idx", 4)) != EGS_OK) return st;
+  if ((st = need(page_cnt, "page_cnt", 4)) != EGS_OK) return st;
+  if ((st = need(workspace, "workspace", kWsAlign)) != EGS_OK) return st;
+  const size_t wsb = egs::page_retain_workspace_bytes(p, q);
+  if (workspace_bytes < wsb)
+    return fail(EGS_EWORKSPACE, "workspace of %zu bytes is below the %zu required",
+                workspace_bytes, wsb);
+  return hip_status(egs::launch_page_retain(p, q, token_scores, page_idx, page_cnt, workspace,
+                                            stream),
+                    "page_retain launch");
+}
+
 }  // extern "C"

@@ -20,6 +20,19 @@ struct DecodeDims {
   float sm_scale;
 };
 
+// Page-level retention (retain.hip): NP pages of S tokens, X members (KV
+// groups or query heads), Y output sets of m members each; ps sink pages
+// [0, ps) and recent pages [pr, NP) are forced; ntl pages per member, at most
+// cap per output set.
+struct PageDims {
+  int S, K, mode, NP, X, Y, m, ps, pr, ntl, cap;
+};
+PageDims page_dims(const DecodeDims& p, int S, int K, int mode);
+size_t page_retain_workspace_bytes(const DecodeDims& p, const PageDims& q);
+hipError_t launch_page_retain(const DecodeDims& p, const PageDims& q, const float* scores,
+                              int32_t* page_idx, int32_t* page_cnt, void* ws, hipStream_t st);
+constexpr int kMaxPages = 262144;
+
 // K1 + K2: key-block means (a bf16 hi/lo pair), probe observation rows and
 // per-(head, segment) entropy.  Workspace layout is owned by score.hip.
 size_t score_workspace_bytes(const PrefillDims& p);

@@ -27,10 +27,14 @@
 //    mu_t; retain_select runs an exact 12/12/8-bit radix select over the
 //    candidates and compacts the kept indices in ascending order through LDS;
 //    gather copies the kept K/V rows.
+//  * Page-level retention (EntroPrefill Sec. 7) keeps whole pages: page maxima
+//    of the token scores, the same select over page scores, and unions over
+//    the heads of a group or the groups of a layer through an LDS bitmap.
 //  * Decode attention splits the kept range into 256-entry chunks; the GQA
 //    group's heads share each 64-entry K / V stage in LDS (lane-per-entry dot
 //    products, lane-per-dim PV) and a combine kernel merges the chunks with
 //    their log-sum-exp.
+#include <algorithm>
 #include <type_traits>
 
 #include "egs_device.h"
@@ -992,6 +996,118 @@ hipError_t launch_decode_attn(const DecodeDims& p, const void* q_new, const void
   else
     decode_attn_combine_kernel<64><<<p.B * p.Hq, 64, 0, st>>>(part, nsplit,
                                                               static_cast<bf16*>(out));
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Page-level retention (EntroPrefill Sec. 7): a page's importance is the
+// largest token score it holds; every member (KV group or query head) keeps
+// the pages that hold a sink or a recent position plus its n_keep best other
+// pages; the head and layer modes take unions of the members' page sets.
+// The forced pages are a prefix and a suffix of the page range, so the
+// member selection is the token-level select run on the page scores.
+// ---------------------------------------------------------------------------
+constexpr int PG_MAX_WORDS = 8192;   // union bitmap: up to 262144 pages
+
+PageDims page_dims(const DecodeDims& p, int S, int K, int mode) {
+  PageDims q;
+  q.S = S;
+  q.K = K;
+  q.mode = mode;
+  q.NP = (p.L + S - 1) / S;
+  q.X = mode == EGS_PAGE_HEAD_UNION ? p.Hq : p.Hkv;
+  q.Y = mode == EGS_PAGE_LAYER_UNION ? 1 : p.Hkv;
+  q.m = q.X / q.Y;
+  q.ps = std::min(q.NP, (p.n_sink + S - 1) / S);                       // pages touching a sink
+  q.pr = p.n_recent > 0 ? std::min(q.NP - 1, (p.L - p.n_recent) / S) : q.NP;   // first recent page
+  const long long forced = (long long)q.ps + (q.NP - q.pr);
+  q.ntl = (int)std::min<long long>(q.NP, forced + K);                 // pages per member
+  q.cap = (int)std::min<long long>(q.NP, forced + (long long)q.m * K);  // pages per output set
+  return q;
+}
+
+size_t page_retain_workspace_bytes(const DecodeDims& p, const PageDims& q) {
+  const size_t a = ((size_t)p.B * q.X * q.NP * sizeof(float) + 255) / 256 * 256;
+  return a + (size_t)p.B * q.X * std::max(q.ntl, 1) * sizeof(int32_t);
+}
+
+// I[row, i] = max of scores[row, i*S .. min(L, (i+1)*S) - 1]; one thread per page
+__global__ __launch_bounds__(256) void page_max_kernel(const float* __restrict__ sc, int L, int S,
+                                                       int NP, float* __restrict__ I) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  const int row = blockIdx.y;
+  if (i >= NP) return;
+  const float* src = sc + (size_t)row * L;
+  const int lo = i * S, hi = min(L, lo + S);
+  float m = src[lo];
+  for (int t = lo + 1; t < hi; ++t) m = fmaxf(m, src[t]);
+  I[(size_t)row * NP + i] = m;
+}
+
+// union of the m member lists of output set (b, y) through an LDS bitmap,
+// compacted in ascending order; -1 past the count
+__global__ __launch_bounds__(SEL_T) void page_union_kernel(const int32_t* __restrict__ lists,
+                                                           int ntl, int m, int X, int Y, int NP,
+                                                           int cap, int32_t* __restrict__ page_idx,
+                                                           int32_t* __restrict__ page_cnt) {
+  __shared__ uint32_t bm[PG_MAX_WORDS];
+  __shared__ int ired[SEL_T / 64];
+  const int set = blockIdx.x, b = set / Y, y = set % Y;
+  const int tid = threadIdx.x;
+  const int nw = (NP + 31) / 32;
+  for (int i = tid; i < nw; i += SEL_T) bm[i] = 0u;
+  __syncthreads();
+  for (int j = 0; j < m; ++j) {
+    const int32_t* lst = lists + ((size_t)b * X + (size_t)y * m + j) * ntl;
+    for (int e = tid; e < ntl; e += SEL_T) {
+      const int pg = lst[e];
+      atomicOr(&bm[pg >> 5], 1u << (pg & 31));
+    }
+  }
+  __syncthreads();
+  // thread tid owns words [tid * WPT, (tid + 1) * WPT)
+  const int WPT = (nw + SEL_T - 1) / SEL_T;
+  const int w0 = tid * WPT;
+  int own = 0;
+  for (int i = w0; i < min(nw, w0 + WPT); ++i) own += __popc(bm[i]);
+  const int excl = block_excl_scan_1024(own, ired);
+  int32_t* out = page_idx + (size_t)set * cap;
+  int pos = excl;
+  for (int i = w0; i < min(nw, w0 + WPT); ++i) {
+    uint32_t bits = bm[i];
+    while (bits) {
+      const int t = __ffs(bits) - 1;
+      bits &= bits - 1;
+      if (pos < cap) out[pos] = i * 32 + t;
+      ++pos;
+    }
+  }
+  // the last thread ends at the total
+  __shared__ int sh_total;
+  if (tid == SEL_T - 1) {
+    sh_total = min(pos, cap);
+    page_cnt[set] = sh_total;
+  }
+  __syncthreads();
+  for (int i = sh_total + tid; i < cap; i += SEL_T) out[i] = -1;
+}
+
+hipError_t launch_page_retain(const DecodeDims& p, const PageDims& q, const float* scores,
+                              int32_t* page_idx, int32_t* page_cnt, void* ws, hipStream_t st) {
+  char* w = static_cast<char*>(ws);
+  float* I = reinterpret_cast<float*>(w);
+  int32_t* lists = reinterpret_cast<int32_t*>(
+      w + ((size_t)p.B * q.X * q.NP * sizeof(float) + 255) / 256 * 256);
+  const int rows = p.B * q.X;
+  page_max_kernel<<<dim3((q.NP + 255) / 256, rows), 256, 0, st>>>(scores, p.L, q.S, q.NP, I);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  if (q.ntl > 0) {
+    retain_select_kernel<<<rows, SEL_T, 0, st>>>(I, q.NP, q.ps, q.NP - q.pr, q.K, q.ntl, lists);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+  }
+  page_union_kernel<<<p.B * q.Y, SEL_T, 0, st>>>(lists, q.ntl, q.m, q.X, q.Y, q.NP, q.cap,
+                                                 page_idx, page_cnt);
   return hipGetLastError();
 }
 

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define EGS_ABI_VERSION 2
+#define EGS_ABI_VERSION 3
 
 typedef enum {
   EGS_OK = 0,
@@ -281,6 +281,47 @@ egs_status egs_sparse_decode_attn(const egs_decode_shape* shape,
                                   const void* v_kept, int32_t n_total,
                                   void* out, void* workspace,
                                   size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Page-level retention ([EP] Sec. 7, GQA unions and physical page budgets):
+ * whole pages of page_size consecutive cache entries are kept or released.
+ *
+ *   pages P_i = [i*S, (i+1)*S) clipped to [0, L), i < N_P = ceil(L / S)
+ *   I_x(P_i) = max over t in P_i of token_scores[b, x, t]   (page importance)
+ *   forced pages: every page holding a sink (t < n_sink) or a recent
+ *                 position (t >= L - n_recent) of the decode shape
+ *   K_x = forced pages U the n_keep_pages best other pages under
+ *         (I_x descending, page index ascending)
+ *   EGS_PAGE_GROUP:        set (b, g) = K_g      token_scores [B, Hkv, L]
+ *                          (e.g. the group scores mu of egs_kv_retain)
+ *   EGS_PAGE_HEAD_UNION:   set (b, g) = union over the heads h of group g of
+ *                          K_h                   token_scores [B, Hq, L]
+ *   EGS_PAGE_LAYER_UNION:  set (b, 0) = union over the groups g of K_g
+ *                          (one physical block holds every group)
+ *                          token_scores [B, Hkv, L]
+ * Outputs: page_idx [B, Y, cap] int32 ascending, -1 past page_cnt[b, y];
+ * page_cnt [B, Y] int32; Y = Hkv (GROUP, HEAD_UNION) or 1 (LAYER_UNION);
+ * cap = egs_page_retain_capacity(...) = min(N_P, forced + m * n_keep_pages)
+ * with m members per set (1, r or Hkv).  The decode shape's cache_len,
+ * batch, head counts, n_sink and n_recent are used; its n_keep is not.
+ * Valid: page_size >= 1, n_keep_pages >= 0, N_P <= 262144.  Capacity and
+ * workspace queries return -1 / 0 for invalid arguments.
+ * ------------------------------------------------------------------------- */
+typedef enum {
+  EGS_PAGE_GROUP = 0,
+  EGS_PAGE_LAYER_UNION = 1,
+  EGS_PAGE_HEAD_UNION = 2
+} egs_page_mode;
+
+int32_t egs_page_retain_capacity(const egs_decode_shape* shape, int32_t page_size,
+                                 int32_t n_keep_pages, int32_t mode);
+size_t egs_page_retain_workspace(const egs_decode_shape* shape, int32_t page_size,
+                                 int32_t n_keep_pages, int32_t mode);
+egs_status egs_page_retain(const egs_decode_shape* shape, int32_t page_size,
+                           int32_t n_keep_pages, int32_t mode,
+                           const float* token_scores, int32_t* page_idx,
+                           int32_t* page_cnt, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
 
 /* Status helpers. */
 const char* egs_status_string(egs_status status);

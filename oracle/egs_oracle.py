@@ -37,7 +37,8 @@ __all__ = [
     "entropy_score", "classify", "kclamp", "allocate_budget", "select_topk",
     "select_blocks", "qblock_list", "sparse_prefill_attn",
     "sparse_prefill_attn_rows", "window_mean", "head_weights", "kv_retain",
-    "kv_retain_slice", "sparse_decode_attn", "softmax",
+    "kv_retain_slice", "sparse_decode_attn", "softmax", "page_scores", "forced_pages",
+    "page_select", "page_retain", "PAGE_GROUP", "PAGE_LAYER_UNION", "PAGE_HEAD_UNION",
 ]
 
 MODE_FIXED, MODE_TWO_LEVEL, MODE_PROPORTIONAL, MODE_ALG3 = 0, 1, 2, 3
@@ -471,3 +472,75 @@ def sparse_decode_attn(q_new, k_kept, v_kept, sm_scale=None):
             p = softmax(sc * (kk @ q_new[b, h]))
             o[b, h] = p @ vv
     return o
+
+
+# ----------------------------------------------------------------------------
+# Page-level retention ([EP] Sec. 7, GQA unions and physical page budgets)
+# ----------------------------------------------------------------------------
+PAGE_GROUP, PAGE_LAYER_UNION, PAGE_HEAD_UNION = 0, 1, 2
+
+
+def page_scores(p, page_size: int) -> np.ndarray:
+    """I(P_i) = max over the tokens j of page P_i of p(j), pages
+    P_i = [i S, (i + 1) S) clipped to [0, L) ([EP] Sec. 7: a page's importance
+    is the largest token mass it holds)."""
+    p = np.asarray(p, dtype=np.float64)
+    L = p.size
+    n_pages = -(-L // page_size)
+    return np.array([p[i * page_size:min(L, (i + 1) * page_size)].max()
+                     for i in range(n_pages)])
+
+
+def forced_pages(L: int, page_size: int, n_sink: int, n_recent: int) -> set:
+    """Pages that hold a sink (t < n_sink) or a recent position
+    (t >= L - n_recent): always kept, as the token-level rule keeps those
+    positions (reading R21)."""
+    n_pages = -(-L // page_size)
+    out = set()
+    for i in range(n_pages):
+        lo, hi = i * page_size, min(L, (i + 1) * page_size) - 1
+        if lo < n_sink or hi >= L - n_recent:
+            out.add(i)
+    return out
+
+
+def page_select(p, page_size: int, n_sink: int, n_recent: int, n_keep_pages: int) -> list:
+    """The forced pages plus the n_keep_pages best other pages under the order
+    (I(P) descending, page index ascending), returned ascending ([EP] Sec. 7:
+    a page set K chosen by page maxima; tie-break as for tokens, R11)."""
+    I = page_scores(p, page_size)
+    forced = forced_pages(len(p), page_size, n_sink, n_recent)
+    cand = [i for i in range(I.size) if i not in forced]
+    top = select_topk([I[i] for i in cand], n_keep_pages)
+    return sorted(forced | {cand[t] for t in top})
+
+
+def page_retain(scores, page_size: int, n_sink: int, n_recent: int, n_keep_pages: int,
+                mode: int = PAGE_GROUP, r: int = 1) -> list:
+    """Kept page lists for every batch element ([EP] Sec. 7).
+
+    scores [B, X, L]: per KV group (X = H_kv) for PAGE_GROUP and
+    PAGE_LAYER_UNION, per query head (X = H_q, r heads per group) for
+    PAGE_HEAD_UNION.
+      PAGE_GROUP        K_{b,g} = page_select(scores[b, g])
+      PAGE_HEAD_UNION   U_{b,g} = union over the r heads h of group g of
+                        page_select(scores[b, h])   (UOR_g = |U_{b,g}| / |K_h|)
+      PAGE_LAYER_UNION  U_b = union over the groups g of page_select(scores[b, g])
+                        (one physical block holds every group)
+    Returns out[b][y] = ascending page indices, y over groups (PAGE_GROUP,
+    PAGE_HEAD_UNION) or the single layer set (PAGE_LAYER_UNION)."""
+    scores = np.asarray(scores, dtype=np.float64)
+    B, X, _ = scores.shape
+    out = []
+    for b in range(B):
+        sets = [page_select(scores[b, x], page_size, n_sink, n_recent, n_keep_pages)
+                for x in range(X)]
+        if mode == PAGE_GROUP:
+            out.append(sets)
+        elif mode == PAGE_HEAD_UNION:
+            out.append([sorted(set().union(*sets[g * r:(g + 1) * r])) for g in range(X // r)])
+        elif mode == PAGE_LAYER_UNION:
+            out.append([sorted(set().union(*sets))])
+        else:
+            raise ValueError(mode)
+    return out

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.LIB.egs_abi_version() == 2
+    assert L.LIB.egs_abi_version() == 3
     for st in range(5):
         assert L.LIB.egs_status_string(st).decode().startswith("EGS_")
 
@@ -205,3 +205,28 @@ def test_retain_param_errors(L):
     if aws > 0:
         assert L.LIB.egs_sparse_decode_attn(ctypes.byref(sc), FAKE, FAKE, FAKE, 772, FAKE, FAKE,
                                             aws - 1, None) == L.EGS_EWORKSPACE
+
+
+def test_page_retain_capacity_and_errors(L):
+    # L = 4096, page 16: 256 pages; sinks 0..3 -> page 0; recent 3840.. -> pages 240..255
+    sc = _dshape(L)
+    cap = lambda S, K, mode: L.LIB.egs_page_retain_capacity(ctypes.byref(sc), S, K, mode)
+    assert cap(16, 32, L.EGS_PAGE_GROUP) == 1 + 16 + 32
+    assert cap(16, 32, L.EGS_PAGE_LAYER_UNION) == 1 + 16 + 2 * 32       # 2 KV groups
+    assert cap(16, 32, L.EGS_PAGE_HEAD_UNION) == 1 + 16 + 4 * 32        # 4 heads per group
+    assert cap(16, 1000, L.EGS_PAGE_HEAD_UNION) == 256                  # every page
+    assert cap(1, 0, L.EGS_PAGE_GROUP) == 4 + 256                       # token pages
+    assert cap(0, 4, L.EGS_PAGE_GROUP) == -1
+    assert cap(16, -1, L.EGS_PAGE_GROUP) == -1
+    assert cap(16, 4, 7) == -1
+    assert L.LIB.egs_page_retain_workspace(ctypes.byref(sc), 16, 32, L.EGS_PAGE_GROUP) > 0
+    ws = L.LIB.egs_page_retain_workspace(ctypes.byref(sc), 16, 32, L.EGS_PAGE_GROUP)
+    call = lambda S=16, K=32, mode=0, ts=FAKE, wsb=ws: L.LIB.egs_page_retain(
+        ctypes.byref(sc), S, K, mode, ts, FAKE, FAKE, FAKE, wsb, None)
+    assert call(S=0) == L.EGS_EINVAL
+    assert call(mode=3) == L.EGS_EINVAL
+    assert call(ts=None) == L.EGS_EINVAL
+    assert call(wsb=ws - 1) == L.EGS_EWORKSPACE
+    big = _dshape(L, cache_len=1 << 20, n_obs=64)
+    assert L.LIB.egs_page_retain(ctypes.byref(big), 2, 4, 0, FAKE, FAKE, FAKE, FAKE, 1 << 40,
+                                 None) == L.EGS_ENOTSUP                 # 2^19 pages
