@@ -582,11 +582,10 @@ __global__ __launch_bounds__(SEL_T) void retain_select_kernel(
       __syncthreads();
       for (int t0 = c_lo; t0 < c_hi; t0 += SEL_T * SEL_U) {
         uint32_t kv[SEL_U];
+        // unconditional loads (index clamped into the candidates, which are
+        // not empty here) so that all SEL_U are in flight before the first use
 #pragma unroll
-        for (int u = 0; u < SEL_U; ++u) {
-          const int t = t0 + u * SEL_T + tid;
-          kv[u] = t < c_hi ? orderable(mu_row[t]) : 0u;
-        }
+        for (int u = 0; u < SEL_U; ++u) kv[u] = orderable(mu_row[min(t0 + u * SEL_T + tid, c_hi - 1)]);
 #pragma unroll
         for (int u = 0; u < SEL_U; ++u) {
           const int t = t0 + u * SEL_T + tid;
@@ -635,8 +634,15 @@ __global__ __launch_bounds__(SEL_T) void retain_select_kernel(
   for (int r0 = 0; r0 < L; r0 += SEL_R) {
     const int rn = min(SEL_R, L - r0);
     __syncthreads();   // the previous round's keys are consumed
-#pragma unroll 4
-    for (int i = tid; i < rn; i += SEL_T) keys[i] = orderable(mu_row[r0 + i]);
+    {
+      // SEL_R / SEL_T loads per thread, issued together (clamped index)
+      uint32_t kk[SEL_R / SEL_T];
+#pragma unroll
+      for (int e = 0; e < SEL_R / SEL_T; ++e) kk[e] = orderable(mu_row[r0 + min(e * SEL_T + tid, rn - 1)]);
+#pragma unroll
+      for (int e = 0; e < SEL_R / SEL_T; ++e)
+        if (e * SEL_T + tid < rn) keys[e * SEL_T + tid] = kk[e];
+    }
     __syncthreads();
     const int j0 = tid * PER;
     int n_sel = 0, n_eq = 0;
