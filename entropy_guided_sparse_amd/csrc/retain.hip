@@ -387,14 +387,34 @@ __global__ __launch_bounds__(64) void head_weight_kernel(const float* __restrict
   const int lane = threadIdx.x;
   const bool on = lane < r;
   const int h = g * r + (on ? lane : 0);
+  // the chunk partial sums: LPH lanes per head, four loads in flight each
+  int rp = 1;
+  while (rp < r) rp <<= 1;   // r <= 16
+  const int LPH = 64 / rp;
+  const int hs = lane / LPH, ph = lane % LPH;
+  float p1 = 0.f, p2 = 0.f;
+  if (hs < r) {
+    const float* e = ent + ((size_t)b * Hq + g * r + hs) * nch * 2;
+    for (int c0 = ph; c0 < nch; c0 += 4 * LPH) {
+      float2 v[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        v[j] = *reinterpret_cast<const float2*>(e + 2 * min(c0 + j * LPH, nch - 1));
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        if (c0 + j * LPH < nch) {
+          p1 += v[j].x;
+          p2 += v[j].y;
+        }
+    }
+  }
+  for (int o = LPH / 2; o > 0; o >>= 1) {
+    p1 += __shfl_xor(p1, o);
+    p2 += __shfl_xor(p2, o);
+  }
+  const float s1 = __shfl(p1, (on ? lane : 0) * LPH), s2 = __shfl(p2, (on ? lane : 0) * LPH);
   double H = 0.0;
   if (on) {
-    float s1 = 0.f, s2 = 0.f;
-    const float* e = ent + ((size_t)b * Hq + h) * nch * 2;
-    for (int c = 0; c < nch; ++c) {
-      s1 += e[2 * c];
-      s2 += e[2 * c + 1];
-    }
     if (s1 > 0.f) {
       if (kind == EGS_SHANNON)
         H = log((double)s1) - (double)s2 / (double)s1;
@@ -536,8 +556,21 @@ __global__ __launch_bounds__(256) void retain_mu_kernel(
   if (t >= L) return;
   const float* mrow = mass + ((size_t)b * Hq + g * r) * L + t;
   const float* wv = weight + (size_t)b * Hq + g * r;
+  // the group's head masses in rounds of four loads issued together (index
+  // clamped; the sum keeps head order)
   float acc = 0.f;
-  for (int hl = 0; hl < r; ++hl) acc += wv[hl] * mrow[(size_t)hl * L];
+  for (int h0 = 0; h0 < r; h0 += 4) {
+    float mv[4], wh[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int hl = min(h0 + j, r - 1);
+      mv[j] = mrow[(size_t)hl * L];
+      wh[j] = wv[hl];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (h0 + j < r) acc += wh[j] * mv[j];
+  }
   if (token_entropy != nullptr) {
     const float sm = expf(token_entropy[(size_t)b * L + t] - tstats[2 * b]) * tstats[2 * b + 1];
     acc = info_alpha * acc + (1.0f - info_alpha) * sm;
@@ -957,17 +990,32 @@ __global__ __launch_bounds__(64) void decode_attn_combine_kernel(const float* __
   constexpr int DPL = D / 64;
   const int bh = blockIdx.x, lane = threadIdx.x;
   const float* pp = part + (size_t)bh * nsplit * (D + 2);
+  // the splits' maxima, one per lane and round
   float M = kNegBig;
-  for (int s = 0; s < nsplit; ++s) M = fmaxf(M, pp[(size_t)s * (D + 2) + D]);
+  for (int s0 = 0; s0 < nsplit; s0 += 64)
+    M = fmaxf(M, wave_max(s0 + lane < nsplit ? pp[(size_t)(s0 + lane) * (D + 2) + D] : kNegBig));
   float Lr = 0.f, o[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) o[e] = 0.f;
-  for (int s = 0; s < nsplit; ++s) {
-    const float* q = pp + (size_t)s * (D + 2);
-    const float f = fast_exp2(q[D] - M);
-    Lr += q[D + 1] * f;
+  // four splits per round, their loads issued together (index clamped)
+  for (int s0 = 0; s0 < nsplit; s0 += 4) {
+    float sm[4], sl[4], so[4][DPL];
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) o[e] += q[lane * DPL + e] * f;
+    for (int j = 0; j < 4; ++j) {
+      const float* q = pp + (size_t)min(s0 + j, nsplit - 1) * (D + 2);
+      sm[j] = q[D];
+      sl[j] = q[D + 1];
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) so[j][e] = q[lane * DPL + e];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (s0 + j < nsplit) {
+        const float f = fast_exp2(sm[j] - M);
+        Lr += sl[j] * f;
+#pragma unroll
+        for (int e = 0; e < DPL; ++e) o[e] += so[j][e] * f;
+      }
   }
   const float inv = 1.0f / Lr;
 #pragma unroll
@@ -1045,8 +1093,15 @@ __global__ __launch_bounds__(256) void page_max_kernel(const float* __restrict__
   if (i >= NP) return;
   const float* src = sc + (size_t)row * L;
   const int lo = i * S, hi = min(L, lo + S);
+  // eight loads in flight; clamped repeats do not change the maximum
   float m = src[lo];
-  for (int t = lo + 1; t < hi; ++t) m = fmaxf(m, src[t]);
+  for (int t0 = lo + 1; t0 < hi; t0 += 8) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = src[min(t0 + j, hi - 1)];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) m = fmaxf(m, v[j]);
+  }
   I[(size_t)row * NP + i] = m;
 }
 

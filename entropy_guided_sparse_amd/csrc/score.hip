@@ -346,10 +346,27 @@ __global__ __launch_bounds__(256) void probe_combine_kernel(
   const int nch_s = ((s + 1) * bps + SC_CK - 1) / SC_CK;
   const float* sm = stat_m + (size_t)hs * nch * P + u;
   const float* sl = stat_l + (size_t)hs * nch * P + u;
-  float M = kNegBig;
-  for (int c = 0; c < nch_s; ++c) M = fmaxf(M, sm[(size_t)c * P]);
-  float L = 0.f;
-  for (int c = 0; c < nch_s; ++c) L += sl[(size_t)c * P] * fast_exp2(sm[(size_t)c * P] - M);
+  // chunks in rounds of eight, loads issued together (index clamped), the
+  // running maximum raised per round
+  float M = kNegBig, L = 0.f;
+  for (int c0 = 0; c0 < nch_s; c0 += 8) {
+    float m8[8], l8[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const size_t c = (size_t)min(c0 + j, nch_s - 1) * P;
+      m8[j] = sm[c];
+      l8[j] = sl[c];
+    }
+    float bm = M;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (c0 + j < nch_s) bm = fmaxf(bm, m8[j]);
+    L *= fast_exp2(M - bm);
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (c0 + j < nch_s) L += l8[j] * fast_exp2(m8[j] - bm);
+    M = bm;
+  }
   row_m[i] = M;
   row_inv[i] = L > 0.f ? 1.0f / L : 0.f;
 }
