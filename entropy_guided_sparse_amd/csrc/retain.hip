@@ -882,13 +882,14 @@ hipError_t launch_kv_retain(const DecodeDims& p, const egs_retain_params& prm, c
 //   QK: a lane owns one entry of the stage; the head's query is broadcast from
 //       LDS; the entry's K row is read as swizzled 16-byte chunks.
 //   softmax: online per head over the split (wave max / sum per stage).
-//   PV: a lane owns D/64 output dims; the probabilities come from LDS.
+//   PV: a lane owns one 16-byte chunk of the V rows for a quarter (d 128) or
+//       an eighth (d 64) of the stage's entries (16-byte LDS reads); the
+//       lanes' partial outputs are summed once per split.
 // Each split leaves its unnormalised output, maximum and sum for the combine.
 template <int D>
 __global__ __launch_bounds__(256) void decode_attn_split_kernel(
     const bf16* __restrict__ Qn, const bf16* __restrict__ K, const bf16* __restrict__ V,
     int Hq, int Hkv, int r, int n, int nsplit, float sl2, float* __restrict__ part) {
-  constexpr int DPL = D / 64;          // output dims per lane
   constexpr int KCH = D / 8;           // 16-byte chunks per row
   constexpr int ST = 64;               // entries per stage
   constexpr int PIECES = ST * D * 2 / 1024;
@@ -928,9 +929,14 @@ __global__ __launch_bounds__(256) void decode_attn_split_kernel(
       for (int d = lane; d < D; d += 64) qsh[w][d] = hv ? bf2f(q[d]) * sl2 : 0.f;
     }
     copy_stage(0, 0);
-    float m = kNegBig, l = 0.f, o[DPL];
+    // PV: lane = (key group kg, 16-byte chunk c of the V row): dims 8c .. 8c+7
+    // over keys kg*KPG .. kg*KPG+KPG-1 of every stage (16-byte LDS reads); the
+    // key groups are summed once after the last stage
+    constexpr int KG = 64 / KCH, KPG = ST / KG;
+    const int vc = lane % KCH, kg = lane / KCH;
+    float m = kNegBig, l = 0.f, o[8];
 #pragma unroll
-    for (int e = 0; e < DPL; ++e) o[e] = 0.f;
+    for (int e = 0; e < 8; ++e) o[e] = 0.f;
     for (int st = 0; st < nst; ++st) {
       wait_vmem();
       __syncthreads();   // stage st landed; every wave is done with stage st-1
@@ -960,21 +966,27 @@ __global__ __launch_bounds__(256) void decode_attn_split_kernel(
       __builtin_amdgcn_wave_barrier();
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) o[e] *= alpha;
-      // dims DPL*lane .. : chunk (DPL*lane)/8 of every V row
-      const int d0 = DPL * lane, c = d0 / 8, off = d0 % 8;
-#pragma unroll 8
-      for (int k = 0; k < ST; ++k) {
-        const float pk = psh[w][k];
-        const bf16* vr = vs + k * D + ((c ^ lds_swz<D * 2>(k)) * 8) + off;
+      for (int e = 0; e < 8; ++e) o[e] *= alpha;
 #pragma unroll
-        for (int e = 0; e < DPL; ++e) o[e] = __builtin_fmaf(pk, bf2f(vr[e]), o[e]);
+      for (int j = 0; j < KPG; ++j) {
+        const int k = kg * KPG + j;
+        const float pk = psh[w][k];
+        const bf16x8 vv = load8(vs + k * D + ((vc ^ lds_swz<D * 2>(k)) * 8));
+#pragma unroll
+        for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf(pk, (float)vv[e], o[e]);
       }
     }
+    // sum the key groups (lanes vc, vc + KCH, ...)
+#pragma unroll
+    for (int sh = KCH; sh < 64; sh <<= 1)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) o[e] += __shfl_xor(o[e], sh);
     if (hv) {
       float* pp = part + (((size_t)b * Hq + h) * nsplit + sp) * (D + 2);
+      if (kg == 0) {
 #pragma unroll
-      for (int e = 0; e < DPL; ++e) pp[DPL * lane + e] = o[e];
+        for (int e = 0; e < 8; ++e) pp[8 * vc + e] = o[e];
+      }
       if (lane == 0) {
         pp[D] = m;
         pp[D + 1] = l;
