@@ -52,6 +52,12 @@ class RetainParamsC(ctypes.Structure):
                 ("raw_logit_mode", ctypes.c_int32), ("info_alpha", ctypes.c_double)]
 
 
+class LatentStateC(ctypes.Structure):
+    _fields_ = [("length", ctypes.c_int32), ("generated", ctypes.c_int32),
+                ("n_delay", ctypes.c_int32), ("interval", ctypes.c_int32),
+                ("compressed", ctypes.c_int32)]
+
+
 _P = ctypes.c_void_p
 _PS = ctypes.POINTER(PrefillShapeC)
 _DS = ctypes.POINTER(DecodeShapeC)
@@ -74,6 +80,10 @@ SIGNATURES = {
     "egs_sparse_decode_attn_workspace": (ctypes.c_size_t, [_DS, ctypes.c_int32]),
     "egs_sparse_decode_attn": (_ST, [_DS, _P, _P, _P, ctypes.c_int32, _P, _P,
                                      ctypes.c_size_t, _P]),
+    "egs_latent_decode_workspace": (ctypes.c_size_t, [_DS]),
+    "egs_latent_decode_step": (_ST, [_DS, ctypes.POINTER(RetainParamsC),
+                                     ctypes.POINTER(LatentStateC), _P, _P, _P, _P, _P, _P, _P,
+                                     _P, _P, ctypes.c_size_t, _P]),
     "egs_page_retain_capacity": (ctypes.c_int32, [_DS, ctypes.c_int32, ctypes.c_int32,
                                                   ctypes.c_int32]),
     "egs_page_retain_workspace": (ctypes.c_size_t, [_DS, ctypes.c_int32, ctypes.c_int32,

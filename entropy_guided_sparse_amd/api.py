@@ -274,6 +274,37 @@ def kv_retain(shape: DecodeShape, params: RetainParams, q_obs, k_cache, v_cache,
             "scores": sco}
 
 
+def latent_decode_step(shape: DecodeShape, params: RetainParams, state, q_new, k_new, v_new,
+                       q_window, k_cache, v_cache, out: Optional[torch.Tensor] = None,
+                       keep_idx: Optional[torch.Tensor] = None,
+                       workspace: Optional[torch.Tensor] = None):
+    """One generated token of latent decoding; `state` is an L.LatentStateC
+    updated in place (shape.cache_len is the capacity of k_cache / v_cache)."""
+    s = shape
+    dev = q_new.device
+    _need(q_new, "q_new", (s.batch, s.n_q_heads, s.head_dim), s.dtype)
+    _need(k_new, "k_new", (s.batch, s.n_kv_heads, s.head_dim), s.dtype, dev)
+    _need(v_new, "v_new", (s.batch, s.n_kv_heads, s.head_dim), s.dtype, dev)
+    _need(q_window, "q_window", (s.batch, s.n_q_heads, s.n_obs, s.head_dim), s.dtype, dev)
+    _need(k_cache, "k_cache", (s.batch, s.n_kv_heads, s.cache_len, s.head_dim), s.dtype, dev)
+    _need(v_cache, "v_cache", (s.batch, s.n_kv_heads, s.cache_len, s.head_dim), s.dtype, dev)
+    if out is None:
+        out = _empty((s.batch, s.n_q_heads, s.head_dim), s.dtype, dev)
+    _need(out, "out", (s.batch, s.n_q_heads, s.head_dim), s.dtype, dev)
+    if keep_idx is not None and not (keep_idx.is_cuda and keep_idx.dtype == torch.int32
+                                     and keep_idx.is_contiguous()):
+        raise ValueError("keep_idx must be a contiguous int32 device tensor")
+    sc, pc = s.c(), params.c()
+    wsb = L.LIB.egs_latent_decode_workspace(ctypes.byref(sc))
+    if workspace is None:
+        workspace = _workspace(wsb, dev)
+    L.check(L.LIB.egs_latent_decode_step(ctypes.byref(sc), ctypes.byref(pc), ctypes.byref(state),
+                                         _ptr(q_new), _ptr(k_new), _ptr(v_new), _ptr(q_window),
+                                         _ptr(k_cache), _ptr(v_cache), _ptr(out), _ptr(keep_idx),
+                                         _ptr(workspace), workspace.numel(), _stream(dev)))
+    return out
+
+
 def page_retain(shape: DecodeShape, token_scores: torch.Tensor, page_size: int,
                 n_keep_pages: int, mode: int = L.EGS_PAGE_GROUP,
                 page_idx: Optional[torch.Tensor] = None,

@@ -133,6 +133,7 @@ egs_status check_decode(const egs_decode_shape* s, DecodeDims* p) {
   p->n_keep = s->n_keep;
   const long long tot = (long long)s->n_sink + s->n_recent + s->n_keep;
   p->n_total = tot >= s->cache_len ? s->cache_len : (int)tot;
+  p->Lk = p->L;
   p->dtype = s->dtype;
   p->sm_scale = s->sm_scale > 0.f ? s->sm_scale : 1.0f / std::sqrt((float)s->head_dim);
   return EGS_OK;
@@ -307,14 +308,8 @@ size_t egs_kv_retain_workspace(const egs_decode_shape* shape) {
   return egs::retain_workspace_bytes(p);
 }
 
-egs_status egs_kv_retain(const egs_decode_shape* shape, const egs_retain_params* params,
-                         const void* q_obs, const void* k_cache, const void* v_cache,
-                         const float* token_entropy, int32_t* keep_idx, void* k_out,
-                         void* v_out, float* head_entropy, float* scores, void* workspace,
-                         size_t workspace_bytes, hipStream_t stream) {
-  DecodeDims p;
-  egs_status st = check_decode(shape, &p);
-  if (st != EGS_OK) return st;
+// retention parameters, normalised (Renyi order 1 is Shannon)
+static egs_status check_retain_params(const egs_retain_params* params, egs_retain_params* out) {
   if (params == nullptr) return fail(EGS_EINVAL, "params is NULL");
   egs_retain_params prm = *params;
   if (prm.raw_logit_mode != 0 && prm.raw_logit_mode != 1)
@@ -332,6 +327,20 @@ egs_status egs_kv_retain(const egs_decode_shape* shape, const egs_retain_params*
     if (!(prm.info_alpha >= 0.0 && prm.info_alpha <= 1.0))
       return fail(EGS_EINVAL, "info_alpha must be in [0, 1]");
   }
+  *out = prm;
+  return EGS_OK;
+}
+
+egs_status egs_kv_retain(const egs_decode_shape* shape, const egs_retain_params* params,
+                         const void* q_obs, const void* k_cache, const void* v_cache,
+                         const float* token_entropy, int32_t* keep_idx, void* k_out,
+                         void* v_out, float* head_entropy, float* scores, void* workspace,
+                         size_t workspace_bytes, hipStream_t stream) {
+  DecodeDims p;
+  egs_status st = check_decode(shape, &p);
+  if (st != EGS_OK) return st;
+  egs_retain_params prm;
+  if ((st = check_retain_params(params, &prm)) != EGS_OK) return st;
   if ((st = need(q_obs, "q_obs", 16)) != EGS_OK) return st;
   if ((st = need(k_cache, "k_cache", 16)) != EGS_OK) return st;
   if ((st = need(keep_idx, "keep_idx", 4)) != EGS_OK) return st;
@@ -383,9 +392,81 @@ egs_status egs_sparse_decode_attn(const egs_decode_shape* shape, const void* q_n
   if (workspace_bytes < wsb)
     return fail(EGS_EWORKSPACE, "workspace of %zu bytes is below the %zu required",
                 workspace_bytes, wsb);
-  return hip_status(egs::launch_decode_attn(p, q_new, k_kept, v_kept, n_total, out, workspace,
-                                            stream),
+  return hip_status(egs::launch_decode_attn(p, q_new, k_kept, v_kept, n_total, n_total, out,
+                                            workspace, stream),
                     "decode_attn launch");
+}
+
+size_t egs_latent_decode_workspace(const egs_decode_shape* shape) {
+  DecodeDims p;
+  if (check_decode(shape, &p) != EGS_OK) return 0;
+  return egs::latent_layout(p).total;
+}
+
+egs_status egs_latent_decode_step(const egs_decode_shape* shape, const egs_retain_params* params,
+                                  egs_latent_state* state, const void* q_new, const void* k_new,
+                                  const void* v_new, void* q_window, void* k_cache,
+                                  void* v_cache, void* out, int32_t* keep_idx, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream) {
+  DecodeDims p;   // p.L = the capacity of the cache rows
+  egs_status st = check_decode(shape, &p);
+  if (st != EGS_OK) return st;
+  egs_retain_params prm;
+  if ((st = check_retain_params(params, &prm)) != EGS_OK) return st;
+  if (state == nullptr) return fail(EGS_EINVAL, "state is NULL");
+  const int cap = p.L, len = state->length;
+  if (len < p.W || len + 1 > cap)
+    return fail(EGS_EINVAL, "length (%d) must be in [n_obs = %d, capacity - 1 = %d]", len, p.W,
+                cap - 1);
+  if (state->generated < 0 || state->n_delay < 0)
+    return fail(EGS_EINVAL, "generated and n_delay must be >= 0");
+  if (state->interval < 0 || (state->interval > 0 && state->interval < p.W))
+    return fail(EGS_EINVAL, "interval must be 0 or >= n_obs (%d)", p.W);
+  if ((st = need(q_new, "q_new", 16)) != EGS_OK) return st;
+  if ((st = need(k_new, "k_new", 16)) != EGS_OK) return st;
+  if ((st = need(v_new, "v_new", 16)) != EGS_OK) return st;
+  if ((st = need(q_window, "q_window", 16)) != EGS_OK) return st;
+  if ((st = need(k_cache, "k_cache", 16)) != EGS_OK) return st;
+  if ((st = need(v_cache, "v_cache", 16)) != EGS_OK) return st;
+  if ((st = need(out, "out", 16)) != EGS_OK) return st;
+  if (keep_idx != nullptr && !aligned(keep_idx, 4))
+    return fail(EGS_EINVAL, "keep_idx is not 4-byte aligned");
+  if ((st = need(workspace, "workspace", kWsAlign)) != EGS_OK) return st;
+  const egs::LatentLayout ly = egs::latent_layout(p);
+  if (workspace_bytes < ly.total)
+    return fail(EGS_EWORKSPACE, "workspace of %zu bytes is below the %zu required",
+                workspace_bytes, ly.total);
+  char* w = static_cast<char*>(workspace);
+  hipError_t e = egs::launch_latent_append(p, q_new, k_new, v_new, q_window, k_cache, v_cache,
+                                           len, cap, stream);
+  if (e != hipSuccess) return hip_status(e, "latent append launch");
+  const int n = len + 1;
+  e = egs::launch_decode_attn(p, q_new, k_cache, v_cache, n, cap, out, w + ly.attn, stream);
+  if (e != hipSuccess) return hip_status(e, "latent decode attention launch");
+  const int gen = state->generated + 1;
+  const bool due = gen == state->n_delay ||
+                   (state->interval > 0 && gen > state->n_delay &&
+                    (gen - state->n_delay) % state->interval == 0);
+  state->generated = gen;
+  state->length = n;
+  state->compressed = 0;
+  if (due) {
+    DecodeDims pr = p;
+    pr.L = n;
+    pr.Lk = cap;
+    const long long tot = (long long)p.n_sink + p.n_recent + p.n_keep;
+    pr.n_total = tot >= n ? n : (int)tot;
+    int32_t* keep = keep_idx != nullptr ? keep_idx : reinterpret_cast<int32_t*>(w + ly.keep);
+    e = egs::launch_kv_retain(pr, prm, q_window, k_cache, v_cache, nullptr, keep, w + ly.ks,
+                              w + ly.vs, nullptr, nullptr, w + ly.retain, stream);
+    if (e != hipSuccess) return hip_status(e, "latent retention launch");
+    e = egs::launch_copy_rows(pr, w + ly.ks, w + ly.vs, pr.n_total, cap, k_cache, v_cache,
+                              stream);
+    if (e != hipSuccess) return hip_status(e, "latent compaction launch");
+    state->length = pr.n_total;
+    state->compressed = 1;
+  }
+  return EGS_OK;
 }
 
 // page-level retention: shape checks shared by the queries and the call

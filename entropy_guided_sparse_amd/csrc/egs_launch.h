@@ -16,6 +16,7 @@ struct PrefillDims {
 
 struct DecodeDims {
   int B, Hq, Hkv, r, D, L, W, n_sink, n_recent, n_keep, n_total;
+  int Lk;   // cache row stride in entries between (batch, KV group) rows (>= L)
   int dtype;
   float sm_scale;
 };
@@ -32,6 +33,21 @@ size_t page_retain_workspace_bytes(const DecodeDims& p, const PageDims& q);
 hipError_t launch_page_retain(const DecodeDims& p, const PageDims& q, const float* scores,
                               int32_t* page_idx, int32_t* page_cnt, void* ws, hipStream_t st);
 constexpr int kMaxPages = 262144;
+
+// Latent decoding (retain.hip): workspace of one step for a cache of p.L
+// entries (attention, retention, keep list, gathered K / V), the append of a
+// generated token and the copy of kept rows back into the cache.
+struct LatentLayout {
+  size_t attn, retain, keep, ks, vs, total;
+  int ntot_max;
+};
+LatentLayout latent_layout(const DecodeDims& p);
+size_t retain_workspace_bytes(const DecodeDims& p);
+hipError_t launch_latent_append(const DecodeDims& p, const void* q_new, const void* k_new,
+                                const void* v_new, void* q_win, void* k_cache, void* v_cache,
+                                int pos, int ldk, hipStream_t st);
+hipError_t launch_copy_rows(const DecodeDims& p, const void* sk, const void* sv, int n, int ldk,
+                            void* dk, void* dv, hipStream_t st);
 
 // K1 + K2: key-block means (a bf16 hi/lo pair), probe observation rows and
 // per-(head, segment) entropy.  Workspace layout is owned by score.hip.
@@ -66,10 +82,11 @@ hipError_t launch_kv_retain(const DecodeDims& p, const egs_retain_params& prm,
                             const float* token_entropy, int32_t* keep_idx,
                             void* k_out, void* v_out, float* head_entropy,
                             float* scores, void* ws, hipStream_t st);
-// K8: decode attention over the kept entries (split over the kept range).
+// K8: decode attention over the first n_total entries of every (batch, KV
+// group) row of k / v, rows ldk entries apart (split over the kept range).
 size_t decode_attn_workspace_bytes(const DecodeDims& p, int n_total);
 hipError_t launch_decode_attn(const DecodeDims& p, const void* q_new, const void* k,
-                              const void* v, int n_total, void* out, void* ws,
+                              const void* v, int n_total, int ldk, void* out, void* ws,
                               hipStream_t st);
 
 }  // namespace egs

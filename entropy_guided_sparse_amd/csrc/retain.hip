@@ -153,7 +153,7 @@ constexpr int RT_DEPTH = 4;
 template <int D, int RT, bool MASS>
 __global__ __launch_bounds__(256) void obs_pass_kernel(
     const bf16* __restrict__ Qo, const bf16* __restrict__ K, int Hq, int Hkv, int r, int L,
-    int W, int nch, float sl2, float* __restrict__ stat_m, float* __restrict__ stat_l,
+    int ldk, int W, int nch, float sl2, float* __restrict__ stat_m, float* __restrict__ stat_l,
     const float* __restrict__ row_m, const float* __restrict__ row_inv, int n_sink, int kind,
     float alpha, float* __restrict__ mass, float* __restrict__ ent) {
   constexpr int NC = D / 16;
@@ -169,7 +169,7 @@ __global__ __launch_bounds__(256) void obs_pass_kernel(
   const int h = g * r + (hvalid ? hl : 0);
   const int t_begin = chunk * RT_CK, t_end = min(L, t_begin + RT_CK);
   const int nst = (t_end - t_begin + RT_KT - 1) / RT_KT;
-  const bf16* Kg = K + (size_t)bg * L * D;
+  const bf16* Kg = K + (size_t)bg * ldk * D;
   const int pos0 = L - W;   // observer u sits at pos0 + u
 
   bf16x8 qf[RT][NC];
@@ -455,7 +455,7 @@ __global__ __launch_bounds__(256) void raw_qsum_kernel(const bf16* __restrict__ 
 template <int D>
 __global__ __launch_bounds__(256) void raw_score_kernel(const bf16* __restrict__ K,
                                                         const float* __restrict__ qsum, int L,
-                                                        float* __restrict__ mu,
+                                                        int ldk, float* __restrict__ mu,
                                                         float* __restrict__ scores) {
   __shared__ float qs[D];
   const int bg = blockIdx.y;
@@ -463,7 +463,7 @@ __global__ __launch_bounds__(256) void raw_score_kernel(const bf16* __restrict__
   __syncthreads();
   const int t = blockIdx.x * 256 + threadIdx.x;
   if (t >= L) return;
-  const bf16* k = K + ((size_t)bg * L + t) * D;
+  const bf16* k = K + ((size_t)bg * ldk + t) * D;
   float acc = 0.f;
 #pragma unroll
   for (int c = 0; c < D / 8; ++c) {
@@ -737,7 +737,7 @@ template <int D>
 __global__ __launch_bounds__(256) void gather_kv_kernel(const bf16* __restrict__ K,
                                                         const bf16* __restrict__ V,
                                                         const int32_t* __restrict__ keep, int L,
-                                                        int n_total, long long units,
+                                                        int ldk, int n_total, long long units,
                                                         bf16* __restrict__ Ko,
                                                         bf16* __restrict__ Vo) {
   const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
@@ -748,7 +748,7 @@ __global__ __launch_bounds__(256) void gather_kv_kernel(const bf16* __restrict__
   const long long bg = row / n_total;
   int t = keep[row];
   t = min(max(t, 0), L - 1);
-  const size_t src = ((size_t)bg * L + t) * D + c8 * 8;
+  const size_t src = ((size_t)bg * ldk + t) * D + c8 * 8;
   const size_t dst = (size_t)row * D + c8 * 8;
   *reinterpret_cast<u32x4*>(Ko + dst) = *reinterpret_cast<const u32x4*>(K + src);
   *reinterpret_cast<u32x4*>(Vo + dst) = *reinterpret_cast<const u32x4*>(V + src);
@@ -776,14 +776,14 @@ static hipError_t retain_passes(const DecodeDims& p, const RetainLayout& lay, ch
   float* row_inv = reinterpret_cast<float*>(ws + lay.row_inv);
   float* mass = reinterpret_cast<float*>(ws + lay.mass);
   float* ent = reinterpret_cast<float*>(ws + lay.ent);
-  obs_pass_kernel<D, RT, false><<<grid, 256, 0, st>>>(Qo, K, p.Hq, p.Hkv, p.r, p.L, p.W, lay.nch,
+  obs_pass_kernel<D, RT, false><<<grid, 256, 0, st>>>(Qo, K, p.Hq, p.Hkv, p.r, p.L, p.Lk, p.W, lay.nch,
                                                       sl2, stat_m, stat_l, row_m, row_inv,
                                                       p.n_sink, kind, alpha, mass, ent);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   obs_combine_kernel<<<p.B * p.Hq, 256, 0, st>>>(stat_m, stat_l, lay.nch, p.W, row_m, row_inv);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  obs_pass_kernel<D, RT, true><<<grid, 256, 0, st>>>(Qo, K, p.Hq, p.Hkv, p.r, p.L, p.W, lay.nch,
+  obs_pass_kernel<D, RT, true><<<grid, 256, 0, st>>>(Qo, K, p.Hq, p.Hkv, p.r, p.L, p.Lk, p.W, lay.nch,
                                                      sl2, stat_m, stat_l, row_m, row_inv,
                                                      p.n_sink, kind, alpha, mass, ent);
   return hipGetLastError();
@@ -827,10 +827,10 @@ hipError_t launch_kv_retain(const DecodeDims& p, const egs_retain_params& prm, c
     dim3 grid((p.L + 255) / 256, p.B * p.Hkv);
     float* mu = reinterpret_cast<float*>(ws + lay.mu);
     if (p.D == 128)
-      raw_score_kernel<128><<<grid, 256, 0, st>>>(static_cast<const bf16*>(k), qsum, p.L, mu,
+      raw_score_kernel<128><<<grid, 256, 0, st>>>(static_cast<const bf16*>(k), qsum, p.L, p.Lk, mu,
                                                   scores);
     else
-      raw_score_kernel<64><<<grid, 256, 0, st>>>(static_cast<const bf16*>(k), qsum, p.L, mu,
+      raw_score_kernel<64><<<grid, 256, 0, st>>>(static_cast<const bf16*>(k), qsum, p.L, p.Lk, mu,
                                                  scores);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     if (head_entropy != nullptr) {
@@ -862,12 +862,12 @@ hipError_t launch_kv_retain(const DecodeDims& p, const egs_retain_params& prm, c
     const unsigned blocks = (unsigned)((units + 255) / 256);
     if (p.D == 128)
       gather_kv_kernel<128><<<blocks, 256, 0, st>>>(
-          static_cast<const bf16*>(k), static_cast<const bf16*>(v), keep_idx, p.L, p.n_total,
-          units, static_cast<bf16*>(k_out), static_cast<bf16*>(v_out));
+          static_cast<const bf16*>(k), static_cast<const bf16*>(v), keep_idx, p.L, p.Lk,
+          p.n_total, units, static_cast<bf16*>(k_out), static_cast<bf16*>(v_out));
     else
       gather_kv_kernel<64><<<blocks, 256, 0, st>>>(
-          static_cast<const bf16*>(k), static_cast<const bf16*>(v), keep_idx, p.L, p.n_total,
-          units, static_cast<bf16*>(k_out), static_cast<bf16*>(v_out));
+          static_cast<const bf16*>(k), static_cast<const bf16*>(v), keep_idx, p.L, p.Lk,
+          p.n_total, units, static_cast<bf16*>(k_out), static_cast<bf16*>(v_out));
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   return hipSuccess;
@@ -889,7 +889,7 @@ hipError_t launch_kv_retain(const DecodeDims& p, const egs_retain_params& prm, c
 template <int D>
 __global__ __launch_bounds__(256) void decode_attn_split_kernel(
     const bf16* __restrict__ Qn, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    int Hq, int Hkv, int r, int n, int nsplit, float sl2, float* __restrict__ part) {
+    int Hq, int Hkv, int r, int n, int ldk, int nsplit, float sl2, float* __restrict__ part) {
   constexpr int KCH = D / 8;           // 16-byte chunks per row
   constexpr int ST = 64;               // entries per stage
   constexpr int PIECES = ST * D * 2 / 1024;
@@ -904,8 +904,8 @@ __global__ __launch_bounds__(256) void decode_attn_split_kernel(
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int t_begin = sp * DA_SPL, t_end = min(n, t_begin + DA_SPL);
   const int nst = (t_end - t_begin + ST - 1) / ST;
-  const bf16* Kg = K + (size_t)bg * n * D;
-  const bf16* Vg = V + (size_t)bg * n * D;
+  const bf16* Kg = K + (size_t)bg * ldk * D;
+  const bf16* Vg = V + (size_t)bg * ldk * D;
   // K and V rows share one layout: swizzled 16-byte chunks
   auto copy_stage = [&](int st, int buf) {
     const int t0 = t_begin + st * ST;
@@ -1040,7 +1040,8 @@ size_t decode_attn_workspace_bytes(const DecodeDims& p, int n_total) {
 }
 
 hipError_t launch_decode_attn(const DecodeDims& p, const void* q_new, const void* k,
-                              const void* v, int n_total, void* out, void* ws, hipStream_t st) {
+                              const void* v, int n_total, int ldk, void* out, void* ws,
+                              hipStream_t st) {
   const int nsplit = (n_total + DA_SPL - 1) / DA_SPL;
   const float sl2 = p.sm_scale * kLog2e;
   float* part = static_cast<float*>(ws);
@@ -1050,10 +1051,10 @@ hipError_t launch_decode_attn(const DecodeDims& p, const void* q_new, const void
   const bf16* V = static_cast<const bf16*>(v);
   if (p.D == 128)
     decode_attn_split_kernel<128><<<grid, 256, 0, st>>>(Qn, K, V, p.Hq, p.Hkv, p.r, n_total,
-                                                        nsplit, sl2, part);
+                                                        ldk, nsplit, sl2, part);
   else
     decode_attn_split_kernel<64><<<grid, 256, 0, st>>>(Qn, K, V, p.Hq, p.Hkv, p.r, n_total,
-                                                       nsplit, sl2, part);
+                                                       ldk, nsplit, sl2, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.D == 128)
@@ -1062,6 +1063,112 @@ hipError_t launch_decode_attn(const DecodeDims& p, const void* q_new, const void
   else
     decode_attn_combine_kernel<64><<<p.B * p.Hq, 64, 0, st>>>(part, nsplit,
                                                               static_cast<bf16*>(out));
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Latent decoding (EntropyInfer Sec. 4.3, App. B): the cache grows by one
+// entry per generated token and is compressed once n_delay tokens have been
+// generated, then every `interval` tokens, with the latest queries (generated
+// ones included) as the observation window.
+// ---------------------------------------------------------------------------
+// Append the new token: its query at the end of the window (rows move up by
+// one, staged through LDS) and, from the first head of every group, its K / V
+// row at position `pos` of the cache (rows ldk entries apart).  One workgroup
+// per (batch, query head).
+template <int D>
+__global__ __launch_bounds__(256) void latent_append_kernel(
+    const bf16* __restrict__ q_new, const bf16* __restrict__ k_new,
+    const bf16* __restrict__ v_new, bf16* __restrict__ q_win, bf16* __restrict__ k_cache,
+    bf16* __restrict__ v_cache, int Hq, int Hkv, int r, int W, int pos, int ldk) {
+  __shared__ bf16 win[128 * D];
+  const int bh = blockIdx.x, b = bh / Hq, h = bh % Hq, g = h / r;
+  const int tid = threadIdx.x;
+  bf16* wrow = q_win + (size_t)bh * W * D;
+  for (int i = tid; i < (W - 1) * D; i += 256) win[i] = wrow[D + i];
+  __syncthreads();
+  for (int i = tid; i < (W - 1) * D; i += 256) wrow[i] = win[i];
+  for (int d = tid; d < D; d += 256) wrow[(size_t)(W - 1) * D + d] = q_new[(size_t)bh * D + d];
+  if (h % r == 0) {
+    const size_t bg = (size_t)b * Hkv + g;
+    for (int d = tid; d < D; d += 256) {
+      k_cache[(bg * ldk + pos) * D + d] = k_new[bg * D + d];
+      v_cache[(bg * ldk + pos) * D + d] = v_new[bg * D + d];
+    }
+  }
+}
+
+// kept rows (contiguous, n per (batch, KV group)) back into the cache rows
+// 0 .. n-1 (rows ldk entries apart); one thread per 16 bytes
+template <int D>
+__global__ __launch_bounds__(256) void copy_rows_kernel(const bf16* __restrict__ sk,
+                                                        const bf16* __restrict__ sv, int n,
+                                                        int ldk, long long units,
+                                                        bf16* __restrict__ dk,
+                                                        bf16* __restrict__ dv) {
+  const long long i = (long long)blockIdx.x * 256 + threadIdx.x;
+  if (i >= units) return;
+  constexpr int CPR = D / 8;
+  const long long row = i / CPR;
+  const int c8 = (int)(i % CPR);
+  const long long bg = row / n, t = row % n;
+  const size_t src = (size_t)row * D + c8 * 8;
+  const size_t dst = ((size_t)bg * ldk + t) * D + c8 * 8;
+  *reinterpret_cast<u32x4*>(dk + dst) = *reinterpret_cast<const u32x4*>(sk + src);
+  *reinterpret_cast<u32x4*>(dv + dst) = *reinterpret_cast<const u32x4*>(sv + src);
+}
+
+LatentLayout latent_layout(const DecodeDims& p) {
+  // p.L is the cache capacity; every phase of a step fits the sizes for it
+  LatentLayout o;
+  const long long tot = (long long)p.n_sink + p.n_recent + p.n_keep;
+  o.ntot_max = (int)std::min<long long>(p.L, tot);
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align_up(bytes);
+    return at;
+  };
+  o.attn = take(decode_attn_workspace_bytes(p, p.L));
+  o.retain = take(retain_workspace_bytes(p));
+  o.keep = take((size_t)p.B * p.Hkv * o.ntot_max * sizeof(int32_t));
+  o.ks = take((size_t)p.B * p.Hkv * o.ntot_max * p.D * sizeof(bf16));
+  o.vs = take((size_t)p.B * p.Hkv * o.ntot_max * p.D * sizeof(bf16));
+  o.total = off;
+  return o;
+}
+
+hipError_t launch_latent_append(const DecodeDims& p, const void* q_new, const void* k_new,
+                                const void* v_new, void* q_win, void* k_cache, void* v_cache,
+                                int pos, int ldk, hipStream_t st) {
+  const bf16* qn = static_cast<const bf16*>(q_new);
+  const bf16* kn = static_cast<const bf16*>(k_new);
+  const bf16* vn = static_cast<const bf16*>(v_new);
+  bf16* qw = static_cast<bf16*>(q_win);
+  bf16* kc = static_cast<bf16*>(k_cache);
+  bf16* vc = static_cast<bf16*>(v_cache);
+  if (p.D == 128)
+    latent_append_kernel<128><<<p.B * p.Hq, 256, 0, st>>>(qn, kn, vn, qw, kc, vc, p.Hq, p.Hkv,
+                                                          p.r, p.W, pos, ldk);
+  else
+    latent_append_kernel<64><<<p.B * p.Hq, 256, 0, st>>>(qn, kn, vn, qw, kc, vc, p.Hq, p.Hkv,
+                                                         p.r, p.W, pos, ldk);
+  return hipGetLastError();
+}
+
+hipError_t launch_copy_rows(const DecodeDims& p, const void* sk, const void* sv, int n, int ldk,
+                            void* dk, void* dv, hipStream_t st) {
+  const long long units = (long long)p.B * p.Hkv * n * (p.D / 8);
+  if (units == 0) return hipSuccess;
+  const unsigned blocks = (unsigned)((units + 255) / 256);
+  if (p.D == 128)
+    copy_rows_kernel<128><<<blocks, 256, 0, st>>>(static_cast<const bf16*>(sk),
+                                                  static_cast<const bf16*>(sv), n, ldk, units,
+                                                  static_cast<bf16*>(dk), static_cast<bf16*>(dv));
+  else
+    copy_rows_kernel<64><<<blocks, 256, 0, st>>>(static_cast<const bf16*>(sk),
+                                                 static_cast<const bf16*>(sv), n, ldk, units,
+                                                 static_cast<bf16*>(dk), static_cast<bf16*>(dv));
   return hipGetLastError();
 }
 

@@ -283,6 +283,46 @@ egs_status egs_sparse_decode_attn(const egs_decode_shape* shape,
                                   size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Latent decoding ([EI] Sec. 4.3 and App. B: compress the cache only after
+ * N_D tokens have been generated, with an observation window that holds the
+ * generated tokens' queries; [KV] InfoKV: compress again every fixed number of
+ * generated tokens).  One call per generated token:
+ *   1. append: k_new / v_new [B, Hkv, d] become entry state->length of every
+ *      (b, g) row of k_cache / v_cache; q_new [B, Hq, d] enters the window
+ *      q_window [B, Hq, W, d] (its rows move up by one; W = n_obs);
+ *   2. out [B, Hq, d] = attention of q_new over entries 0 .. length (the new
+ *      entry included, no mask: every entry precedes or is the new token);
+ *   3. generated += 1; if generated == n_delay, or interval > 0, generated >
+ *      n_delay and (generated - n_delay) % interval == 0: the egs_kv_retain
+ *      rule (params; sinks, n_keep, recent of the shape) with the window as the
+ *      observers of the last W entries; the kept entries are compacted, in
+ *      order, to positions 0 .. n_total-1 and length becomes n_total
+ *      (keep_idx, if not NULL, receives the kept positions [B, Hkv, n_total]
+ *      in the pre-compression numbering; compressed is set to 1).
+ * The shape's cache_len is the capacity C of k_cache / v_cache [B, Hkv, C, d]
+ * (bf16).  The caller fills q_window with the queries of the last W prompt
+ * positions before the first step.  Errors (nothing launched): length + 1 > C,
+ * W > length, 0 < interval < W, n_delay < 0.  workspace >=
+ * egs_latent_decode_workspace(shape) bytes, 256-byte aligned.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  int32_t length;      /* entries in use (in / out) */
+  int32_t generated;   /* tokens generated so far (in / out) */
+  int32_t n_delay;     /* N_D: first compression after this many tokens */
+  int32_t interval;    /* then every `interval` tokens; 0 = once; else >= n_obs */
+  int32_t compressed;  /* out: 1 when this call compressed the cache */
+} egs_latent_state;
+
+size_t egs_latent_decode_workspace(const egs_decode_shape* shape);
+egs_status egs_latent_decode_step(const egs_decode_shape* shape,
+                                  const egs_retain_params* params,
+                                  egs_latent_state* state, const void* q_new,
+                                  const void* k_new, const void* v_new,
+                                  void* q_window, void* k_cache, void* v_cache,
+                                  void* out, int32_t* keep_idx, void* workspace,
+                                  size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Page-level retention ([EP] Sec. 7, GQA unions and physical page budgets):
  * whole pages of page_size consecutive cache entries are kept or released.
  *

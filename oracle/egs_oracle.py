@@ -39,6 +39,7 @@ __all__ = [
     "sparse_prefill_attn_rows", "window_mean", "head_weights", "kv_retain",
     "kv_retain_slice", "sparse_decode_attn", "softmax", "page_scores", "forced_pages",
     "page_select", "page_retain", "PAGE_GROUP", "PAGE_LAYER_UNION", "PAGE_HEAD_UNION",
+    "latent_due", "latent_decode",
 ]
 
 MODE_FIXED, MODE_TWO_LEVEL, MODE_PROPORTIONAL, MODE_ALG3 = 0, 1, 2, 3
@@ -544,3 +545,69 @@ def page_retain(scores, page_size: int, n_sink: int, n_recent: int, n_keep_pages
         else:
             raise ValueError(mode)
     return out
+
+
+# ----------------------------------------------------------------------------
+# Latent decoding ([EI] Sec. 4.3 and App. B; [KV] InfoKV: compress every fixed
+# number of generated tokens)
+# ----------------------------------------------------------------------------
+def latent_due(step: int, n_delay: int, interval: int) -> bool:
+    """Compression after the step-th generated token: once n_delay tokens have
+    been generated ([EI] Sec. 4.3, N_d), then every `interval` tokens (0 = once)."""
+    return step == n_delay or (interval > 0 and step > n_delay
+                               and (step - n_delay) % interval == 0)
+
+
+def latent_decode(k0, v0, q_win0, steps, n_sink: int, n_recent: int, n_keep: int,
+                  n_delay: int, interval: int, keep_fn=None, sm_scale=None, **retain_kw):
+    """Decode loop with latent compression.
+
+    k0, v0 [B, Hkv, L0, d]: the prompt's cache; q_win0 [B, Hq, W, d]: the
+    queries of its last W positions; steps: (q [B, Hq, d], k [B, Hkv, d],
+    v [B, Hkv, d]) per generated token.  Each step appends (k, v), moves the
+    query window by one, attends q over every cache entry (the new one
+    included), and when latent_due() compresses every (b, g) cache with
+    kv_retain_slice using the window as observers (so the generated queries
+    take part in the ranking, [EI] Sec. 4.3); kept entries stay in order
+    ([EI] Alg. 4 step 4).  keep_fn(step, b, g, keep, mu) may replace a keep set
+    (tests use it to follow another implementation's equal-score choices).
+    Returns (outputs [T, B, Hq, d], events [(step, {(b, g): (keep, mu)})])."""
+    k0 = np.asarray(k0, dtype=np.float64)
+    v0 = np.asarray(v0, dtype=np.float64)
+    win = np.array(q_win0, dtype=np.float64)
+    B, Hkv, _, d = k0.shape
+    Hq = win.shape[1]
+    r = Hq // Hkv
+    Kc = [[k0[b, g] for g in range(Hkv)] for b in range(B)]
+    Vc = [[v0[b, g] for g in range(Hkv)] for b in range(B)]
+    outs, events = [], []
+    for step, (q, k, v) in enumerate(steps, 1):
+        q = np.asarray(q, dtype=np.float64)
+        k = np.asarray(k, dtype=np.float64)
+        v = np.asarray(v, dtype=np.float64)
+        for b in range(B):
+            for g in range(Hkv):
+                Kc[b][g] = np.vstack([Kc[b][g], k[b, g][None]])
+                Vc[b][g] = np.vstack([Vc[b][g], v[b, g][None]])
+        win = np.concatenate([win[:, :, 1:], q[:, :, None]], axis=2)
+        o = np.zeros((B, Hq, d))
+        for b in range(B):
+            for h in range(Hq):
+                g = h // r
+                o[b, h] = sparse_decode_attn(q[b:b + 1, h:h + 1], Kc[b][g][None, None],
+                                             Vc[b][g][None, None], sm_scale)[0, 0]
+        outs.append(o)
+        if latent_due(step, n_delay, interval):
+            ev = {}
+            for b in range(B):
+                for g in range(Hkv):
+                    keep, mu, _ = kv_retain_slice(win[b, g * r:(g + 1) * r], Kc[b][g], n_sink,
+                                                  n_recent, n_keep, sm_scale=sm_scale,
+                                                  **retain_kw)
+                    if keep_fn is not None:
+                        keep = np.asarray(keep_fn(step, b, g, keep, mu))
+                    Kc[b][g] = Kc[b][g][keep]
+                    Vc[b][g] = Vc[b][g][keep]
+                    ev[(b, g)] = (keep, mu)
+            events.append((step, ev))
+    return np.stack(outs), events

@@ -230,3 +230,29 @@ def test_page_retain_capacity_and_errors(L):
     big = _dshape(L, cache_len=1 << 20, n_obs=64)
     assert L.LIB.egs_page_retain(ctypes.byref(big), 2, 4, 0, FAKE, FAKE, FAKE, FAKE, 1 << 40,
                                  None) == L.EGS_ENOTSUP                 # 2^19 pages
+
+
+def test_latent_step_errors(L):
+    # capacity 300, W = 64: every case below is rejected before any launch
+    sc = _dshape(L, cache_len=300, n_sink=4, n_recent=16, n_keep=32)
+    prm = L.RetainParamsC(0, 2.0, 0.5, 1.0, 0, 1.0)
+    ws = L.LIB.egs_latent_decode_workspace(ctypes.byref(sc))
+    assert ws > 0
+
+    def call(wsb=ws, **kw):
+        base = dict(length=100, generated=0, n_delay=5, interval=0, compressed=0)
+        base.update(kw)
+        st = L.LatentStateC(**base)
+        return L.LIB.egs_latent_decode_step(ctypes.byref(sc), ctypes.byref(prm), ctypes.byref(st),
+                                            FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE,
+                                            wsb, None)
+
+    assert call(length=300) == L.EGS_EINVAL          # no room for the new entry
+    assert call(length=63) == L.EGS_EINVAL           # fewer entries than observers
+    assert call(interval=10) == L.EGS_EINVAL         # re-compression inside one window
+    assert call(n_delay=-1) == L.EGS_EINVAL
+    assert call(generated=-2) == L.EGS_EINVAL
+    assert call(wsb=ws - 1) == L.EGS_EWORKSPACE
+    assert L.LIB.egs_latent_decode_step(ctypes.byref(sc), ctypes.byref(prm), None, FAKE, FAKE,
+                                        FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws,
+                                        None) == L.EGS_EINVAL
