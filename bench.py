@@ -345,6 +345,53 @@ def main():
             torch.cuda.synchronize()
             page_us[name] = round(e0.elapsed_time(e1) / args.steps * 1e3, 2)
 
+    # latent decoding ([EI] Sec. 4.3): 32 generated tokens over the decode
+    # workload's 128k cache, compressed after 16; per-token GPU time of the
+    # steps before, at and after the compression
+    latent = None
+    if decode is not None:
+        dc = decode["cfg"]
+        G, ND = 32, 16
+        C = dc.cache_len + G
+        lshape = api.DecodeShape(dc.batch, dc.n_q_heads, dc.n_kv_heads, dc.head_dim, C,
+                                 dc.n_obs, dc.n_sink, dc.n_recent, dc.n_keep)
+        kc = torch.empty((dc.batch, dc.n_kv_heads, C, dc.head_dim), dtype=torch.bfloat16,
+                         device=dev)
+        vc = torch.empty_like(kc)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(7)
+        toks = [(torch.randn((dc.batch, dc.n_q_heads, dc.head_dim), generator=gen, device=dev),
+                 torch.randn((dc.batch, dc.n_kv_heads, dc.head_dim), generator=gen, device=dev),
+                 torch.randn((dc.batch, dc.n_kv_heads, dc.head_dim), generator=gen, device=dev))
+                for _ in range(G)]
+        toks = [tuple(t.bfloat16() for t in tk) for tk in toks]
+        lws = torch.empty(L.LIB.egs_latent_decode_workspace(ctypes.byref(lshape.c())),
+                          dtype=torch.uint8, device=dev)
+        lout = torch.empty((dc.batch, dc.n_q_heads, dc.head_dim), dtype=torch.bfloat16,
+                           device=dev)
+        per_step = []
+        for rep in range(2):                       # the first pass warms up
+            kc[:, :, :dc.cache_len].copy_(dk)
+            vc[:, :, :dc.cache_len].copy_(dv)
+            win = dq.clone()
+            stt = L.LatentStateC(length=dc.cache_len, generated=0, n_delay=ND, interval=0,
+                                 compressed=0)
+            evs = [torch.cuda.Event(enable_timing=True) for _ in range(G + 1)]
+            torch.cuda.synchronize()
+            evs[0].record()
+            for i, (q1, k1, v1) in enumerate(toks):
+                api.latent_decode_step(lshape, prm, stt, q1, k1, v1, win, kc, vc, out=lout,
+                                       workspace=lws)
+                evs[i + 1].record()
+            torch.cuda.synchronize()
+            per_step = [evs[i].elapsed_time(evs[i + 1]) * 1e3 for i in range(G)]
+        latent = {"tokens": G, "n_delay": ND, "cache_len": dc.cache_len,
+                  "kept_after": int(stt.length) - (G - ND),
+                  "dense_step_us": round(float(np.mean(per_step[:ND - 1])), 1),
+                  "compress_step_us": round(per_step[ND - 1], 1),
+                  "compressed_step_us": round(float(np.mean(per_step[ND:])), 1)}
+        del kc, vc, lws
+
     traffic = measured_traffic(cfg.name)
     if args.calib_copy_mib > 0:
         calib_copy(torch, dev, args.calib_copy_mib)
@@ -401,6 +448,7 @@ def main():
         res["decode_kv_retain_gbps"] = round(kv_bytes / (kernel_us["kv_retain"] * 1e-6) / 1e9, 1)
         res["decode_n_total"] = decode["n_total"]
         res["page_retain_us"] = page_us
+        res["latent_decode"] = latent
         res["page_retain_config"] = {"page_size": pg_S, "n_keep_pages": pg_K,
                                      "scores": "kv_retain group scores, batch 8, 8 groups, 128k"}
     if not args.no_cpu_baseline:
