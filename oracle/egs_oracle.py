@@ -39,7 +39,8 @@ __all__ = [
     "sparse_prefill_attn_rows", "window_mean", "head_weights", "kv_retain",
     "kv_retain_slice", "sparse_decode_attn", "softmax", "page_scores", "forced_pages",
     "page_select", "page_retain", "PAGE_GROUP", "PAGE_LAYER_UNION", "PAGE_HEAD_UNION",
-    "latent_due", "latent_decode",
+    "latent_due", "latent_decode", "prune_pooled_measure", "prune_row_chunk_mass",
+    "prune_priorities", "prune_greedy", "prune_certificate", "chunk_prune",
 ]
 
 MODE_FIXED, MODE_TWO_LEVEL, MODE_PROPORTIONAL, MODE_ALG3 = 0, 1, 2, 3
@@ -611,3 +612,123 @@ def latent_decode(k0, v0, q_win0, steps, n_sink: int, n_recent: int, n_keep: int
                     ev[(b, g)] = (keep, mu)
             events.append((step, ev))
     return np.stack(outs), events
+
+
+# ----------------------------------------------------------------------------
+# Chunk pruning ([EP] Sec. 2.1, Sec. 3.1-3.2, Sec. 4.1-4.2)
+# ----------------------------------------------------------------------------
+def _obs_rows(q_obs_h, k_g, T, sc):
+    """Causal attention rows of the observers u (positions T - W + u) over all
+    T positions ([EP] Sec. 2.1): A [W, T]."""
+    W = q_obs_h.shape[0]
+    z = sc * (q_obs_h @ k_g.T)
+    pos = T - W + np.arange(W)
+    z[np.arange(T)[None, :] > pos[:, None]] = -np.inf
+    return softmax(z, axis=1)
+
+
+def prune_pooled_measure(q_obs, k, n_sink: int, zeta: float = 0.5, tau: float = 1.0,
+                         sm_scale=None):
+    """mu^l_j = (1/G) sum_g sum_{h in g} w_h a^h_j with the window means a^h,
+    Renyi-2 sink-isolated head entropies and the regularized weights
+    ([EP] Sec. 3.1); q_obs [Hq, W, d], k [Hkv, T, d].  Returns (mu [T],
+    A [Hq, W, T])."""
+    q_obs = np.asarray(q_obs, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    Hq, W, d = q_obs.shape
+    Hkv, T, _ = k.shape
+    r = Hq // Hkv
+    sc = _sm_scale(d, sm_scale)
+    A = np.stack([_obs_rows(q_obs[h], k[h // r], T, sc) for h in range(Hq)])
+    mu = np.zeros(T)
+    for g in range(Hkv):
+        a = A[g * r:(g + 1) * r].mean(axis=1)
+        H = np.array([sink_isolated_entropy(a[i], n_sink, RENYI, 2.0) for i in range(r)])
+        w = head_weights(H, zeta, tau)
+        mu += (w[:, None] * a).sum(axis=0)
+    return mu / Hkv, A
+
+
+def prune_row_chunk_mass(A, chunks) -> np.ndarray:
+    """m[a, i] = sum over j in chunk i of A_{a, j}, rows a = (h, u) in
+    head-major order ([EP] Sec. 4.2, the row constraints)."""
+    A = np.asarray(A, dtype=np.float64)
+    rows = A.reshape(-1, A.shape[-1])
+    return np.stack([rows[:, b:e].sum(axis=1) for (b, e) in chunks], axis=1)
+
+
+def prune_priorities(mu, chunks, eps_s: float, lam: float):
+    """Null-calibrated chunk priorities ([EP] Sec. 3.2), reading R23:
+    p = mu restricted to the candidate tokens and renormalised; pi_i = n_i / N
+    (uniform null); M_i = sum_{j in c_i} p_j;
+    p_hat_ij = (p_j + eps_s pi_i / n_i) / (M_i + eps_s pi_i);
+    l_i = (M_i + eps_s pi_i) / ((1 + eps_s) pi_i);
+    kappa_i = -H_2(p_hat_i) / ln n_i in [-1, 0] (0 for a one-token chunk);
+    S_i = ln l_i + lam kappa_i.  Returns (S, l, kappa, M)."""
+    mu = np.asarray(mu, dtype=np.float64)
+    n = np.array([e - b for (b, e) in chunks], dtype=np.float64)
+    N = n.sum()
+    Z = sum(mu[b:e].sum() for (b, e) in chunks)
+    S, ell, kap, M = [], [], [], []
+    for i, (b, e) in enumerate(chunks):
+        p = mu[b:e] / Z
+        pi = n[i] / N
+        Mi = p.sum()
+        ph = (p + eps_s * pi / n[i]) / (Mi + eps_s * pi)
+        li = (Mi + eps_s * pi) / ((1.0 + eps_s) * pi)
+        ki = 0.0 if n[i] < 2 else -(-math.log(float((ph ** 2).sum()))) / math.log(n[i])
+        S.append(math.log(li) + lam * ki)
+        ell.append(li)
+        kap.append(ki)
+        M.append(Mi)
+    return np.array(S), np.array(ell), np.array(kap), np.array(M)
+
+
+def prune_greedy(S, n, m, eps: float, m0: int, target: int, dtype=np.float64):
+    """The reference proposer of [EP] Sec. 4.2: chunks in increasing S_i, ties
+    by larger n_i, then lower index; one scan; chunk i joins the removal set
+    only if every row keeps sum_{i in E} m[a, i] <= eps and |E| <= k - m0; the
+    scan stops once the removed tokens reach `target`.  The running row sums
+    are kept in `dtype` (float32 when following a float32 implementation).
+    Returns (removed flags [k] bool, removed tokens)."""
+    k = len(S)
+    order = sorted(range(k), key=lambda i: (float(S[i]), -int(n[i]), i))
+    cur = np.zeros(m.shape[0], dtype=dtype)
+    m = np.asarray(m, dtype=dtype)
+    removed = np.zeros(k, dtype=bool)
+    tokens, count = 0, 0
+    for i in order:
+        if tokens >= target:
+            break
+        if count + 1 > k - m0:
+            break
+        nxt = cur + m[:, i]
+        if np.all(nxt <= dtype(eps)):
+            cur = nxt
+            removed[i] = True
+            tokens += int(n[i])
+            count += 1
+    return removed, tokens
+
+
+def prune_certificate(n, m, eps: float, m0: int, y: float, t: float) -> float:
+    """U(y, t) = sum_a y eps + t (k - m0) + sum_i [n_i - sum_a y m[a, i] - t]_+
+    with one price y >= 0 for every row and t >= 0 ([EP] Sec. 4.2): an upper
+    bound on the most tokens any feasible removal set can remove."""
+    n = np.asarray(n, dtype=np.float64)
+    m = np.asarray(m, dtype=np.float64)
+    R, k = m.shape
+    return (R * y * eps + t * (k - m0)
+            + float(np.maximum(n - y * m.sum(axis=0) - t, 0.0).sum()))
+
+
+def chunk_prune(q_obs, k, chunks, n_sink: int, eps_s: float, lam: float, eps: float,
+                m0: int, target: int, zeta: float = 0.5, tau: float = 1.0, sm_scale=None):
+    """Steps together: pooled measure, row-chunk masses, priorities, greedy
+    removal.  Returns dict(mu, m, S, removed, tokens)."""
+    mu, A = prune_pooled_measure(q_obs, k, n_sink, zeta, tau, sm_scale)
+    m = prune_row_chunk_mass(A, chunks)
+    S, ell, kap, M = prune_priorities(mu, chunks, eps_s, lam)
+    n = np.array([e - b for (b, e) in chunks])
+    removed, tokens = prune_greedy(S, n, m, eps, m0, target)
+    return dict(mu=mu, m=m, S=S, ell=ell, kappa=kap, M=M, removed=removed, tokens=tokens)
