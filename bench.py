@@ -392,6 +392,31 @@ def main():
                   "compressed_step_us": round(float(np.mean(per_step[ND:])), 1)}
         del kc, vc, lws
 
+    # chunk pruning ([EP] Sec. 3-4) of one 128k prompt of the decode workload
+    # (batch element 0): 64 candidate documents, removal up to half the prompt
+    prune = None
+    if decode is not None:
+        dc = decode["cfg"]
+        pshape = api.DecodeShape(1, dc.n_q_heads, dc.n_kv_heads, dc.head_dim, dc.cache_len,
+                                 dc.n_obs, dc.n_sink, dc.n_recent, dc.n_keep)
+        pch = synth.prune_chunks(dc.cache_len, dc.n_obs, 64, seed=11)
+        pws = torch.empty(L.LIB.egs_chunk_prune_workspace(ctypes.byref(pshape.c()), len(pch)),
+                          dtype=torch.uint8, device=dev)
+        pargs = (pshape, dq[0], dk[0], pch, 0.1, 0.5, 0.1, 4, dc.cache_len // 2)
+        for _ in range(2):
+            api.chunk_prune(*pargs, workspace=pws)
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        for _ in range(args.steps):
+            prem, ptok, _, _ = api.chunk_prune(*pargs, workspace=pws)
+        e1.record()
+        torch.cuda.synchronize()
+        prune = {"us": round(e0.elapsed_time(e1) / args.steps * 1e3, 1), "chunks": len(pch),
+                 "seq_len": dc.cache_len, "n_obs": dc.n_obs, "eps": 0.1, "m0": 4,
+                 "target": dc.cache_len // 2, "removed": int(prem.sum().item()),
+                 "removed_tokens": int(ptok.item())}
+        del pws
+
     traffic = measured_traffic(cfg.name)
     if args.calib_copy_mib > 0:
         calib_copy(torch, dev, args.calib_copy_mib)
@@ -449,6 +474,7 @@ def main():
         res["decode_n_total"] = decode["n_total"]
         res["page_retain_us"] = page_us
         res["latent_decode"] = latent
+        res["chunk_prune"] = prune
         res["page_retain_config"] = {"page_size": pg_S, "n_keep_pages": pg_K,
                                      "scores": "kv_retain group scores, batch 8, 8 groups, 128k"}
     if not args.no_cpu_baseline:

@@ -58,6 +58,12 @@ class LatentStateC(ctypes.Structure):
                 ("compressed", ctypes.c_int32)]
 
 
+class PruneParamsC(ctypes.Structure):
+    _fields_ = [("eps_s", ctypes.c_double), ("lam", ctypes.c_double), ("eps", ctypes.c_double),
+                ("m0", ctypes.c_int32), ("target", ctypes.c_int32), ("zeta", ctypes.c_double),
+                ("tau", ctypes.c_double)]
+
+
 _P = ctypes.c_void_p
 _PS = ctypes.POINTER(PrefillShapeC)
 _DS = ctypes.POINTER(DecodeShapeC)
@@ -80,6 +86,9 @@ SIGNATURES = {
     "egs_sparse_decode_attn_workspace": (ctypes.c_size_t, [_DS, ctypes.c_int32]),
     "egs_sparse_decode_attn": (_ST, [_DS, _P, _P, _P, ctypes.c_int32, _P, _P,
                                      ctypes.c_size_t, _P]),
+    "egs_chunk_prune_workspace": (ctypes.c_size_t, [_DS, ctypes.c_int32]),
+    "egs_chunk_prune": (_ST, [_DS, ctypes.POINTER(PruneParamsC), _P, _P, _P, ctypes.c_int32, _P,
+                              _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "egs_latent_decode_workspace": (ctypes.c_size_t, [_DS]),
     "egs_latent_decode_step": (_ST, [_DS, ctypes.POINTER(RetainParamsC),
                                      ctypes.POINTER(LatentStateC), _P, _P, _P, _P, _P, _P, _P,

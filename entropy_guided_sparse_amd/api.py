@@ -274,6 +274,35 @@ def kv_retain(shape: DecodeShape, params: RetainParams, q_obs, k_cache, v_cache,
             "scores": sco}
 
 
+def chunk_prune(shape: DecodeShape, q_obs, k, chunk_bounds, eps_s: float, lam: float,
+                eps: float, m0: int, target: int, zeta: float = 0.5, tau: float = 1.0,
+                want_row_mass: bool = False, workspace: Optional[torch.Tensor] = None):
+    """Removal flags [k] int8, removed tokens [1] int32, priorities [k] and
+    (optionally) the row-chunk masses [k, Hq*W]; chunk_bounds is a host array
+    [k, 2] of int32 (begin, end)."""
+    import numpy as np
+    s = shape
+    dev = q_obs.device
+    _need(q_obs, "q_obs", (s.n_q_heads, s.n_obs, s.head_dim), s.dtype)
+    _need(k, "k", (s.n_kv_heads, s.cache_len, s.head_dim), s.dtype, dev)
+    b = np.ascontiguousarray(np.asarray(chunk_bounds, dtype=np.int32).reshape(-1, 2))
+    nk = b.shape[0]
+    removed = _empty((nk,), torch.int8, dev)
+    tokens = _empty((1,), torch.int32, dev)
+    prio = _empty((nk,), torch.float32, dev)
+    row_mass = _empty((nk, s.n_q_heads * s.n_obs), torch.float32, dev) if want_row_mass else None
+    sc = s.c()
+    pc = L.PruneParamsC(eps_s, lam, eps, m0, target, zeta, tau)
+    wsb = L.LIB.egs_chunk_prune_workspace(ctypes.byref(sc), nk)
+    if workspace is None:
+        workspace = _workspace(wsb, dev)
+    L.check(L.LIB.egs_chunk_prune(ctypes.byref(sc), ctypes.byref(pc), _ptr(q_obs), _ptr(k),
+                                  b.ctypes.data_as(ctypes.c_void_p), nk, _ptr(removed),
+                                  _ptr(tokens), _ptr(prio), _ptr(row_mass), _ptr(workspace),
+                                  workspace.numel(), _stream(dev)))
+    return removed, tokens, prio, row_mass
+
+
 def latent_decode_step(shape: DecodeShape, params: RetainParams, state, q_new, k_new, v_new,
                        q_window, k_cache, v_cache, out: Optional[torch.Tensor] = None,
                        keep_idx: Optional[torch.Tensor] = None,

@@ -397,6 +397,76 @@ egs_status egs_sparse_decode_attn(const egs_decode_shape* shape, const void* q_n
                     "decode_attn launch");
 }
 
+static egs_status check_prune(const egs_decode_shape* shape, int32_t n_chunks, DecodeDims* p) {
+  egs_status st = check_decode(shape, p);
+  if (st != EGS_OK) return st;
+  if (p->B != 1) return fail(EGS_EINVAL, "chunk pruning takes one prompt (batch 1)");
+  if (n_chunks < 1 || n_chunks > egs::kMaxPruneChunks)
+    return fail(EGS_EINVAL, "n_chunks must be in [1, %d]", egs::kMaxPruneChunks);
+  if (p->Hq * p->W > egs::kMaxPruneRows)
+    return fail(EGS_ENOTSUP, "more than %d observer rows", egs::kMaxPruneRows);
+  return EGS_OK;
+}
+
+size_t egs_chunk_prune_workspace(const egs_decode_shape* shape, int32_t n_chunks) {
+  DecodeDims p;
+  if (check_prune(shape, n_chunks, &p) != EGS_OK) return 0;
+  return egs::prune_layout(p, n_chunks).total;
+}
+
+egs_status egs_chunk_prune(const egs_decode_shape* shape, const egs_prune_params* params,
+                           const void* q_obs, const void* k, const int32_t* chunk_bounds,
+                           int32_t n_chunks, int8_t* removed, int32_t* removed_tokens,
+                           float* priority, float* row_mass, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream) {
+  DecodeDims p;
+  egs_status st = check_prune(shape, n_chunks, &p);
+  if (st != EGS_OK) return st;
+  if (params == nullptr) return fail(EGS_EINVAL, "params is NULL");
+  const egs_prune_params& q = *params;
+  if (!(std::isfinite(q.eps_s) && q.eps_s > 0.0)) return fail(EGS_EINVAL, "eps_s must be > 0");
+  if (!(std::isfinite(q.lambda) && q.lambda >= 0.0))
+    return fail(EGS_EINVAL, "lambda must be >= 0");
+  if (!(std::isfinite(q.eps) && q.eps >= 0.0)) return fail(EGS_EINVAL, "eps must be >= 0");
+  if (q.m0 < 0 || q.target < 0) return fail(EGS_EINVAL, "m0 and target must be >= 0");
+  if (!(q.zeta > 0.0 && q.zeta <= 1.0)) return fail(EGS_EINVAL, "zeta must be in (0, 1]");
+  if (!(std::isfinite(q.tau) && q.tau > 0.0)) return fail(EGS_EINVAL, "tau must be > 0");
+  if (chunk_bounds == nullptr) return fail(EGS_EINVAL, "chunk_bounds is NULL");
+  int prev = 0;
+  for (int i = 0; i < n_chunks; ++i) {
+    const int b = chunk_bounds[2 * i], e = chunk_bounds[2 * i + 1];
+    if (b < prev || e <= b || e > p.L - p.W)
+      return fail(EGS_EINVAL, "chunk %d = [%d, %d) is not ascending, disjoint and before the "
+                  "observers (T - W = %d)", i, b, e, p.L - p.W);
+    prev = e;
+  }
+  if ((st = need(q_obs, "q_obs", 16)) != EGS_OK) return st;
+  if ((st = need(k, "k", 16)) != EGS_OK) return st;
+  if ((st = need(removed, "removed", 1)) != EGS_OK) return st;
+  if ((st = need(removed_tokens, "removed_tokens", 4)) != EGS_OK) return st;
+  if ((st = need(priority, "priority", 4)) != EGS_OK) return st;
+  if (row_mass != nullptr && !aligned(row_mass, 4))
+    return fail(EGS_EINVAL, "row_mass is not 4-byte aligned");
+  if ((st = need(workspace, "workspace", kWsAlign)) != EGS_OK) return st;
+  const size_t wsb = egs::prune_layout(p, n_chunks).total;
+  if (workspace_bytes < wsb)
+    return fail(EGS_EWORKSPACE, "workspace of %zu bytes is below the %zu required",
+                workspace_bytes, wsb);
+  egs::PruneArgs a;
+  a.k = n_chunks;
+  a.zeta = q.zeta;
+  a.tau = q.tau;
+  a.eps_s = (float)q.eps_s;
+  a.lam = (float)q.lambda;
+  a.eps = (float)q.eps;
+  a.m0 = q.m0;
+  a.target = q.target;
+  return hip_status(egs::launch_chunk_prune(p, a, q_obs, k, chunk_bounds, removed,
+                                            removed_tokens, priority, row_mass, workspace,
+                                            stream),
+                    "chunk_prune launch");
+}
+
 size_t egs_latent_decode_workspace(const egs_decode_shape* shape) {
   DecodeDims p;
   if (check_decode(shape, &p) != EGS_OK) return 0;

@@ -34,6 +34,24 @@ hipError_t launch_page_retain(const DecodeDims& p, const PageDims& q, const floa
                               int32_t* page_idx, int32_t* page_cnt, void* ws, hipStream_t st);
 constexpr int kMaxPages = 262144;
 
+// Chunk pruning (retain.hip) of one prompt: p.L = T, p.W observers.
+struct PruneArgs {
+  int k;            // chunks
+  double zeta, tau;
+  float eps_s, lam, eps;
+  int m0, target;
+};
+struct PruneLayout {
+  size_t retain, cid, bounds, stats, mtab, total;
+};
+constexpr int kMaxPruneChunks = 4096;
+constexpr int kMaxPruneRows = 8192;
+PruneLayout prune_layout(const DecodeDims& p, int k);
+hipError_t launch_chunk_prune(const DecodeDims& p, const PruneArgs& a, const void* q_obs,
+                              const void* k, const int32_t* bounds_host, int8_t* removed,
+                              int32_t* removed_tokens, float* prio, float* row_mass, void* workspace,
+                              hipStream_t st);
+
 // Latent decoding (retain.hip): workspace of one step for a cache of p.L
 // entries (attention, retention, keep list, gathered K / V), the append of a
 // generated token and the copy of kept rows back into the cache.

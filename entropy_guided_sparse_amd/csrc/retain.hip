@@ -1067,6 +1067,363 @@ hipError_t launch_decode_attn(const DecodeDims& p, const void* q_new, const void
 }
 
 // ---------------------------------------------------------------------------
+// Chunk pruning (EntroPrefill Sec. 3.1-3.2, 4.1-4.2): the observer-pooled
+// measure of one prompt (the retention passes with Renyi-2 head entropies,
+// averaged over the KV groups), the mass every observer row puts on every
+// candidate chunk, null-calibrated chunk priorities and the greedy feasible
+// removal scan.
+// ---------------------------------------------------------------------------
+constexpr int PR_MAX_CHUNKS = 4096;
+constexpr int PR_MAX_ROWS = 8192;
+
+// chunk id of every position (-1 outside the chunks); bounds [k][2] ascending
+__global__ __launch_bounds__(256) void chunk_of_kernel(const int32_t* __restrict__ bounds, int k,
+                                                       int T, int32_t* __restrict__ cid) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= T) return;
+  int lo = 0, hi = k - 1, id = -1;
+  while (lo <= hi) {   // the last chunk whose begin is <= t
+    const int mid = (lo + hi) >> 1;
+    if (bounds[2 * mid] <= t) {
+      id = mid;
+      lo = mid + 1;
+    } else {
+      hi = mid - 1;
+    }
+  }
+  cid[t] = (id >= 0 && t < bounds[2 * id + 1]) ? id : -1;
+}
+
+// m[i][a] += sum over the positions t of chunk i of A_{a,t}, rows a = h*W + u.
+// Workgroup = (1024-key span, KV group, 4-head group); 64-key K stages in LDS
+// shared by the four heads; S^T with keys as M so a lane owns an observer
+// row, its probabilities summed per chunk in registers (chunk ids rise with
+// the position) and added to m when the chunk changes.
+template <int D, int RT>
+__global__ __launch_bounds__(256) void chunk_mass_kernel(
+    const bf16* __restrict__ Qo, const bf16* __restrict__ K, const int32_t* __restrict__ cid,
+    int Hq, int Hkv, int r, int T, int W, float sl2, const float* __restrict__ row_m,
+    const float* __restrict__ row_inv, int R, float* __restrict__ m) {
+  constexpr int NC = D / 16;
+  __shared__ __attribute__((aligned(1024))) bf16 Ks[RT_KT * D];
+  __shared__ int cs[RT_KT];
+  const int span = blockIdx.x, g = blockIdx.y;
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int l32 = lane & 31, hg = lane >> 5;
+  const int hl = blockIdx.z * 4 + w;
+  const bool hvalid = hl < r;
+  const int h = g * r + (hvalid ? hl : 0);
+  const int t_begin = span * RT_CK, t_end = min(T, t_begin + RT_CK);
+  const int nst = (t_end - t_begin + RT_KT - 1) / RT_KT;
+  const bf16* Kg = K + (size_t)g * T * D;
+  const int pos0 = T - W;
+  bf16x8 qf[RT][NC];
+  load_obs_q<D, RT>(qf, Qo, 0, h, Hq, W, hvalid, lane);
+  float rm[RT];
+  int cur[RT];
+  float acc[RT];
+#pragma unroll
+  for (int rt = 0; rt < RT; ++rt) {
+    const int u = rt * 32 + l32;
+    const bool ok = hvalid && u < W;
+    const float inv = ok ? row_inv[(size_t)h * W + u] : 0.f;
+    rm[rt] = ok && inv > 0.f ? row_m[(size_t)h * W + u] - __log2f(inv) : INFINITY;
+    cur[rt] = -1;
+    acc[rt] = 0.f;
+  }
+  for (int st = 0; st < nst; ++st) {
+    const int t0 = t_begin + st * RT_KT;
+    __syncthreads();   // the previous stage is consumed
+    KPipe<D>::copy(Ks, Kg, t0, t_end - 1, w, lane);
+    if (tid < RT_KT) cs[tid] = t0 + tid < t_end ? cid[t0 + tid] : -1;
+    wait_vmem();
+    __syncthreads();
+    if (!hvalid) continue;
+#pragma unroll
+    for (int kt = 0; kt < RT_KT / 32; ++kt) {
+      floatx16 z[RT];
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) z[rt][i] = 0.f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const bf16x8 a = KPipe<D>::frag(Ks, kt * 32 + l32, c, hg);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) z[rt] = mfma32(a, qf[rt][c], z[rt]);
+      }
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        const int u = rt * 32 + l32;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+          const int kk = kt * 32 + acc_row(i, lane);
+          const int t = t0 + kk;
+          const int c = cs[kk];
+          float pv = fast_exp2(__builtin_fmaf(z[rt][i], sl2, -rm[rt]));
+          if (t >= t_end || t > pos0 + u) pv = 0.f;
+          if (c != cur[rt]) {
+            if (cur[rt] >= 0 && u < W) atomicAdd(&m[(size_t)cur[rt] * R + h * W + u], acc[rt]);
+            cur[rt] = c;
+            acc[rt] = 0.f;
+          }
+          acc[rt] += pv;
+        }
+      }
+    }
+  }
+  if (hvalid) {
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const int u = rt * 32 + l32;
+      if (cur[rt] >= 0 && u < W) atomicAdd(&m[(size_t)cur[rt] * R + h * W + u], acc[rt]);
+    }
+  }
+}
+
+// per chunk: s[i] = (sum, sum of squares) of the pooled measure
+// mu^l_t = (1/G) sum_g mu_g[t] over the chunk; one workgroup per chunk
+__global__ __launch_bounds__(256) void chunk_stats_kernel(const float* __restrict__ mu_g,
+                                                          int Hkv, int T,
+                                                          const int32_t* __restrict__ bounds,
+                                                          float* __restrict__ stats) {
+  __shared__ float red[2][4];
+  const int i = blockIdx.x, tid = threadIdx.x;
+  const int b0 = bounds[2 * i], b1 = bounds[2 * i + 1];
+  float s1 = 0.f, s2 = 0.f;
+  for (int t = b0 + tid; t < b1; t += 256) {
+    float v = 0.f;
+    for (int g = 0; g < Hkv; ++g) v += mu_g[(size_t)g * T + t];
+    v /= (float)Hkv;
+    s1 += v;
+    s2 += v * v;
+  }
+  s1 = wave_sum(s1);
+  s2 = wave_sum(s2);
+  if ((tid & 63) == 0) {
+    red[0][tid >> 6] = s1;
+    red[1][tid >> 6] = s2;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    stats[2 * i] = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
+    stats[2 * i + 1] = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+  }
+}
+
+// priorities, their order and the greedy scan; one workgroup of 1024 threads
+__global__ __launch_bounds__(SEL_T) void prune_select_kernel(
+    const float* __restrict__ stats, const int32_t* __restrict__ bounds, int k, int R,
+    const float* __restrict__ m, float eps_s, float lam, float eps, int m0, int target,
+    float* __restrict__ prio, int8_t* __restrict__ removed, int32_t* __restrict__ removed_tokens) {
+  __shared__ float key_s[PR_MAX_CHUNKS];
+  __shared__ int key_n[PR_MAX_CHUNKS];
+  __shared__ int key_i[PR_MAX_CHUNKS];
+  __shared__ float red[SEL_T / 64];
+  __shared__ int ired[SEL_T / 64];
+  const int tid = threadIdx.x;
+  // totals: Z = sum of the chunks' pooled mass, N = candidate tokens
+  float z = 0.f;
+  int nn = 0;
+  for (int i = tid; i < k; i += SEL_T) {
+    z += stats[2 * i];
+    nn += bounds[2 * i + 1] - bounds[2 * i];
+  }
+  z = wave_sum(z);
+  if ((tid & 63) == 0) red[tid >> 6] = z;
+  const int ntot = block_excl_scan_1024(nn, ired) + nn;   // the last thread holds the total
+  __shared__ float shZ;
+  __shared__ int shN;
+  __syncthreads();
+  if (tid == SEL_T - 1) {
+    float a = 0.f;
+    for (int j = 0; j < SEL_T / 64; ++j) a += red[j];
+    shZ = a;
+    shN = ntot;
+  }
+  __syncthreads();
+  const float Z = shZ, N = (float)shN;
+  int P = 1;
+  while (P < k) P <<= 1;
+  for (int i = tid; i < P; i += SEL_T) {
+    if (i < k) {
+      const int n = bounds[2 * i + 1] - bounds[2 * i];
+      const float M = stats[2 * i] / Z, sq = stats[2 * i + 1] / (Z * Z);
+      const float pi = (float)n / N;
+      const float c = eps_s * pi / (float)n;
+      const float den = M + eps_s * pi;
+      const float ph2 = (sq + 2.f * c * M + (float)n * c * c) / (den * den);   // sum p_hat^2
+      const float ell = den / ((1.f + eps_s) * pi);
+      const float kap = n >= 2 ? logf(ph2) / logf((float)n) : 0.f;
+      const float S = logf(ell) + lam * kap;
+      prio[i] = S;
+      key_s[i] = S;
+      key_n[i] = n;
+      key_i[i] = i;
+      removed[i] = 0;
+    } else {
+      key_s[i] = INFINITY;
+      key_n[i] = 0;
+      key_i[i] = 0x7fffffff;
+    }
+  }
+  __syncthreads();
+  // bitonic sort by (S ascending, n descending, index ascending)
+  auto before = [&](int a, int b) {
+    if (key_s[a] != key_s[b]) return key_s[a] < key_s[b];
+    if (key_n[a] != key_n[b]) return key_n[a] > key_n[b];
+    return key_i[a] < key_i[b];
+  };
+  for (int size = 2; size <= P; size <<= 1) {
+    for (int stride = size >> 1; stride > 0; stride >>= 1) {
+      for (int x = tid; x < P; x += SEL_T) {
+        const int y = x ^ stride;
+        if (y > x) {
+          const bool up = (x & size) == 0;
+          if (before(y, x) == up) {
+            const float ts = key_s[x];
+            key_s[x] = key_s[y];
+            key_s[y] = ts;
+            const int tn = key_n[x];
+            key_n[x] = key_n[y];
+            key_n[y] = tn;
+            const int ti = key_i[x];
+            key_i[x] = key_i[y];
+            key_i[y] = ti;
+          }
+        }
+      }
+      __syncthreads();
+    }
+  }
+  // greedy scan: this thread's rows a = tid, tid + 1024, ...
+  constexpr int RPT = PR_MAX_ROWS / SEL_T;
+  float cur[RPT];
+#pragma unroll
+  for (int j = 0; j < RPT; ++j) cur[j] = 0.f;
+  int tokens = 0, count = 0;
+  for (int o = 0; o < k; ++o) {
+    if (tokens >= target || count + 1 > k - m0) break;
+    const int i = key_i[o];
+    const float* mi = m + (size_t)i * R;
+    float nxt[RPT];
+    bool ok = true;
+#pragma unroll
+    for (int j = 0; j < RPT; ++j) {
+      const int a = tid + j * SEL_T;
+      nxt[j] = a < R ? cur[j] + mi[a] : 0.f;
+      ok = ok && (a >= R || nxt[j] <= eps);
+    }
+    if (__syncthreads_and(ok)) {
+#pragma unroll
+      for (int j = 0; j < RPT; ++j) cur[j] = nxt[j];
+      tokens += key_n[o];
+      count += 1;
+      if (tid == 0) removed[i] = 1;
+    }
+  }
+  if (tid == 0) *removed_tokens = tokens;
+}
+
+PruneLayout prune_layout(const DecodeDims& p, int k) {
+  PruneLayout o;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = off;
+    off += align_up(bytes);
+    return at;
+  };
+  o.retain = take(retain_workspace_bytes(p));
+  o.cid = take((size_t)p.L * sizeof(int32_t));
+  o.bounds = take((size_t)2 * k * sizeof(int32_t));
+  o.stats = take((size_t)2 * k * sizeof(float));
+  o.mtab = take((size_t)k * p.Hq * p.W * sizeof(float));
+  o.total = off;
+  return o;
+}
+
+template <int D, int RT>
+static hipError_t prune_mass(const DecodeDims& p, const RetainLayout& lay, char* ws,
+                             const void* q_obs, const void* k, const int32_t* cid, float* m,
+                             hipStream_t st) {
+  dim3 grid(lay.nch, p.Hkv, (p.r + 3) / 4);
+  chunk_mass_kernel<D, RT><<<grid, 256, 0, st>>>(
+      static_cast<const bf16*>(q_obs), static_cast<const bf16*>(k), cid, p.Hq, p.Hkv, p.r, p.L,
+      p.W, p.sm_scale * kLog2e, reinterpret_cast<const float*>(ws + lay.row_m),
+      reinterpret_cast<const float*>(ws + lay.row_inv), p.Hq * p.W, m);
+  return hipGetLastError();
+}
+
+hipError_t launch_chunk_prune(const DecodeDims& p, const PruneArgs& a, const void* q_obs,
+                              const void* k, const int32_t* bounds_host, int8_t* removed,
+                              int32_t* removed_tokens, float* prio, float* row_mass, void* workspace,
+                              hipStream_t st) {
+  const PruneLayout ly = prune_layout(p, a.k);
+  const RetainLayout lay = retain_layout(p);
+  char* w = static_cast<char*>(workspace);
+  char* rws = w + ly.retain;
+  int32_t* bounds = reinterpret_cast<int32_t*>(w + ly.bounds);
+  int32_t* cid = reinterpret_cast<int32_t*>(w + ly.cid);
+  float* stats = reinterpret_cast<float*>(w + ly.stats);
+  float* m = row_mass != nullptr ? row_mass : reinterpret_cast<float*>(w + ly.mtab);
+  const int R = p.Hq * p.W;
+  hipError_t e = hipMemcpyAsync(bounds, bounds_host, (size_t)2 * a.k * sizeof(int32_t),
+                                hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return e;
+  chunk_of_kernel<<<(p.L + 255) / 256, 256, 0, st>>>(bounds, a.k, p.L, cid);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // pooled measure: the retention passes with Renyi-2 head entropies
+  const int RT = (p.W + 31) / 32;
+#define EGS_RP(DD, RR) e = retain_passes<DD, RR>(p, lay, rws, q_obs, k, EGS_RENYI, 2.0f, st)
+  if (p.D == 128) {
+    if (RT == 1) EGS_RP(128, 1);
+    else if (RT == 2) EGS_RP(128, 2);
+    else if (RT == 3) EGS_RP(128, 3);
+    else EGS_RP(128, 4);
+  } else {
+    if (RT == 1) EGS_RP(64, 1);
+    else if (RT == 2) EGS_RP(64, 2);
+    else if (RT == 3) EGS_RP(64, 3);
+    else EGS_RP(64, 4);
+  }
+#undef EGS_RP
+  if (e != hipSuccess) return e;
+  head_weight_kernel<<<p.Hkv, 64, 0, st>>>(reinterpret_cast<const float*>(rws + lay.ent), p.Hq,
+                                           p.Hkv, p.r, lay.nch, EGS_RENYI, 2.0f, a.zeta, a.tau,
+                                           reinterpret_cast<float*>(rws + lay.weight), nullptr);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  float* mu = reinterpret_cast<float*>(rws + lay.mu);
+  retain_mu_kernel<<<dim3((p.L + 255) / 256, p.Hkv), 256, 0, st>>>(
+      reinterpret_cast<const float*>(rws + lay.mass),
+      reinterpret_cast<const float*>(rws + lay.weight), nullptr, nullptr, 1.0f, p.Hq, p.Hkv, p.r,
+      p.L, mu, nullptr);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // row-chunk masses
+  const int nm = a.k * R;
+  fill_zero_kernel<<<(nm + 255) / 256, 256, 0, st>>>(m, nm);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+#define EGS_PM(DD, RR) e = prune_mass<DD, RR>(p, lay, rws, q_obs, k, cid, m, st)
+  if (p.D == 128) {
+    if (RT == 1) EGS_PM(128, 1);
+    else if (RT == 2) EGS_PM(128, 2);
+    else if (RT == 3) EGS_PM(128, 3);
+    else EGS_PM(128, 4);
+  } else {
+    if (RT == 1) EGS_PM(64, 1);
+    else if (RT == 2) EGS_PM(64, 2);
+    else if (RT == 3) EGS_PM(64, 3);
+    else EGS_PM(64, 4);
+  }
+#undef EGS_PM
+  if (e != hipSuccess) return e;
+  chunk_stats_kernel<<<a.k, 256, 0, st>>>(mu, p.Hkv, p.L, bounds, stats);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  prune_select_kernel<<<1, SEL_T, 0, st>>>(stats, bounds, a.k, R, m, a.eps_s, a.lam, a.eps, a.m0,
+                                           a.target, prio, removed, removed_tokens);
+  return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
 // Latent decoding (EntropyInfer Sec. 4.3, App. B): the cache grows by one
 // entry per generated token and is compressed once n_delay tokens have been
 // generated, then every `interval` tokens, with the latest queries (generated

@@ -30,6 +30,11 @@ Recipe (c = sqrt(d), directions orthonormal within a KV group):
   * Decode: per (batch, KV group) one unit direction; 1% of cache positions in
     [4, L-256) get + 4 * c * direction on their keys; observer and new-token
     queries of "focused" heads get + c * direction.
+  * Chunk pruning (EntroPrefill Sec. 3): a prompt of T tokens is a protected
+    prefix, k candidate documents separated by one protected delimiter token,
+    and the protected query whose last W tokens are the observers; document
+    lengths are drawn uniformly from [1/2, 3/2] of the mean and scaled to fill
+    the space between prefix and query.
 """
 from __future__ import annotations
 
@@ -41,7 +46,7 @@ import numpy as np
 __all__ = [
     "PrefillConfig", "DecodeConfig", "PREFILL_CONFIGS", "DECODE_CONFIGS",
     "PrefillInputs", "DecodeInputs", "make_prefill", "make_decode",
-    "round_to_bf16", "bf16_bits_to_f32",
+    "round_to_bf16", "bf16_bits_to_f32", "prune_chunks",
 ]
 
 
@@ -325,6 +330,28 @@ def make_decode(cfg: DecodeConfig, seed: int = 0,
     del v
     qn, qns = _store(q_new, cfg.dtype)
     return DecodeInputs(cfg, seed, qo, kk, vv, qn, qos, ks, vs, qns, focused, planted)
+
+
+def prune_chunks(T: int, W: int, k: int, n_prefix: int = 64, n_query: int = 0,
+                 seed: int = 0) -> np.ndarray:
+    """Candidate document chunks [k, 2] int32 (begin, end) for a prompt of T
+    tokens: `n_prefix` protected tokens, k documents with one protected
+    delimiter after each, then the protected query of max(n_query, W) tokens."""
+    q_len = max(n_query, W)
+    space = T - n_prefix - q_len - k
+    if k < 1 or space < k:
+        raise ValueError("prompt too short for the chunks")
+    rng = np.random.default_rng(seed)
+    w = rng.uniform(0.5, 1.5, k)
+    n = np.maximum(1, np.floor(w / w.sum() * space).astype(np.int64))
+    while n.sum() > space:
+        n[int(np.argmax(n))] -= 1
+    out = np.empty((k, 2), dtype=np.int32)
+    pos = n_prefix
+    for i in range(k):
+        out[i] = (pos, pos + n[i])
+        pos += int(n[i]) + 1
+    return out
 
 
 def small_prefill_config(**kw) -> PrefillConfig:

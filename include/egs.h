@@ -283,6 +283,48 @@ egs_status egs_sparse_decode_attn(const egs_decode_shape* shape,
                                   size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
+ * Chunk pruning of one prompt ([EP] Sec. 2.1, 3.1-3.2, 4.1-4.2).
+ * The prompt's candidate chunks c_i = [begin_i, end_i) (disjoint, ascending,
+ * before the W observer positions T-W .. T-1) may be removed; everything else
+ * is protected.
+ *   pooled measure mu_t = (1/G) sum_g sum_{h in g} w_h a^h_t: window means of
+ *     the observers' causal attention rows, Renyi-2 sink-isolated head
+ *     entropies, w_h = zeta/r + (1-zeta) softmax(-H/tau)   (Sec. 2.1, 3.1)
+ *   p = mu on the candidate tokens, renormalised; pi_i = n_i / N;
+ *   M_i = sum_{c_i} p;  p_hat_ij = (p_j + eps_s pi_i/n_i) / (M_i + eps_s pi_i);
+ *   l_i = (M_i + eps_s pi_i) / ((1 + eps_s) pi_i);
+ *   kappa_i = -H_2(p_hat_i) / ln n_i (0 for n_i = 1);
+ *   priority S_i = ln l_i + lambda kappa_i                     (Sec. 3.2)
+ *   row masses m[i][a] = sum_{t in c_i} A_{a,t}, rows a = h*W + u
+ *   greedy: chunks by (S_i ascending, n_i descending, index ascending), one
+ *     scan; chunk i is removed only if every row keeps sum_{E} m[., a] <= eps
+ *     and |E| <= k - m0; the scan stops once `target` tokens are removed
+ *                                                               (Sec. 4.2)
+ * shape: batch 1, cache_len T, n_obs W, n_sink (and the heads); its n_keep
+ * and n_recent are not used.  q_obs [Hq, W, d], k [Hkv, T, d] bf16 (device).
+ * chunk_bounds: HOST int32 [n_chunks][2].  Outputs (device): removed [k] int8,
+ * removed_tokens [1] int32, priority [k] float32, row_mass [k][Hq*W] float32
+ * or NULL.  Valid: 1 <= n_chunks <= 4096, Hq*W <= 8192, eps_s > 0,
+ * lambda >= 0, eps >= 0, m0 >= 0, target >= 0.
+ * ------------------------------------------------------------------------- */
+typedef struct {
+  double eps_s;     /* null smoothing epsilon_s > 0 */
+  double lambda;    /* concentration weight >= 0 */
+  double eps;       /* deletion budget of every observer row (epsilon_a) */
+  int32_t m0;       /* at least m0 chunks stay */
+  int32_t target;   /* stop once this many tokens are removed */
+  double zeta;      /* head-weight floor in (0, 1] */
+  double tau;       /* head-weight temperature > 0 */
+} egs_prune_params;
+
+size_t egs_chunk_prune_workspace(const egs_decode_shape* shape, int32_t n_chunks);
+egs_status egs_chunk_prune(const egs_decode_shape* shape, const egs_prune_params* params,
+                           const void* q_obs, const void* k, const int32_t* chunk_bounds,
+                           int32_t n_chunks, int8_t* removed, int32_t* removed_tokens,
+                           float* priority, float* row_mass, void* workspace,
+                           size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
  * Latent decoding ([EI] Sec. 4.3 and App. B: compress the cache only after
  * N_D tokens have been generated, with an observation window that holds the
  * generated tokens' queries; [KV] InfoKV: compress again every fixed number of

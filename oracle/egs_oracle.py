@@ -628,25 +628,42 @@ def _obs_rows(q_obs_h, k_g, T, sc):
 
 
 def prune_pooled_measure(q_obs, k, n_sink: int, zeta: float = 0.5, tau: float = 1.0,
-                         sm_scale=None):
+                         sm_scale=None, rows: bool = True):
     """mu^l_j = (1/G) sum_g sum_{h in g} w_h a^h_j with the window means a^h,
     Renyi-2 sink-isolated head entropies and the regularized weights
     ([EP] Sec. 3.1); q_obs [Hq, W, d], k [Hkv, T, d].  Returns (mu [T],
-    A [Hq, W, T])."""
-    q_obs = np.asarray(q_obs, dtype=np.float64)
-    k = np.asarray(k, dtype=np.float64)
-    Hq, W, d = q_obs.shape
-    Hkv, T, _ = k.shape
+    A [Hq, W, T]); with rows=False, A is not kept (None) and the heads'
+    rows are formed one head at a time."""
+    Hq, W, d = np.shape(q_obs)
+    Hkv, T, _ = np.shape(k)
     r = Hq // Hkv
     sc = _sm_scale(d, sm_scale)
-    A = np.stack([_obs_rows(q_obs[h], k[h // r], T, sc) for h in range(Hq)])
+    A = np.empty((Hq, W, T)) if rows else None
     mu = np.zeros(T)
     for g in range(Hkv):
-        a = A[g * r:(g + 1) * r].mean(axis=1)
+        kg = np.asarray(k[g], dtype=np.float64)
+        a = np.empty((r, T))
+        for i in range(r):
+            h = g * r + i
+            Ah = _obs_rows(np.asarray(q_obs[h], dtype=np.float64), kg, T, sc)
+            a[i] = Ah.mean(axis=0)
+            if rows:
+                A[h] = Ah
         H = np.array([sink_isolated_entropy(a[i], n_sink, RENYI, 2.0) for i in range(r)])
         w = head_weights(H, zeta, tau)
         mu += (w[:, None] * a).sum(axis=0)
     return mu / Hkv, A
+
+
+def prune_head_rows(q_obs, k, h: int, sm_scale=None) -> np.ndarray:
+    """A[h] alone, the observer rows [W, T] of query head h over its group's
+    keys ([EP] Sec. 2.1), for checking single heads at sizes where all of A
+    does not fit."""
+    Hq, W, d = np.shape(q_obs)
+    Hkv, T, _ = np.shape(k)
+    g = h // (Hq // Hkv)
+    return _obs_rows(np.asarray(q_obs[h], dtype=np.float64), np.asarray(k[g], dtype=np.float64),
+                     T, _sm_scale(d, sm_scale))
 
 
 def prune_row_chunk_mass(A, chunks) -> np.ndarray:

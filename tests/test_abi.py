@@ -256,3 +256,32 @@ def test_latent_step_errors(L):
     assert L.LIB.egs_latent_decode_step(ctypes.byref(sc), ctypes.byref(prm), None, FAKE, FAKE,
                                         FAKE, FAKE, FAKE, FAKE, FAKE, None, FAKE, ws,
                                         None) == L.EGS_EINVAL
+
+
+def test_chunk_prune_errors(L):
+    import numpy as np
+    sc = _dshape(L, batch=1, cache_len=4096, n_obs=64)
+    good = np.array([[10, 100], [100, 200], [300, 4032]], dtype=np.int32)
+    P = lambda **kw: L.PruneParamsC(**{**dict(eps_s=0.1, lam=0.5, eps=0.05, m0=0, target=100,
+                                              zeta=0.5, tau=1.0), **kw})
+    ws = L.LIB.egs_chunk_prune_workspace(ctypes.byref(sc), 3)
+    assert ws > 0
+
+    def call(bounds=good, nk=None, prm=None, wsb=ws, shape=sc):
+        b = np.ascontiguousarray(bounds, dtype=np.int32)
+        return L.LIB.egs_chunk_prune(ctypes.byref(shape), ctypes.byref(prm or P()), FAKE, FAKE,
+                                     b.ctypes.data_as(ctypes.c_void_p),
+                                     len(b) if nk is None else nk, FAKE, FAKE, FAKE, None, FAKE,
+                                     wsb, None)
+
+    assert call(bounds=np.array([[10, 100], [90, 200]])) == L.EGS_EINVAL     # overlap
+    assert call(bounds=np.array([[10, 100], [100, 4040]])) == L.EGS_EINVAL   # into observers
+    assert call(bounds=np.array([[50, 50]])) == L.EGS_EINVAL                 # empty chunk
+    assert call(nk=0) == L.EGS_EINVAL
+    assert call(prm=P(eps_s=0.0)) == L.EGS_EINVAL
+    assert call(prm=P(lam=-1.0)) == L.EGS_EINVAL
+    assert call(prm=P(target=-1)) == L.EGS_EINVAL
+    assert call(wsb=ws - 1) == L.EGS_EWORKSPACE
+    assert call(shape=_dshape(L, batch=2, cache_len=4096, n_obs=64)) == L.EGS_EINVAL
+    big = _dshape(L, batch=1, n_q_heads=128, n_kv_heads=8, cache_len=4096, n_obs=128)
+    assert call(shape=big) == L.EGS_ENOTSUP                                  # 16384 rows

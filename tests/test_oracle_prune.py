@@ -119,3 +119,23 @@ def test_certificate_weak_duality_by_brute_force():
         for _ in range(5):
             y, t = float(rng.uniform(0, 50)), float(rng.uniform(0, 10))
             assert O.prune_certificate(n, m, eps, m0, y, t) >= best - 1e-9
+
+
+def test_streaming_paths_agree_with_the_stacked_rows():
+    # rows=False (no A kept) and single-head rows give the same values as the
+    # stacked computation; each observer row is a causal softmax over T keys
+    rng = np.random.default_rng(5)
+    Hq, Hkv, W, d, T = 6, 2, 7, 16, 90
+    q = rng.standard_normal((Hq, W, d))
+    k = rng.standard_normal((Hkv, T, d))
+    mu, A = O.prune_pooled_measure(q, k, n_sink=3)
+    mu2, none = O.prune_pooled_measure(q, k, n_sink=3, rows=False)
+    assert none is None
+    np.testing.assert_array_equal(mu, mu2)
+    for h in range(Hq):
+        np.testing.assert_array_equal(O.prune_head_rows(q, k, h), A[h])
+    u = 2                                         # observer u sits at T - W + u
+    z = k[1] @ q[4, u] / math.sqrt(d)
+    z[T - W + u + 1:] = -np.inf
+    p = np.exp(z - z.max())
+    np.testing.assert_allclose(A[4, u], p / p.sum(), atol=1e-15)

@@ -1,0 +1,143 @@
+"""GPU parity of chunk pruning (EntroPrefill Sec. 3.1-3.2, 4.1-4.2) through the
+C ABI: row-chunk masses and priorities against the oracle's float64 values,
+and the removal decisions bit-exact against the oracle's greedy proposer run
+on the GPU's own float32 priorities and masses, in float32 (floating point
+decides the integer outputs, so both sides decide in the same precision)."""
+import numpy as np
+import pytest
+import torch
+
+from _parity import dev_tensor, log
+from entropy_guided_sparse_amd import synth
+from oracle import egs_oracle as O
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def api():
+    if not torch.cuda.is_available():
+        pytest.skip("no HIP device")
+    from entropy_guided_sparse_amd import api as A
+    return A
+
+
+def _chunks(rng, T, W, k, lo=64):
+    """k disjoint chunks with protected gaps, before the observers."""
+    edges = np.sort(rng.choice(np.arange(lo, T - W), 2 * k, replace=False))
+    return [(int(edges[2 * i]), int(edges[2 * i + 1])) for i in range(k)]
+
+
+def _run(api, Hq, Hkv, T, W, chunks, eps_s, lam, eps, m0, target, seed=0, n_sink=4):
+    cfg = synth.DecodeConfig("prune", 1, Hq, Hkv, 128, T, W, n_sink, 16, 16)
+    inp = synth.make_decode(cfg, seed=seed)
+    log(f"[prune] Hq={Hq} Hkv={Hkv} T={T} W={W} chunks={len(chunks)} eps={eps} m0={m0} "
+        f"target={target} lam={lam}")
+    shape = api.DecodeShape(1, Hq, Hkv, 128, T, W, n_sink, 16, 16)
+    q = dev_tensor(inp.q_obs_store[0], "bf16")
+    k = dev_tensor(inp.k_store[0], "bf16")
+    removed, tokens, prio, mass = api.chunk_prune(shape, q, k, chunks, eps_s, lam, eps, m0,
+                                                  target, want_row_mass=True)
+    torch.cuda.synchronize()
+    g_rem = removed.cpu().numpy().astype(bool)
+    g_tok = int(tokens.cpu().item())
+    g_S = prio.cpu().numpy()
+    g_m = mass.cpu().numpy()                          # [k, R]
+    mu, A = O.prune_pooled_measure(inp.q_obs[0], inp.k[0], n_sink)
+    r_m = O.prune_row_chunk_mass(A, chunks)           # [R, k]
+    r_S = O.prune_priorities(mu, chunks, eps_s, lam)[0]
+    dm = float(np.abs(g_m.T - r_m).max())
+    dS = float(np.abs(g_S - r_S).max())
+    log(f"  row mass max|d|={dm:.3e} priority max|d|={dS:.3e} removed={int(g_rem.sum())} "
+        f"tokens={g_tok}")
+    assert dm <= 1e-4
+    assert dS <= 2e-3
+    n = np.array([e - b for (b, e) in chunks])
+    o_rem, o_tok = O.prune_greedy(g_S.astype(np.float64), n, g_m.T, eps, m0, target,
+                                  dtype=np.float32)
+    np.testing.assert_array_equal(g_rem, o_rem)
+    assert g_tok == o_tok
+    # feasibility of the GPU's set on the oracle's own masses (within rounding)
+    assert np.all(r_m[:, g_rem].sum(axis=1) <= eps + 1e-4)
+    assert g_rem.sum() <= max(len(chunks) - m0, 0)
+    return g_rem, g_tok
+
+
+@pytest.mark.parametrize("case", ["basic", "tight_rows", "loose_rows", "count_bound",
+                                  "nothing_removable", "zero_target", "w_odd"])
+def test_chunk_prune(api, case):
+    rng = np.random.default_rng(3)
+    T, W = 4096, 64
+    chunks = _chunks(rng, T, W, 24)
+    kw = dict(Hq=8, Hkv=2, T=T, W=W, chunks=chunks, eps_s=0.1, lam=0.5, eps=0.05, m0=2,
+              target=T // 2)
+    if case == "tight_rows":
+        kw.update(eps=0.005)
+    elif case == "loose_rows":
+        kw.update(eps=10.0, target=10 ** 6)
+    elif case == "count_bound":
+        kw.update(eps=10.0, target=10 ** 6, m0=20)
+    elif case == "nothing_removable":
+        kw.update(eps=0.0)
+    elif case == "zero_target":
+        kw.update(target=0)
+    elif case == "w_odd":
+        kw.update(W=40, Hq=6, Hkv=3, lam=1.5, chunks=_chunks(rng, T, 40, 31))
+    rem, tok = _run(api, **kw)
+    if case == "loose_rows":                  # only the count bound k - m0 binds
+        assert rem.sum() == 24 - 2
+    if case == "count_bound":
+        assert rem.sum() == 24 - 20
+    if case in ("nothing_removable", "zero_target"):
+        assert not rem.any() and tok == 0
+
+
+def test_chunk_prune_single_and_unit_chunks(api):
+    _run(api, 4, 2, 1024, 32, [(100, 101)], 0.2, 0.3, 1.0, 0, 10)
+    _run(api, 4, 2, 1024, 32, [(5, 6), (6, 9), (9, 300), (400, 401), (500, 990)], 0.2, 0.3,
+         0.5, 1, 10 ** 6)
+
+
+def test_chunk_prune_full_context(api):
+    """One 128k prompt with 32 query / 8 KV heads, 64 observers and 64 candidate
+    documents (the decode workload's shape at batch 1, the launch the bench
+    times): priorities against the oracle's pooled measure, the row masses of
+    three sampled heads against the oracle's rows, the greedy decisions
+    replayed on the GPU's values, and feasibility."""
+    cfg = synth.DECODE_CONFIGS["decode-retain-b8-128k"]
+    inp = synth.make_decode(cfg, seed=11, batch=1)
+    Hq, Hkv, W, T = cfg.n_q_heads, cfg.n_kv_heads, cfg.n_obs, cfg.cache_len
+    chunks = synth.prune_chunks(T, W, 64, seed=11)
+    eps, m0, target = 0.1, 4, T // 2
+    log(f"[prune full] Hq={Hq} Hkv={Hkv} T={T} W={W} chunks=64")
+    shape = api.DecodeShape(1, Hq, Hkv, cfg.head_dim, T, W, cfg.n_sink, cfg.n_recent,
+                            cfg.n_keep)
+    q = dev_tensor(inp.q_obs_store[0], "bf16")
+    k = dev_tensor(inp.k_store[0], "bf16")
+    removed, tokens, prio, mass = api.chunk_prune(shape, q, k, chunks, 0.1, 0.5, eps, m0,
+                                                  target, want_row_mass=True)
+    torch.cuda.synchronize()
+    g_rem = removed.cpu().numpy().astype(bool)
+    g_tok = int(tokens.cpu().item())
+    g_S = prio.cpu().numpy()
+    g_m = mass.cpu().numpy().T                        # [R, k]
+    del q, k
+    cl = [tuple(map(int, c)) for c in chunks]
+    mu, _ = O.prune_pooled_measure(inp.q_obs[0], inp.k[0], cfg.n_sink, rows=False)
+    r_S = O.prune_priorities(mu, cl, 0.1, 0.5)[0]
+    dS = float(np.abs(g_S - r_S).max())
+    dm = 0.0
+    for h in (0, 13, Hq - 1):
+        r_m = O.prune_row_chunk_mass(O.prune_head_rows(inp.q_obs[0], inp.k[0], h)[None], cl)
+        dm = max(dm, float(np.abs(g_m[h * W:(h + 1) * W] - r_m).max()))
+    log(f"  priority max|d|={dS:.3e} sampled row mass max|d|={dm:.3e} "
+        f"removed={int(g_rem.sum())} tokens={g_tok}")
+    assert dS <= 2e-3 and dm <= 1e-4
+    n = chunks[:, 1] - chunks[:, 0]
+    o_rem, o_tok = O.prune_greedy(g_S.astype(np.float64), n, g_m, eps, m0, target,
+                                  dtype=np.float32)
+    np.testing.assert_array_equal(g_rem, o_rem)
+    assert g_tok == o_tok == int(n[g_rem].sum())
+    assert np.all(g_m[:, g_rem].astype(np.float64).sum(axis=1) <= eps + 1e-5)
+    # chunks never hold more than a row's whole mass (protected tokens hold the rest)
+    assert np.all(g_m.astype(np.float64).sum(axis=1) <= 1.0 + 1e-4)
