@@ -42,7 +42,7 @@ struct PruneArgs {
   int m0, target;
 };
 struct PruneLayout {
-  size_t retain, cid, bounds, stats, mtab, total;
+  size_t retain, cid, bounds, segb, stats, mtab, seg_v, seg_m, total;
 };
 constexpr int kMaxPruneChunks = 4096;
 constexpr int kMaxPruneRows = 8192;

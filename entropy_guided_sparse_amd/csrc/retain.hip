@@ -147,19 +147,42 @@ __device__ __forceinline__ void load_obs_q(bf16x8 (&qf)[RT][D / 16], const bf16*
 // workgroup keeps three 16-KB copies in flight against HBM latency; the pass-2
 // masses collect in LDS and leave after the loop, so that only the copies
 // are outstanding while the loop waits on them.
+// SEG (pass 1 of chunk pruning, one sequence): the same tile sums are also
+// split by candidate chunk.  A row's sum over the keys of chunk c in this
+// span, taken against the row's reference, is written with that reference as
+// segment seg_base[c] + span - first span of c, row h * W + u, of
+// (seg_v, seg_m); after the combine, chunk_norm_kernel turns the segments
+// into probabilities.  Tiles inside one chunk cost one add; tiles where a
+// chunk starts or ends split the sum by the chunk ids of their keys.
 // ---------------------------------------------------------------------------
 constexpr int RT_DEPTH = 4;
 
-template <int D, int RT, bool MASS>
+__device__ __forceinline__ int wave_min_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = min(v, __shfl_xor(v, o));
+  return v;
+}
+__device__ __forceinline__ int wave_max_i(int v) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v = max(v, __shfl_xor(v, o));
+  return v;
+}
+
+template <int D, int RT, bool MASS, bool SEG = false>
 __global__ __launch_bounds__(256) void obs_pass_kernel(
     const bf16* __restrict__ Qo, const bf16* __restrict__ K, int Hq, int Hkv, int r, int L,
     int ldk, int W, int nch, float sl2, float* __restrict__ stat_m, float* __restrict__ stat_l,
     const float* __restrict__ row_m, const float* __restrict__ row_inv, int n_sink, int kind,
-    float alpha, float* __restrict__ mass, float* __restrict__ ent) {
+    float alpha, float* __restrict__ mass, float* __restrict__ ent,
+    const int32_t* __restrict__ cid = nullptr, const int32_t* __restrict__ bounds = nullptr,
+    const int32_t* __restrict__ seg_base = nullptr, float* __restrict__ seg_v = nullptr,
+    float* __restrict__ seg_m = nullptr) {
+  static_assert(!SEG || !MASS, "chunk segments ride on pass 1");
   constexpr int NC = D / 16;
   constexpr int PW = KPipe<D>::PER_W;
   __shared__ __attribute__((aligned(1024))) bf16 Ks[RT_DEPTH][RT_KT * D];
   __shared__ float mbuf[MASS ? 4 * RT_CK : 1];
+  __shared__ int cs[SEG ? RT_CK : 1];
   const int chunk = blockIdx.x, bg = blockIdx.y;
   const int b = bg / Hkv, g = bg % Hkv;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -198,6 +221,33 @@ __global__ __launch_bounds__(256) void obs_pass_kernel(
         rm[rt][i] = ok && inv > 0.f ? row_m[rbase + u] - __log2f(inv) : INFINITY;
       }
   }
+  // chunk segments: the chunk id of every key of the span (-1 outside the
+  // chunks and past the end), read after the first barrier of the loop; the
+  // open chunk and its sums against m
+  float cacc[RT];
+  int curc = -1;
+  if constexpr (SEG) {
+    for (int j = tid; j < RT_CK; j += 256) cs[j] = t_begin + j < t_end ? cid[t_begin + j] : -1;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) cacc[rt] = 0.f;
+  }
+  // closes the open chunk c: both halves of the row to one reference
+  auto flush = [&](int c) {
+    if (c < 0) return;
+    const int seg = seg_base[c] + chunk - bounds[2 * c] / RT_CK;
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt) {
+      const float M = xhalf_max(m[rt]);
+      const float v = xhalf_sum(cacc[rt] * fast_exp2(m[rt] - M));
+      const int u = rt * 32 + l32;
+      if (hg == 0 && u < W) {
+        const size_t o = (size_t)seg * Hq * W + (size_t)h * W + u;
+        seg_v[o] = v;
+        seg_m[o] = M;
+      }
+      cacc[rt] = 0.f;
+    }
+  };
   wait_vmem();   // only the copies below are in flight from here on
 #pragma unroll
   for (int d = 0; d < RT_DEPTH - 1; ++d)
@@ -223,6 +273,18 @@ __global__ __launch_bounds__(256) void obs_pass_kernel(
           const bf16x8 a = KPipe<D>::frag(ks, kt * 32 + l32, c, hg);
 #pragma unroll
           for (int rt = 0; rt < RT; ++rt) z[rt] = mfma32(a, qf[rt][c], z[rt]);
+        }
+        // chunk ids rise with the position: keys tk and tk + 31 in one chunk
+        // means the whole tile is in it
+        int tc = -1;
+        if constexpr (SEG) {
+          const int cf = __builtin_amdgcn_readfirstlane(cs[tk - t_begin]);
+          const int cb = __builtin_amdgcn_readfirstlane(cs[tk + 31 - t_begin]);
+          tc = (cf == cb && cf >= 0) ? cf : -2;
+          if (tc >= 0 && tc != curc) {
+            flush(curc);
+            curc = tc;
+          }
         }
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
@@ -252,10 +314,46 @@ __global__ __launch_bounds__(256) void obs_pass_kernel(
             sum = 0.f;
 #pragma unroll
             for (int i = 0; i < 16; ++i) sum += fast_exp2(__builtin_fmaf(z[rt][i], sl2, -mn));
-            l[rt] *= fast_exp2(m[rt] - mn);
+            const float sc = fast_exp2(m[rt] - mn);
+            l[rt] *= sc;
+            if constexpr (SEG) cacc[rt] *= sc;
             m[rt] = mn;
           }
           l[rt] += sum;
+          if constexpr (SEG) {
+            if (tc >= 0) cacc[rt] += sum;
+          }
+        }
+        if constexpr (SEG) {
+          if (tc == -2) {
+            // a chunk starts or ends in this tile (or none is in it): the
+            // ids of the lane's keys, the range lo..hi over the wave, and
+            // the sums split by id
+            int ci[16];
+            int lo = 0x7fffffff, hi = -1;
+#pragma unroll
+            for (int i = 0; i < 16; ++i) {
+              ci[i] = cs[tk - t_begin + acc_row(i, lane)];
+              if (ci[i] >= 0) lo = min(lo, ci[i]);
+              hi = max(hi, ci[i]);
+            }
+            lo = __builtin_amdgcn_readfirstlane(wave_min_i(lo));
+            hi = __builtin_amdgcn_readfirstlane(wave_max_i(hi));
+            for (int cc = lo; cc <= hi; ++cc) {
+              if (cc != curc) {
+                flush(curc);
+                curc = cc;
+              }
+#pragma unroll
+              for (int rt = 0; rt < RT; ++rt) {
+                float part = 0.f;
+#pragma unroll
+                for (int i = 0; i < 16; ++i)
+                  if (ci[i] == cc) part += fast_exp2(__builtin_fmaf(z[rt][i], sl2, -m[rt]));
+                cacc[rt] += part;
+              }
+            }
+          }
         }
       } else {
         // Z: lane owns key (tk + l32), registers hold observer rows
@@ -309,6 +407,7 @@ __global__ __launch_bounds__(256) void obs_pass_kernel(
     }
   }
   if (!hvalid) return;
+  if constexpr (SEG) flush(curc);
   if (!MASS) {
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
@@ -762,10 +861,19 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(float* __restrict__ x, i
 // ---------------------------------------------------------------------------
 // launcher
 // ---------------------------------------------------------------------------
+// With sg (chunk pruning, batch 1), pass 1 also writes the chunk segments.
+struct SegArgs {
+  const int32_t* cid;
+  const int32_t* bounds;
+  const int32_t* seg_base;
+  float* seg_v;
+  float* seg_m;
+};
+
 template <int D, int RT>
 static hipError_t retain_passes(const DecodeDims& p, const RetainLayout& lay, char* ws,
                                 const void* q_obs, const void* k, int kind, float alpha,
-                                hipStream_t st) {
+                                hipStream_t st, const SegArgs* sg = nullptr) {
   const float sl2 = p.sm_scale * kLog2e;
   dim3 grid(lay.nch, p.B * p.Hkv, (p.r + 3) / 4);
   const bf16* Qo = static_cast<const bf16*>(q_obs);
@@ -776,16 +884,22 @@ static hipError_t retain_passes(const DecodeDims& p, const RetainLayout& lay, ch
   float* row_inv = reinterpret_cast<float*>(ws + lay.row_inv);
   float* mass = reinterpret_cast<float*>(ws + lay.mass);
   float* ent = reinterpret_cast<float*>(ws + lay.ent);
-  obs_pass_kernel<D, RT, false><<<grid, 256, 0, st>>>(Qo, K, p.Hq, p.Hkv, p.r, p.L, p.Lk, p.W, lay.nch,
-                                                      sl2, stat_m, stat_l, row_m, row_inv,
-                                                      p.n_sink, kind, alpha, mass, ent);
+  if (sg != nullptr)
+    obs_pass_kernel<D, RT, false, true><<<grid, 256, 0, st>>>(
+        Qo, K, p.Hq, p.Hkv, p.r, p.L, p.Lk, p.W, lay.nch, sl2, stat_m, stat_l, row_m, row_inv,
+        p.n_sink, kind, alpha, mass, ent, sg->cid, sg->bounds, sg->seg_base, sg->seg_v,
+        sg->seg_m);
+  else
+    obs_pass_kernel<D, RT, false><<<grid, 256, 0, st>>>(Qo, K, p.Hq, p.Hkv, p.r, p.L, p.Lk, p.W,
+                                                        lay.nch, sl2, stat_m, stat_l, row_m,
+                                                        row_inv, p.n_sink, kind, alpha, mass, ent);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   obs_combine_kernel<<<p.B * p.Hq, 256, 0, st>>>(stat_m, stat_l, lay.nch, p.W, row_m, row_inv);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  obs_pass_kernel<D, RT, true><<<grid, 256, 0, st>>>(Qo, K, p.Hq, p.Hkv, p.r, p.L, p.Lk, p.W, lay.nch,
-                                                     sl2, stat_m, stat_l, row_m, row_inv,
-                                                     p.n_sink, kind, alpha, mass, ent);
+  obs_pass_kernel<D, RT, true><<<grid, 256, 0, st>>>(Qo, K, p.Hq, p.Hkv, p.r, p.L, p.Lk, p.W,
+                                                     lay.nch, sl2, stat_m, stat_l, row_m,
+                                                     row_inv, p.n_sink, kind, alpha, mass, ent);
   return hipGetLastError();
 }
 
@@ -1094,109 +1208,96 @@ __global__ __launch_bounds__(256) void chunk_of_kernel(const int32_t* __restrict
   cid[t] = (id >= 0 && t < bounds[2 * id + 1]) ? id : -1;
 }
 
-// m[i][a] += sum over the positions t of chunk i of A_{a,t}, rows a = h*W + u.
-// Workgroup = (1024-key span, KV group, 4-head group); 64-key K stages in LDS
-// shared by the four heads; S^T with keys as M so a lane owns an observer
-// row, its probabilities summed per chunk in registers (chunk ids rise with
-// the position) and added to m when the chunk changes.
-template <int D, int RT>
-__global__ __launch_bounds__(256) void chunk_mass_kernel(
-    const bf16* __restrict__ Qo, const bf16* __restrict__ K, const int32_t* __restrict__ cid,
-    int Hq, int Hkv, int r, int T, int W, float sl2, const float* __restrict__ row_m,
-    const float* __restrict__ row_inv, int R, float* __restrict__ m) {
-  constexpr int NC = D / 16;
-  __shared__ __attribute__((aligned(1024))) bf16 Ks[RT_KT * D];
-  __shared__ int cs[RT_KT];
-  const int span = blockIdx.x, g = blockIdx.y;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int l32 = lane & 31, hg = lane >> 5;
-  const int hl = blockIdx.z * 4 + w;
-  const bool hvalid = hl < r;
-  const int h = g * r + (hvalid ? hl : 0);
-  const int t_begin = span * RT_CK, t_end = min(T, t_begin + RT_CK);
-  const int nst = (t_end - t_begin + RT_KT - 1) / RT_KT;
-  const bf16* Kg = K + (size_t)g * T * D;
-  const int pos0 = T - W;
-  bf16x8 qf[RT][NC];
-  load_obs_q<D, RT>(qf, Qo, 0, h, Hq, W, hvalid, lane);
-  float rm[RT];
-  int cur[RT];
-  float acc[RT];
+// first segment of every chunk: seg_base[c] = sum over c' < c of the number of
+// 1024-key spans chunk c' touches; seg_base[k] = the total.  One workgroup.
+__global__ __launch_bounds__(SEL_T) void seg_base_kernel(const int32_t* __restrict__ bounds,
+                                                         int k, int32_t* __restrict__ seg_base) {
+  __shared__ int ired[SEL_T / 64];
+  constexpr int PER = PR_MAX_CHUNKS / SEL_T;
+  const int tid = threadIdx.x;
+  int n[PER], own = 0;
 #pragma unroll
-  for (int rt = 0; rt < RT; ++rt) {
-    const int u = rt * 32 + l32;
-    const bool ok = hvalid && u < W;
-    const float inv = ok ? row_inv[(size_t)h * W + u] : 0.f;
-    rm[rt] = ok && inv > 0.f ? row_m[(size_t)h * W + u] - __log2f(inv) : INFINITY;
-    cur[rt] = -1;
-    acc[rt] = 0.f;
+  for (int j = 0; j < PER; ++j) {
+    const int c = tid * PER + j;
+    n[j] = c < k ? (bounds[2 * c + 1] - 1) / RT_CK - bounds[2 * c] / RT_CK + 1 : 0;
+    own += n[j];
   }
-  for (int st = 0; st < nst; ++st) {
-    const int t0 = t_begin + st * RT_KT;
-    __syncthreads();   // the previous stage is consumed
-    KPipe<D>::copy(Ks, Kg, t0, t_end - 1, w, lane);
-    if (tid < RT_KT) cs[tid] = t0 + tid < t_end ? cid[t0 + tid] : -1;
-    wait_vmem();
-    __syncthreads();
-    if (!hvalid) continue;
+  int pos = block_excl_scan_1024(own, ired);
 #pragma unroll
-    for (int kt = 0; kt < RT_KT / 32; ++kt) {
-      floatx16 z[RT];
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt)
-#pragma unroll
-        for (int i = 0; i < 16; ++i) z[rt][i] = 0.f;
-#pragma unroll
-      for (int c = 0; c < NC; ++c) {
-        const bf16x8 a = KPipe<D>::frag(Ks, kt * 32 + l32, c, hg);
-#pragma unroll
-        for (int rt = 0; rt < RT; ++rt) z[rt] = mfma32(a, qf[rt][c], z[rt]);
-      }
-#pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        const int u = rt * 32 + l32;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const int kk = kt * 32 + acc_row(i, lane);
-          const int t = t0 + kk;
-          const int c = cs[kk];
-          float pv = fast_exp2(__builtin_fmaf(z[rt][i], sl2, -rm[rt]));
-          if (t >= t_end || t > pos0 + u) pv = 0.f;
-          if (c != cur[rt]) {
-            if (cur[rt] >= 0 && u < W) atomicAdd(&m[(size_t)cur[rt] * R + h * W + u], acc[rt]);
-            cur[rt] = c;
-            acc[rt] = 0.f;
-          }
-          acc[rt] += pv;
-        }
-      }
-    }
-  }
-  if (hvalid) {
-#pragma unroll
-    for (int rt = 0; rt < RT; ++rt) {
-      const int u = rt * 32 + l32;
-      if (cur[rt] >= 0 && u < W) atomicAdd(&m[(size_t)cur[rt] * R + h * W + u], acc[rt]);
-    }
+  for (int j = 0; j < PER; ++j) {
+    const int c = tid * PER + j;
+    if (c < k) seg_base[c] = pos;
+    pos += n[j];
+    if (c == k - 1) seg_base[k] = pos;
   }
 }
 
-// per chunk: s[i] = (sum, sum of squares) of the pooled measure
-// mu^l_t = (1/G) sum_g mu_g[t] over the chunk; one workgroup per chunk
-__global__ __launch_bounds__(256) void chunk_stats_kernel(const float* __restrict__ mu_g,
-                                                          int Hkv, int T,
+// m[c][a] = sum over the segments of chunk c of seg_v exp2(seg_m - M_a) / L_a,
+// with the row's final reference M_a and sum L_a (row_m, row_inv);
+// workgroup per chunk, thread per row a = h * W + u
+__global__ __launch_bounds__(256) void chunk_norm_kernel(
+    const int32_t* __restrict__ seg_base, const float* __restrict__ seg_v,
+    const float* __restrict__ seg_m, const float* __restrict__ row_m,
+    const float* __restrict__ row_inv, int R, float* __restrict__ m) {
+  const int c = blockIdx.x;
+  const int s0 = seg_base[c], s1 = seg_base[c + 1];
+  for (int a = threadIdx.x; a < R; a += 256) {
+    const float M = row_m[a], inv = row_inv[a];
+    float acc = 0.f;
+    for (int sg = s0; sg < s1; ++sg)
+      acc += seg_v[(size_t)sg * R + a] * fast_exp2(seg_m[(size_t)sg * R + a] - M);
+    m[(size_t)c * R + a] = acc * inv;
+  }
+}
+
+// pooled measure mu^l_t = (1/G) sum_g sum_{h in g} w_h a^h_t of one sequence
+// (the group sums in head order, then the mean over groups); one thread per
+// position, the head masses in rounds of eight loads issued together
+__global__ __launch_bounds__(256) void pooled_mu_kernel(const float* __restrict__ mass,
+                                                        const float* __restrict__ weight, int Hq,
+                                                        int Hkv, int r, int L,
+                                                        float* __restrict__ pooled) {
+  const int t = blockIdx.x * 256 + threadIdx.x;
+  if (t >= L) return;
+  float tot = 0.f;
+  for (int g = 0; g < Hkv; ++g) {
+    float acc = 0.f;
+    for (int h0 = 0; h0 < r; h0 += 8) {
+      float mv[8], wh[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const int h = g * r + min(h0 + j, r - 1);
+        mv[j] = mass[(size_t)h * L + t];
+        wh[j] = weight[h];
+      }
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        if (h0 + j < r) acc += wh[j] * mv[j];
+    }
+    tot += acc;
+  }
+  pooled[t] = tot / (float)Hkv;
+}
+
+// per chunk: s[i] = (sum, sum of squares) of the pooled measure over the
+// chunk; one workgroup per chunk, eight coalesced loads in flight per thread
+__global__ __launch_bounds__(256) void chunk_stats_kernel(const float* __restrict__ pooled,
                                                           const int32_t* __restrict__ bounds,
                                                           float* __restrict__ stats) {
   __shared__ float red[2][4];
   const int i = blockIdx.x, tid = threadIdx.x;
   const int b0 = bounds[2 * i], b1 = bounds[2 * i + 1];
   float s1 = 0.f, s2 = 0.f;
-  for (int t = b0 + tid; t < b1; t += 256) {
-    float v = 0.f;
-    for (int g = 0; g < Hkv; ++g) v += mu_g[(size_t)g * T + t];
-    v /= (float)Hkv;
-    s1 += v;
-    s2 += v * v;
+  for (int base = b0; base < b1; base += 8 * 256) {
+    float v[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) v[j] = pooled[min(base + j * 256 + tid, b1 - 1)];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (base + j * 256 + tid < b1) {
+        s1 += v[j];
+        s2 += v[j] * v[j];
+      }
   }
   s1 = wave_sum(s1);
   s2 = wave_sum(s2);
@@ -1211,7 +1312,11 @@ __global__ __launch_bounds__(256) void chunk_stats_kernel(const float* __restric
   }
 }
 
-// priorities, their order and the greedy scan; one workgroup of 1024 threads
+// priorities, their order and the greedy scan; one workgroup of 1024 threads,
+// thread tid keeping the running sums of rows tid + j * 1024, j < RPT.  The
+// scan is sequential over the sorted chunks; their mass columns are fetched
+// PR_PF chunks at a time so that one memory latency covers PR_PF steps.
+template <int RPT>
 __global__ __launch_bounds__(SEL_T) void prune_select_kernel(
     const float* __restrict__ stats, const int32_t* __restrict__ bounds, int k, int R,
     const float* __restrict__ m, float eps_s, float lam, float eps, int m0, int target,
@@ -1296,30 +1401,43 @@ __global__ __launch_bounds__(SEL_T) void prune_select_kernel(
       __syncthreads();
     }
   }
-  // greedy scan: this thread's rows a = tid, tid + 1024, ...
-  constexpr int RPT = PR_MAX_ROWS / SEL_T;
+  // greedy scan (the stop test only depends on uniform values, so every
+  // thread leaves at the same step)
   float cur[RPT];
 #pragma unroll
   for (int j = 0; j < RPT; ++j) cur[j] = 0.f;
   int tokens = 0, count = 0;
-  for (int o = 0; o < k; ++o) {
-    if (tokens >= target || count + 1 > k - m0) break;
-    const int i = key_i[o];
-    const float* mi = m + (size_t)i * R;
-    float nxt[RPT];
-    bool ok = true;
+  bool done = false;
+  constexpr int PR_PF = 32 / RPT > 4 ? 32 / RPT : 4;
+  for (int o0 = 0; o0 < k && !done; o0 += PR_PF) {
+    float mv[PR_PF][RPT];
 #pragma unroll
-    for (int j = 0; j < RPT; ++j) {
-      const int a = tid + j * SEL_T;
-      nxt[j] = a < R ? cur[j] + mi[a] : 0.f;
-      ok = ok && (a >= R || nxt[j] <= eps);
+    for (int q = 0; q < PR_PF; ++q) {
+      const float* mi = m + (size_t)key_i[min(o0 + q, k - 1)] * R;
+#pragma unroll
+      for (int j = 0; j < RPT; ++j) mv[q][j] = mi[min(tid + j * SEL_T, R - 1)];
     }
-    if (__syncthreads_and(ok)) {
 #pragma unroll
-      for (int j = 0; j < RPT; ++j) cur[j] = nxt[j];
-      tokens += key_n[o];
-      count += 1;
-      if (tid == 0) removed[i] = 1;
+    for (int q = 0; q < PR_PF; ++q) {
+      const int o = o0 + q;
+      if (o >= k || tokens >= target || count + 1 > k - m0) {
+        done = true;
+        break;
+      }
+      float nxt[RPT];
+      bool ok = true;
+#pragma unroll
+      for (int j = 0; j < RPT; ++j) {
+        nxt[j] = cur[j] + mv[q][j];
+        ok = ok && (tid + j * SEL_T >= R || nxt[j] <= eps);
+      }
+      if (__syncthreads_and(ok)) {
+#pragma unroll
+        for (int j = 0; j < RPT; ++j) cur[j] = nxt[j];
+        tokens += key_n[o];
+        count += 1;
+        if (tid == 0) removed[key_i[o]] = 1;
+      }
     }
   }
   if (tid == 0) *removed_tokens = tokens;
@@ -1336,22 +1454,15 @@ PruneLayout prune_layout(const DecodeDims& p, int k) {
   o.retain = take(retain_workspace_bytes(p));
   o.cid = take((size_t)p.L * sizeof(int32_t));
   o.bounds = take((size_t)2 * k * sizeof(int32_t));
+  o.segb = take((size_t)(k + 1) * sizeof(int32_t));
   o.stats = take((size_t)2 * k * sizeof(float));
   o.mtab = take((size_t)k * p.Hq * p.W * sizeof(float));
+  // disjoint ascending chunks touch at most k + spans - 1 (span, chunk) pairs
+  const size_t nseg = (size_t)k + (p.L + RT_CK - 1) / RT_CK;
+  o.seg_v = take(nseg * p.Hq * p.W * sizeof(float));
+  o.seg_m = take(nseg * p.Hq * p.W * sizeof(float));
   o.total = off;
   return o;
-}
-
-template <int D, int RT>
-static hipError_t prune_mass(const DecodeDims& p, const RetainLayout& lay, char* ws,
-                             const void* q_obs, const void* k, const int32_t* cid, float* m,
-                             hipStream_t st) {
-  dim3 grid(lay.nch, p.Hkv, (p.r + 3) / 4);
-  chunk_mass_kernel<D, RT><<<grid, 256, 0, st>>>(
-      static_cast<const bf16*>(q_obs), static_cast<const bf16*>(k), cid, p.Hq, p.Hkv, p.r, p.L,
-      p.W, p.sm_scale * kLog2e, reinterpret_cast<const float*>(ws + lay.row_m),
-      reinterpret_cast<const float*>(ws + lay.row_inv), p.Hq * p.W, m);
-  return hipGetLastError();
 }
 
 hipError_t launch_chunk_prune(const DecodeDims& p, const PruneArgs& a, const void* q_obs,
@@ -1372,9 +1483,16 @@ hipError_t launch_chunk_prune(const DecodeDims& p, const PruneArgs& a, const voi
   if (e != hipSuccess) return e;
   chunk_of_kernel<<<(p.L + 255) / 256, 256, 0, st>>>(bounds, a.k, p.L, cid);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // pooled measure: the retention passes with Renyi-2 head entropies
+  int32_t* segb = reinterpret_cast<int32_t*>(w + ly.segb);
+  seg_base_kernel<<<1, SEL_T, 0, st>>>(bounds, a.k, segb);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  // the retention passes with Renyi-2 head entropies; pass 1 also writes the
+  // chunk segments of the row masses
+  const SegArgs sg{cid, bounds, segb, reinterpret_cast<float*>(w + ly.seg_v),
+                   reinterpret_cast<float*>(w + ly.seg_m)};
   const int RT = (p.W + 31) / 32;
-#define EGS_RP(DD, RR) e = retain_passes<DD, RR>(p, lay, rws, q_obs, k, EGS_RENYI, 2.0f, st)
+#define EGS_RP(DD, RR) \
+  e = retain_passes<DD, RR>(p, lay, rws, q_obs, k, EGS_RENYI, 2.0f, st, &sg)
   if (p.D == 128) {
     if (RT == 1) EGS_RP(128, 1);
     else if (RT == 2) EGS_RP(128, 2);
@@ -1388,38 +1506,29 @@ hipError_t launch_chunk_prune(const DecodeDims& p, const PruneArgs& a, const voi
   }
 #undef EGS_RP
   if (e != hipSuccess) return e;
+  chunk_norm_kernel<<<a.k, 256, 0, st>>>(segb, sg.seg_v, sg.seg_m,
+                                         reinterpret_cast<const float*>(rws + lay.row_m),
+                                         reinterpret_cast<const float*>(rws + lay.row_inv), R, m);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
   head_weight_kernel<<<p.Hkv, 64, 0, st>>>(reinterpret_cast<const float*>(rws + lay.ent), p.Hq,
                                            p.Hkv, p.r, lay.nch, EGS_RENYI, 2.0f, a.zeta, a.tau,
                                            reinterpret_cast<float*>(rws + lay.weight), nullptr);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  float* mu = reinterpret_cast<float*>(rws + lay.mu);
-  retain_mu_kernel<<<dim3((p.L + 255) / 256, p.Hkv), 256, 0, st>>>(
+  float* pooled = reinterpret_cast<float*>(rws + lay.mu);
+  pooled_mu_kernel<<<(p.L + 255) / 256, 256, 0, st>>>(
       reinterpret_cast<const float*>(rws + lay.mass),
-      reinterpret_cast<const float*>(rws + lay.weight), nullptr, nullptr, 1.0f, p.Hq, p.Hkv, p.r,
-      p.L, mu, nullptr);
+      reinterpret_cast<const float*>(rws + lay.weight), p.Hq, p.Hkv, p.r, p.L, pooled);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  // row-chunk masses
-  const int nm = a.k * R;
-  fill_zero_kernel<<<(nm + 255) / 256, 256, 0, st>>>(m, nm);
+  chunk_stats_kernel<<<a.k, 256, 0, st>>>(pooled, bounds, stats);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-#define EGS_PM(DD, RR) e = prune_mass<DD, RR>(p, lay, rws, q_obs, k, cid, m, st)
-  if (p.D == 128) {
-    if (RT == 1) EGS_PM(128, 1);
-    else if (RT == 2) EGS_PM(128, 2);
-    else if (RT == 3) EGS_PM(128, 3);
-    else EGS_PM(128, 4);
-  } else {
-    if (RT == 1) EGS_PM(64, 1);
-    else if (RT == 2) EGS_PM(64, 2);
-    else if (RT == 3) EGS_PM(64, 3);
-    else EGS_PM(64, 4);
-  }
-#undef EGS_PM
-  if (e != hipSuccess) return e;
-  chunk_stats_kernel<<<a.k, 256, 0, st>>>(mu, p.Hkv, p.L, bounds, stats);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  prune_select_kernel<<<1, SEL_T, 0, st>>>(stats, bounds, a.k, R, m, a.eps_s, a.lam, a.eps, a.m0,
-                                           a.target, prio, removed, removed_tokens);
+#define EGS_PS(RPT)                                                                              \
+  prune_select_kernel<RPT><<<1, SEL_T, 0, st>>>(stats, bounds, a.k, R, m, a.eps_s, a.lam, a.eps, \
+                                                a.m0, a.target, prio, removed, removed_tokens)
+  if (R <= SEL_T) EGS_PS(1);
+  else if (R <= 2 * SEL_T) EGS_PS(2);
+  else if (R <= 4 * SEL_T) EGS_PS(4);
+  else EGS_PS(8);
+#undef EGS_PS
   return hipGetLastError();
 }
 
