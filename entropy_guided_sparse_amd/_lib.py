@@ -18,7 +18,7 @@ EGS_SHANNON, EGS_RENYI = 0, 1
 EGS_POOL_MEAN_PROBE, EGS_POOL_MAXMIN = 0, 1
 EGS_BUDGET_FIXED, EGS_BUDGET_TWO_LEVEL, EGS_BUDGET_PROPORTIONAL, EGS_BUDGET_ALG3 = range(4)
 EGS_PAGE_GROUP, EGS_PAGE_LAYER_UNION, EGS_PAGE_HEAD_UNION = 0, 1, 2
-ABI_VERSION = 3
+ABI_VERSION = 4
 
 
 class PrefillShapeC(ctypes.Structure):
@@ -89,6 +89,10 @@ SIGNATURES = {
     "egs_chunk_prune_workspace": (ctypes.c_size_t, [_DS, ctypes.c_int32]),
     "egs_chunk_prune": (_ST, [_DS, ctypes.POINTER(PruneParamsC), _P, _P, _P, ctypes.c_int32, _P,
                               _P, _P, _P, _P, ctypes.c_size_t, _P]),
+    "egs_prune_certificate_workspace": (ctypes.c_size_t, [ctypes.c_int32]),
+    "egs_prune_certificate": (_ST, [_P, ctypes.c_int32, ctypes.c_int32, _P, _P, ctypes.c_double,
+                                    ctypes.c_int32, ctypes.c_double, _P, _P, ctypes.c_size_t,
+                                    _P]),
     "egs_latent_decode_workspace": (ctypes.c_size_t, [_DS]),
     "egs_latent_decode_step": (_ST, [_DS, ctypes.POINTER(RetainParamsC),
                                      ctypes.POINTER(LatentStateC), _P, _P, _P, _P, _P, _P, _P,

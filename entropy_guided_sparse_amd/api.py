@@ -303,6 +303,29 @@ def chunk_prune(shape: DecodeShape, q_obs, k, chunk_bounds, eps_s: float, lam: f
     return removed, tokens, prio, row_mass
 
 
+def prune_certificate(chunk_bounds, row_mass, row_price, eps: float, m0: int, t: float,
+                      workspace: Optional[torch.Tensor] = None):
+    """U(y, t) of a removal as a float64 device tensor [1]; row_mass [k, R]
+    and row_price [R] are float32 device tensors, chunk_bounds a host array
+    [k, 2] of int32."""
+    import numpy as np
+    b = np.ascontiguousarray(np.asarray(chunk_bounds, dtype=np.int32).reshape(-1, 2))
+    nk = b.shape[0]
+    dev = row_mass.device
+    if row_mass.dtype != torch.float32 or not row_mass.is_contiguous() or row_mass.dim() != 2 \
+            or row_mass.shape[0] != nk:
+        raise ValueError(f"row_mass must be contiguous float32 [{nk}, R]")
+    R = row_mass.shape[1]
+    _need(row_price, "row_price", (R,), torch.float32, dev)
+    out = _empty((1,), torch.float64, dev)
+    if workspace is None:
+        workspace = _workspace(L.LIB.egs_prune_certificate_workspace(nk), dev)
+    L.check(L.LIB.egs_prune_certificate(b.ctypes.data_as(ctypes.c_void_p), nk, R,
+                                        _ptr(row_mass), _ptr(row_price), eps, m0, t, _ptr(out),
+                                        _ptr(workspace), workspace.numel(), _stream(dev)))
+    return out
+
+
 def latent_decode_step(shape: DecodeShape, params: RetainParams, state, q_new, k_new, v_new,
                        q_window, k_cache, v_cache, out: Optional[torch.Tensor] = None,
                        keep_idx: Optional[torch.Tensor] = None,

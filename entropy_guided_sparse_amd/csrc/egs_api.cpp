@@ -467,6 +467,42 @@ egs_status egs_chunk_prune(const egs_decode_shape* shape, const egs_prune_params
                     "chunk_prune launch");
 }
 
+size_t egs_prune_certificate_workspace(int32_t n_chunks) {
+  if (n_chunks < 1 || n_chunks > egs::kMaxPruneChunks) return 0;
+  return egs::certificate_workspace_bytes(n_chunks);
+}
+
+egs_status egs_prune_certificate(const int32_t* chunk_bounds, int32_t n_chunks, int32_t n_rows,
+                                 const float* row_mass, const float* row_price, double eps,
+                                 int32_t m0, double t, double* certificate, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream) {
+  if (n_chunks < 1 || n_chunks > egs::kMaxPruneChunks)
+    return fail(EGS_EINVAL, "n_chunks must be in [1, %d]", egs::kMaxPruneChunks);
+  if (n_rows < 1 || n_rows > egs::kMaxPruneRows)
+    return fail(EGS_EINVAL, "n_rows must be in [1, %d]", egs::kMaxPruneRows);
+  if (!(std::isfinite(eps) && eps >= 0.0)) return fail(EGS_EINVAL, "eps must be >= 0");
+  if (!(std::isfinite(t) && t >= 0.0)) return fail(EGS_EINVAL, "t must be >= 0");
+  if (m0 < 0) return fail(EGS_EINVAL, "m0 must be >= 0");
+  if (chunk_bounds == nullptr) return fail(EGS_EINVAL, "chunk_bounds is NULL");
+  for (int i = 0; i < n_chunks; ++i)
+    if (chunk_bounds[2 * i + 1] <= chunk_bounds[2 * i])
+      return fail(EGS_EINVAL, "chunk %d = [%d, %d) is empty", i, chunk_bounds[2 * i],
+                  chunk_bounds[2 * i + 1]);
+  egs_status st;
+  if ((st = need(row_mass, "row_mass", 4)) != EGS_OK) return st;
+  if ((st = need(row_price, "row_price", 4)) != EGS_OK) return st;
+  if ((st = need(certificate, "certificate", 8)) != EGS_OK) return st;
+  if ((st = need(workspace, "workspace", kWsAlign)) != EGS_OK) return st;
+  const size_t wsb = egs::certificate_workspace_bytes(n_chunks);
+  if (workspace_bytes < wsb)
+    return fail(EGS_EWORKSPACE, "workspace of %zu bytes is below the %zu required",
+                workspace_bytes, wsb);
+  return hip_status(egs::launch_prune_certificate(chunk_bounds, n_chunks, n_rows, row_mass,
+                                                  row_price, eps, m0, t, certificate, workspace,
+                                                  stream),
+                    "prune_certificate launch");
+}
+
 size_t egs_latent_decode_workspace(const egs_decode_shape* shape) {
   DecodeDims p;
   if (check_decode(shape, &p) != EGS_OK) return 0;

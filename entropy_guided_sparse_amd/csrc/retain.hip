@@ -1532,6 +1532,82 @@ hipError_t launch_chunk_prune(const DecodeDims& p, const PruneArgs& a, const voi
   return hipGetLastError();
 }
 
+// Optimality-gap certificate of a removal (EntroPrefill Sec. 4.2):
+// U = eps sum_a y_a + t (k - m0) + sum_i [n_i - sum_a y_a m[i][a] - t]_+,
+// in float64 over the float32 masses and prices.  Per chunk, one workgroup
+// forms the priced mass and its hinge; one workgroup then adds the terms in
+// index order (no atomics: the result does not depend on timing).
+__device__ __forceinline__ double block_sum_d(double v, double* red) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o);
+  const int w = threadIdx.x >> 6, nw = blockDim.x >> 6;
+  __syncthreads();   // red may still be read by a previous call
+  if ((threadIdx.x & 63) == 0) red[w] = v;
+  __syncthreads();
+  double tot = 0.0;
+  for (int j = 0; j < nw; ++j) tot += red[j];
+  return tot;
+}
+
+__global__ __launch_bounds__(256) void cert_chunk_kernel(const int32_t* __restrict__ bounds,
+                                                         const float* __restrict__ m,
+                                                         const float* __restrict__ y, int R,
+                                                         double t, double* __restrict__ hinge) {
+  __shared__ double red[4];
+  const int i = blockIdx.x;
+  const float* mi = m + (size_t)i * R;
+  double acc = 0.0;
+  for (int a0 = 0; a0 < R; a0 += 4 * 256) {
+    float mv[4], yv[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int a = min(a0 + j * 256 + (int)threadIdx.x, R - 1);
+      mv[j] = mi[a];
+      yv[j] = y[a];
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j)
+      if (a0 + j * 256 + (int)threadIdx.x < R) acc += (double)yv[j] * (double)mv[j];
+  }
+  const double priced = block_sum_d(acc, red);
+  if (threadIdx.x == 0) {
+    const double n = (double)(bounds[2 * i + 1] - bounds[2 * i]);
+    hinge[i] = fmax(n - priced - t, 0.0);
+  }
+}
+
+__global__ __launch_bounds__(SEL_T) void cert_total_kernel(const double* __restrict__ hinge,
+                                                           int k, const float* __restrict__ y,
+                                                           int R, double eps, int m0, double t,
+                                                           double* __restrict__ out) {
+  __shared__ double red[SEL_T / 64];
+  double ys = 0.0, hs = 0.0;
+  for (int a = threadIdx.x; a < R; a += SEL_T) ys += (double)y[a];
+  for (int i = threadIdx.x; i < k; i += SEL_T) hs += hinge[i];
+  ys = block_sum_d(ys, red);
+  hs = block_sum_d(hs, red);
+  if (threadIdx.x == 0) *out = eps * ys + t * (double)(k - m0) + hs;
+}
+
+size_t certificate_workspace_bytes(int k) {
+  return align_up((size_t)2 * k * sizeof(int32_t)) + align_up((size_t)k * sizeof(double));
+}
+
+hipError_t launch_prune_certificate(const int32_t* bounds_host, int k, int R, const float* m,
+                                    const float* y, double eps, int m0, double t, double* out,
+                                    void* workspace, hipStream_t st) {
+  char* w = static_cast<char*>(workspace);
+  int32_t* bounds = reinterpret_cast<int32_t*>(w);
+  double* hinge = reinterpret_cast<double*>(w + align_up((size_t)2 * k * sizeof(int32_t)));
+  hipError_t e = hipMemcpyAsync(bounds, bounds_host, (size_t)2 * k * sizeof(int32_t),
+                                hipMemcpyHostToDevice, st);
+  if (e != hipSuccess) return e;
+  cert_chunk_kernel<<<k, 256, 0, st>>>(bounds, m, y, R, t, hinge);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  cert_total_kernel<<<1, SEL_T, 0, st>>>(hinge, k, y, R, eps, m0, t, out);
+  return hipGetLastError();
+}
+
 // ---------------------------------------------------------------------------
 // Latent decoding (EntropyInfer Sec. 4.3, App. B): the cache grows by one
 // entry per generated token and is compressed once n_delay tokens have been

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define EGS_ABI_VERSION 3
+#define EGS_ABI_VERSION 4
 
 typedef enum {
   EGS_OK = 0,
@@ -323,6 +323,26 @@ egs_status egs_chunk_prune(const egs_decode_shape* shape, const egs_prune_params
                            int32_t n_chunks, int8_t* removed, int32_t* removed_tokens,
                            float* priority, float* row_mass, void* workspace,
                            size_t workspace_bytes, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Optimality-gap certificate of a chunk removal ([EP] Sec. 4.2):
+ *   U(y, t) = eps sum_a y_a + t (k - m0) + sum_i [n_i - sum_a y_a m[i][a] - t]_+
+ * For prices y_a >= 0 (one per observer row) and t >= 0, U bounds the tokens
+ * that any removal set keeping every row within eps and at most k - m0
+ * chunks can remove; U - removed_tokens bounds the greedy scan's shortfall.
+ * chunk_bounds: HOST int32 [n_chunks][2] (begin, end), only the lengths
+ * n_i = end - begin are used.  Device: row_mass [n_chunks][n_rows] float32
+ * (the egs_chunk_prune output), row_price [n_rows] float32, certificate [1]
+ * float64.  Computed in float64.  Valid: 1 <= n_chunks <= 4096,
+ * 1 <= n_rows <= 8192, every chunk non-empty, eps >= 0, t >= 0, m0 >= 0.
+ * The prices are not checked (device memory): with a negative price U is no
+ * bound.  workspace >= egs_prune_certificate_workspace(n_chunks) bytes.
+ * ------------------------------------------------------------------------- */
+size_t egs_prune_certificate_workspace(int32_t n_chunks);
+egs_status egs_prune_certificate(const int32_t* chunk_bounds, int32_t n_chunks, int32_t n_rows,
+                                 const float* row_mass, const float* row_price, double eps,
+                                 int32_t m0, double t, double* certificate, void* workspace,
+                                 size_t workspace_bytes, hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Latent decoding ([EI] Sec. 4.3 and App. B: compress the cache only after

@@ -728,15 +728,17 @@ def prune_greedy(S, n, m, eps: float, m0: int, target: int, dtype=np.float64):
     return removed, tokens
 
 
-def prune_certificate(n, m, eps: float, m0: int, y: float, t: float) -> float:
-    """U(y, t) = sum_a y eps + t (k - m0) + sum_i [n_i - sum_a y m[a, i] - t]_+
-    with one price y >= 0 for every row and t >= 0 ([EP] Sec. 4.2): an upper
-    bound on the most tokens any feasible removal set can remove."""
+def prune_certificate(n, m, eps: float, m0: int, y, t: float) -> float:
+    """U(y, t) = sum_a y_a eps + t (k - m0) + sum_i [n_i - sum_a y_a m[a, i] - t]_+
+    with prices y_a >= 0 (one per row; a scalar prices every row alike) and
+    t >= 0 ([EP] Sec. 4.2): an upper bound on the most tokens any feasible
+    removal set can remove."""
     n = np.asarray(n, dtype=np.float64)
     m = np.asarray(m, dtype=np.float64)
     R, k = m.shape
-    return (R * y * eps + t * (k - m0)
-            + float(np.maximum(n - y * m.sum(axis=0) - t, 0.0).sum()))
+    ya = np.broadcast_to(np.asarray(y, dtype=np.float64), (R,))
+    return (float(ya.sum()) * eps + t * (k - m0)
+            + float(np.maximum(n - ya @ m - t, 0.0).sum()))
 
 
 def chunk_prune(q_obs, k, chunks, n_sink: int, eps_s: float, lam: float, eps: float,

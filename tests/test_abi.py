@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.LIB.egs_abi_version() == 3
+    assert L.LIB.egs_abi_version() == 4
     for st in range(5):
         assert L.LIB.egs_status_string(st).decode().startswith("EGS_")
 
@@ -285,3 +285,27 @@ def test_chunk_prune_errors(L):
     assert call(shape=_dshape(L, batch=2, cache_len=4096, n_obs=64)) == L.EGS_EINVAL
     big = _dshape(L, batch=1, n_q_heads=128, n_kv_heads=8, cache_len=4096, n_obs=128)
     assert call(shape=big) == L.EGS_ENOTSUP                                  # 16384 rows
+
+
+def test_prune_certificate_errors(L):
+    import numpy as np
+    good = np.array([[10, 100], [100, 200]], dtype=np.int32)
+    ws = L.LIB.egs_prune_certificate_workspace(2)
+    assert ws > 0 and L.LIB.egs_prune_certificate_workspace(0) == 0
+
+    def call(bounds=good, nk=None, R=512, eps=0.1, m0=0, t=1.0, wsb=ws, mass=FAKE):
+        b = np.ascontiguousarray(bounds, dtype=np.int32)
+        return L.LIB.egs_prune_certificate(b.ctypes.data_as(ctypes.c_void_p),
+                                           len(b) if nk is None else nk, R, mass, FAKE, eps, m0,
+                                           t, FAKE, FAKE, wsb, None)
+
+    assert call(bounds=np.array([[10, 10]])) == L.EGS_EINVAL    # empty chunk
+    assert call(nk=0) == L.EGS_EINVAL
+    assert call(R=0) == L.EGS_EINVAL
+    assert call(R=8193) == L.EGS_EINVAL
+    assert call(eps=-0.5) == L.EGS_EINVAL
+    assert call(t=-1.0) == L.EGS_EINVAL
+    assert call(t=float("nan")) == L.EGS_EINVAL
+    assert call(m0=-1) == L.EGS_EINVAL
+    assert call(mass=None) == L.EGS_EINVAL
+    assert call(wsb=ws - 1) == L.EGS_EWORKSPACE

@@ -119,6 +119,24 @@ def test_certificate_weak_duality_by_brute_force():
         for _ in range(5):
             y, t = float(rng.uniform(0, 50)), float(rng.uniform(0, 10))
             assert O.prune_certificate(n, m, eps, m0, y, t) >= best - 1e-9
+            ya = rng.uniform(0, 50, R)                 # one price per row
+            assert O.prune_certificate(n, m, eps, m0, ya, t) >= best - 1e-9
+        # zero prices and t = 0 give the trivial bound N; a scalar price is
+        # the same as that price on every row
+        assert O.prune_certificate(n, m, eps, m0, 0.0, 0.0) == float(n.sum())
+        assert abs(O.prune_certificate(n, m, eps, m0, 3.5, 1.0)
+                   - O.prune_certificate(n, m, eps, m0, np.full(R, 3.5), 1.0)) < 1e-9
+
+
+def test_certificate_by_hand():
+    # two rows, three chunks: n = (4, 2, 5), eps = 0.5, m0 = 1, y = (1, 2), t = 1
+    m = np.array([[0.2, 0.1, 0.4],
+                  [0.3, 0.0, 0.1]])
+    n = np.array([4, 2, 5])
+    # sum_a y_a eps = 1.5; t (k - m0) = 2; priced masses (0.8, 0.1, 0.6);
+    # hinges [4 - 0.8 - 1]+ = 2.2, [2 - 0.1 - 1]+ = 0.9, [5 - 0.6 - 1]+ = 3.4
+    assert abs(O.prune_certificate(n, m, 0.5, 1, np.array([1.0, 2.0]), 1.0)
+               - (1.5 + 2.0 + 2.2 + 0.9 + 3.4)) < 1e-12
 
 
 def test_streaming_paths_agree_with_the_stacked_rows():

@@ -141,3 +141,35 @@ def test_chunk_prune_full_context(api):
     assert np.all(g_m[:, g_rem].astype(np.float64).sum(axis=1) <= eps + 1e-5)
     # chunks never hold more than a row's whole mass (protected tokens hold the rest)
     assert np.all(g_m.astype(np.float64).sum(axis=1) <= 1.0 + 1e-4)
+
+
+def test_prune_certificate(api):
+    """U(y, t) on the GPU's row masses: float64 on both sides over the same
+    float32 inputs (only the order of the sums differs), weak duality against
+    the greedy removal, and the trivial and scalar-price cases."""
+    cfg = synth.DecodeConfig("cert", 1, 8, 2, 128, 4096, 64, 4, 16, 16)
+    inp = synth.make_decode(cfg, seed=2)
+    chunks = synth.prune_chunks(4096, 64, 40, seed=2)
+    shape = api.DecodeShape(1, 8, 2, 128, 4096, 64, 4, 16, 16)
+    q = dev_tensor(inp.q_obs_store[0], "bf16")
+    k = dev_tensor(inp.k_store[0], "bf16")
+    eps, m0 = 0.05, 3
+    removed, tokens, _, mass = api.chunk_prune(shape, q, k, chunks, 0.1, 0.5, eps, m0, 4096,
+                                               want_row_mass=True)
+    torch.cuda.synchronize()
+    g_m = mass.cpu().numpy().T.astype(np.float64)     # [R, k]
+    n = chunks[:, 1] - chunks[:, 0]
+    got_tokens = int(tokens.cpu().item())
+    rng = np.random.default_rng(8)
+    R = g_m.shape[0]
+    cases = [(np.zeros(R), 0.0), (np.full(R, 40.0), 2.0)] + \
+            [(rng.uniform(0, 200, R), float(rng.uniform(0, 50))) for _ in range(4)]
+    for y, t in cases:
+        yd = torch.from_numpy(y.astype(np.float32)).cuda()
+        U = float(api.prune_certificate(chunks, mass, yd, eps, m0, t).cpu().item())
+        want = O.prune_certificate(n, g_m, eps, m0, y.astype(np.float32).astype(np.float64), t)
+        log(f"[cert] t={t:.2f} U={U:.6f} oracle={want:.6f} greedy tokens={got_tokens}")
+        assert abs(U - want) <= 1e-9 * max(1.0, abs(want))
+        assert U >= got_tokens - 1e-6
+    assert float(api.prune_certificate(chunks, mass, torch.zeros(R, device="cuda"), eps, m0,
+                                       0.0).cpu().item()) == float(n.sum())
