@@ -1233,21 +1233,21 @@ __global__ __launch_bounds__(SEL_T) void seg_base_kernel(const int32_t* __restri
 }
 
 // m[c][a] = sum over the segments of chunk c of seg_v exp2(seg_m - M_a) / L_a,
-// with the row's final reference M_a and sum L_a (row_m, row_inv);
-// workgroup per chunk, thread per row a = h * W + u
+// with the row's final reference M_a and sum L_a (row_m, row_inv); workgroup
+// per (chunk, 256 rows), thread per row a = h * W + u
 __global__ __launch_bounds__(256) void chunk_norm_kernel(
     const int32_t* __restrict__ seg_base, const float* __restrict__ seg_v,
     const float* __restrict__ seg_m, const float* __restrict__ row_m,
     const float* __restrict__ row_inv, int R, float* __restrict__ m) {
   const int c = blockIdx.x;
+  const int a = blockIdx.y * 256 + threadIdx.x;
+  if (a >= R) return;
   const int s0 = seg_base[c], s1 = seg_base[c + 1];
-  for (int a = threadIdx.x; a < R; a += 256) {
-    const float M = row_m[a], inv = row_inv[a];
-    float acc = 0.f;
-    for (int sg = s0; sg < s1; ++sg)
-      acc += seg_v[(size_t)sg * R + a] * fast_exp2(seg_m[(size_t)sg * R + a] - M);
-    m[(size_t)c * R + a] = acc * inv;
-  }
+  const float M = row_m[a], inv = row_inv[a];
+  float acc = 0.f;
+  for (int sg = s0; sg < s1; ++sg)
+    acc += seg_v[(size_t)sg * R + a] * fast_exp2(seg_m[(size_t)sg * R + a] - M);
+  m[(size_t)c * R + a] = acc * inv;
 }
 
 // pooled measure mu^l_t = (1/G) sum_g sum_{h in g} w_h a^h_t of one sequence
@@ -1312,10 +1312,34 @@ __global__ __launch_bounds__(256) void chunk_stats_kernel(const float* __restric
   }
 }
 
+// Block-wide AND of 32-bit masks (one bit per scan step).  Two LDS slots are
+// used in turn, so one barrier per call suffices: a slot is written again only
+// after every thread has passed the barrier of the call in between.
+__device__ __forceinline__ uint32_t block_and_mask(uint32_t v, uint32_t (*red)[SEL_T / 64],
+                                                   int& slot) {
+#pragma unroll
+  for (int o = 32; o > 0; o >>= 1) v &= (uint32_t)__shfl_xor((int)v, o);
+  if ((threadIdx.x & 63) == 0) red[slot][threadIdx.x >> 6] = v;
+  __syncthreads();
+  uint32_t r = ~0u;
+#pragma unroll
+  for (int w = 0; w < SEL_T / 64; ++w) r &= red[slot][w];
+  slot ^= 1;
+  return r;
+}
+
 // priorities, their order and the greedy scan; one workgroup of 1024 threads,
-// thread tid keeping the running sums of rows tid + j * 1024, j < RPT.  The
-// scan is sequential over the sorted chunks; their mass columns are fetched
-// PR_PF chunks at a time so that one memory latency covers PR_PF steps.
+// thread tid keeping the running sums of rows tid + j * 1024, j < RPT.
+// Order: up to 512 chunks by rank (each thread counts the chunks that come
+// before its own; the order (S, -n, index) is total), more by bitonic sort.
+// Scan: the masses are >= 0, so the running sums only grow and a chunk that
+// does not fit on its own never fits later.  The mass columns of PF sorted
+// chunks are fetched at once; a round votes (1) which of them fit on their
+// own and (2) which fit when every earlier one that fits on its own is also
+// removed; the steps are then taken in order, and a round ends early only at
+// a chunk that fits alone but not after the earlier ones (its rejection
+// changes what the later ones see).  Two barriers per round instead of one per
+// chunk.
 template <int RPT>
 __global__ __launch_bounds__(SEL_T) void prune_select_kernel(
     const float* __restrict__ stats, const int32_t* __restrict__ bounds, int k, int R,
@@ -1324,8 +1348,10 @@ __global__ __launch_bounds__(SEL_T) void prune_select_kernel(
   __shared__ float key_s[PR_MAX_CHUNKS];
   __shared__ int key_n[PR_MAX_CHUNKS];
   __shared__ int key_i[PR_MAX_CHUNKS];
+  __shared__ int order[PR_MAX_CHUNKS];
   __shared__ float red[SEL_T / 64];
   __shared__ int ired[SEL_T / 64];
+  __shared__ uint32_t vote[2][SEL_T / 64];
   const int tid = threadIdx.x;
   // totals: Z = sum of the chunks' pooled mass, N = candidate tokens
   float z = 0.f;
@@ -1348,9 +1374,11 @@ __global__ __launch_bounds__(SEL_T) void prune_select_kernel(
   }
   __syncthreads();
   const float Z = shZ, N = (float)shN;
+  const bool by_rank = k <= 512;
   int P = 1;
   while (P < k) P <<= 1;
-  for (int i = tid; i < P; i += SEL_T) {
+  const int nkeys = by_rank ? k : P;
+  for (int i = tid; i < nkeys; i += SEL_T) {
     if (i < k) {
       const int n = bounds[2 * i + 1] - bounds[2 * i];
       const float M = stats[2 * i] / Z, sq = stats[2 * i + 1] / (Z * Z);
@@ -1362,7 +1390,9 @@ __global__ __launch_bounds__(SEL_T) void prune_select_kernel(
       const float kap = n >= 2 ? logf(ph2) / logf((float)n) : 0.f;
       const float S = logf(ell) + lam * kap;
       prio[i] = S;
-      key_s[i] = S;
+      // a NaN priority (all candidate mass underflowed) sorts last: the sort
+      // keys must form a total order, or ranks would repeat
+      key_s[i] = S == S ? S : INFINITY;
       key_n[i] = n;
       key_i[i] = i;
       removed[i] = 0;
@@ -1373,71 +1403,121 @@ __global__ __launch_bounds__(SEL_T) void prune_select_kernel(
     }
   }
   __syncthreads();
-  // bitonic sort by (S ascending, n descending, index ascending)
+  // (S ascending, n descending, index ascending)
   auto before = [&](int a, int b) {
     if (key_s[a] != key_s[b]) return key_s[a] < key_s[b];
     if (key_n[a] != key_n[b]) return key_n[a] > key_n[b];
     return key_i[a] < key_i[b];
   };
-  for (int size = 2; size <= P; size <<= 1) {
-    for (int stride = size >> 1; stride > 0; stride >>= 1) {
-      for (int x = tid; x < P; x += SEL_T) {
-        const int y = x ^ stride;
-        if (y > x) {
-          const bool up = (x & size) == 0;
-          if (before(y, x) == up) {
-            const float ts = key_s[x];
-            key_s[x] = key_s[y];
-            key_s[y] = ts;
-            const int tn = key_n[x];
-            key_n[x] = key_n[y];
-            key_n[y] = tn;
-            const int ti = key_i[x];
-            key_i[x] = key_i[y];
-            key_i[y] = ti;
+  if (by_rank) {
+    for (int i = tid; i < k; i += SEL_T) {
+      const float si = key_s[i];
+      const int ni = key_n[i];
+      int rank = 0;
+      for (int j = 0; j < k; ++j) {
+        const float sj = key_s[j];
+        const int nj = key_n[j];
+        rank += (sj < si || (sj == si && (nj > ni || (nj == ni && j < i)))) ? 1 : 0;
+      }
+      order[rank] = i;
+    }
+  } else {
+    for (int size = 2; size <= P; size <<= 1) {
+      for (int stride = size >> 1; stride > 0; stride >>= 1) {
+        for (int x = tid; x < P; x += SEL_T) {
+          const int y = x ^ stride;
+          if (y > x) {
+            const bool up = (x & size) == 0;
+            if (before(y, x) == up) {
+              const float ts = key_s[x];
+              key_s[x] = key_s[y];
+              key_s[y] = ts;
+              const int tn = key_n[x];
+              key_n[x] = key_n[y];
+              key_n[y] = tn;
+              const int ti = key_i[x];
+              key_i[x] = key_i[y];
+              key_i[y] = ti;
+            }
           }
         }
+        __syncthreads();
       }
-      __syncthreads();
     }
+    for (int x = tid; x < k; x += SEL_T) order[x] = key_i[x];
   }
-  // greedy scan (the stop test only depends on uniform values, so every
-  // thread leaves at the same step)
+  __syncthreads();
+  // key_n is indexed by chunk in the rank order and by position after the
+  // bitonic sort
+  auto n_of = [&](int o) { return by_rank ? key_n[order[o]] : key_n[o]; };
+
   float cur[RPT];
 #pragma unroll
   for (int j = 0; j < RPT; ++j) cur[j] = 0.f;
-  int tokens = 0, count = 0;
+  int tokens = 0, count = 0, slot = 0;
   bool done = false;
-  constexpr int PR_PF = 32 / RPT > 4 ? 32 / RPT : 4;
-  for (int o0 = 0; o0 < k && !done; o0 += PR_PF) {
-    float mv[PR_PF][RPT];
+  constexpr int PF = 32 / RPT > 4 ? 32 / RPT : 4;
+  for (int o0 = 0; o0 < k && !done; o0 += PF) {
+    float mv[PF][RPT];
 #pragma unroll
-    for (int q = 0; q < PR_PF; ++q) {
-      const float* mi = m + (size_t)key_i[min(o0 + q, k - 1)] * R;
+    for (int q = 0; q < PF; ++q) {
+      const float* mi = m + (size_t)order[min(o0 + q, k - 1)] * R;
 #pragma unroll
       for (int j = 0; j < RPT; ++j) mv[q][j] = mi[min(tid + j * SEL_T, R - 1)];
     }
+    int q0 = 0;
+    while (q0 < PF && !done) {
+      // (1) fits on its own
+      uint32_t alone = 0u;
 #pragma unroll
-    for (int q = 0; q < PR_PF; ++q) {
-      const int o = o0 + q;
-      if (o >= k || tokens >= target || count + 1 > k - m0) {
-        done = true;
-        break;
-      }
-      float nxt[RPT];
-      bool ok = true;
+      for (int q = 0; q < PF; ++q) {
+        bool ok = true;
 #pragma unroll
-      for (int j = 0; j < RPT; ++j) {
-        nxt[j] = cur[j] + mv[q][j];
-        ok = ok && (tid + j * SEL_T >= R || nxt[j] <= eps);
+        for (int j = 0; j < RPT; ++j)
+          ok = ok && (tid + j * SEL_T >= R || cur[j] + mv[q][j] <= eps);
+        alone |= (ok ? 1u : 0u) << q;
       }
-      if (__syncthreads_and(ok)) {
+      alone = block_and_mask(alone, vote, slot);
+      // (2) fits after every earlier chunk of the round that fits alone
+      float acc[RPT];
 #pragma unroll
-        for (int j = 0; j < RPT; ++j) cur[j] = nxt[j];
-        tokens += key_n[o];
-        count += 1;
-        if (tid == 0) removed[key_i[o]] = 1;
+      for (int j = 0; j < RPT; ++j) acc[j] = cur[j];
+      uint32_t after = 0u;
+#pragma unroll
+      for (int q = 0; q < PF; ++q) {
+        if (q >= q0 && ((alone >> q) & 1u)) {
+          bool ok = true;
+#pragma unroll
+          for (int j = 0; j < RPT; ++j) {
+            acc[j] += mv[q][j];
+            ok = ok && (tid + j * SEL_T >= R || acc[j] <= eps);
+          }
+          after |= (ok ? 1u : 0u) << q;
+        }
       }
+      after = block_and_mask(after, vote, slot);
+      // take the steps in order
+      int qn = PF;
+#pragma unroll
+      for (int q = 0; q < PF; ++q) {
+        if (q < q0 || qn < PF || done) continue;
+        const int o = o0 + q;
+        if (o >= k || tokens >= target || count + 1 > k - m0) {
+          done = true;
+          continue;
+        }
+        if (!((alone >> q) & 1u)) continue;   // never fits
+        if ((after >> q) & 1u) {
+#pragma unroll
+          for (int j = 0; j < RPT; ++j) cur[j] += mv[q][j];
+          tokens += n_of(o);
+          count += 1;
+          if (tid == 0) removed[order[o]] = 1;
+        } else {
+          qn = q + 1;   // rejected; the later ones need a new vote
+        }
+      }
+      q0 = qn;
     }
   }
   if (tid == 0) *removed_tokens = tokens;
@@ -1506,7 +1586,7 @@ hipError_t launch_chunk_prune(const DecodeDims& p, const PruneArgs& a, const voi
   }
 #undef EGS_RP
   if (e != hipSuccess) return e;
-  chunk_norm_kernel<<<a.k, 256, 0, st>>>(segb, sg.seg_v, sg.seg_m,
+  chunk_norm_kernel<<<dim3(a.k, (R + 255) / 256), 256, 0, st>>>(segb, sg.seg_v, sg.seg_m,
                                          reinterpret_cast<const float*>(rws + lay.row_m),
                                          reinterpret_cast<const float*>(rws + lay.row_inv), R, m);
   if ((e = hipGetLastError()) != hipSuccess) return e;

@@ -92,6 +92,15 @@ def test_chunk_prune(api, case):
         assert not rem.any() and tok == 0
 
 
+@pytest.mark.parametrize("k,eps", [(300, 0.02), (300, 0.3), (700, 0.05)])
+def test_chunk_prune_many_chunks(api, k, eps):
+    # 300 chunks: rank order, ten fetched batches of the scan; 700: bitonic sort
+    rng = np.random.default_rng(k)
+    T, W = 8192, 64
+    chunks = _chunks(rng, T, W, k, lo=8)
+    _run(api, 8, 2, T, W, chunks, 0.1, 0.5, eps, 5, T // 3, seed=k)
+
+
 def test_chunk_prune_single_and_unit_chunks(api):
     _run(api, 4, 2, 1024, 32, [(100, 101)], 0.2, 0.3, 1.0, 0, 10)
     _run(api, 4, 2, 1024, 32, [(5, 6), (6, 9), (9, 300), (400, 401), (500, 990)], 0.2, 0.3,
