@@ -13,15 +13,15 @@
 // always kept; compaction preserves token order (EntroPrefill Sec. 8.1).
 //
 // gfx950 design:
-//  * Both passes run obs_pass_kernel: one workgroup per (1024-key chunk,
+//  * Both passes run obs_pass_kernel: one workgroup per (1024-key span,
 //    batch x KV group, 4-head group).  64-key K stages are copied straight
 //    into LDS, four deep, and shared by the four wavefronts (one query head
 //    each); the logits of a stage take v_mfma_f32_32x32x16_bf16.
-//    Pass 1 (keys as M: a lane owns an observer row) keeps the chunk's
-//    running max / sum of every row; a combine kernel folds the chunks into
+//    Pass 1 (keys as M: a lane owns an observer row) keeps the span's
+//    running max / sum of every row; a combine kernel folds the spans into
 //    each row's final max and 1/sum.  Pass 2 recomputes the logits with keys
 //    as N, so a lane owns one key and the window mean is a register sum; it
-//    writes the per-head mass and the chunk's sink-isolated entropy partial
+//    writes the per-head mass and the span's sink-isolated entropy partial
 //    sums.
 //  * head_weight turns the partial sums into H_h and w_h; retain_mu forms
 //    mu_t; retain_select runs an exact 12/12/8-bit radix select over the
@@ -30,10 +30,17 @@
 //  * Page-level retention (EntroPrefill Sec. 7) keeps whole pages: page maxima
 //    of the token scores, the same select over page scores, and unions over
 //    the heads of a group or the groups of a layer through an LDS bitmap.
-//  * Decode attention splits the kept range into 256-entry chunks; the GQA
+//  * Decode attention splits the kept range into 256-entry splits; the GQA
 //    group's heads share each 64-entry K / V stage in LDS (lane-per-entry dot
-//    products, lane-per-dim PV) and a combine kernel merges the chunks with
+//    products, lane-per-dim PV) and a combine kernel merges the splits with
 //    their log-sum-exp.
+//  * Chunk pruning (EntroPrefill Sec. 3.1-3.2, 4.2) runs both passes on one
+//    prompt; pass 1 also splits each row's sums by candidate chunk (a
+//    "chunk" below is always one of the prompt's candidate documents, a
+//    "span" the passes' 1024-key work unit).  The pooled measure is formed
+//    per position, one workgroup orders the chunks by priority and scans
+//    them greedily with block votes, and two small kernels evaluate the
+//    Sec. 4.2 optimality-gap certificate for caller prices.
 #include <algorithm>
 #include <type_traits>
 
@@ -42,14 +49,14 @@
 
 namespace egs {
 
-constexpr int RT_CK = 1024;   // keys per chunk (pass 1 / pass 2 work unit)
+constexpr int RT_CK = 1024;   // keys per span (the pass 1 / pass 2 work unit)
 constexpr int RT_KT = 64;     // keys per LDS stage
 constexpr int SEL_T = 1024;   // threads of the select kernel
 constexpr int DA_SPL = 256;   // kept entries per decode-attention split
 
 struct RetainLayout {
   size_t stat_m, stat_l, row_m, row_inv, mass, ent, weight, mu, qsum, tstats, total;
-  int nch;
+  int nch;   // 1024-key spans of the cache
 };
 
 static size_t align_up(size_t x) {
@@ -88,7 +95,7 @@ size_t retain_workspace_bytes(const DecodeDims& p) {
 // shared pieces of pass 1 / pass 2
 // ---------------------------------------------------------------------------
 // 64-key K stages copied straight into LDS (global_load_lds_dwordx4) by the
-// four wavefronts, 16-byte chunks XOR-swizzled by row; rows past the chunk's
+// four wavefronts, 16-byte pieces XOR-swizzled by row; rows past the span's
 // last key repeat that key (in bounds) and are masked by the consumer.
 template <int D>
 struct KPipe {
@@ -137,11 +144,11 @@ __device__ __forceinline__ void load_obs_q(bf16x8 (&qf)[RT][D / 16], const bf16*
 }
 
 // ---------------------------------------------------------------------------
-// pass 1 (MASS = false): per chunk and observer row, a reference m (at most
+// pass 1 (MASS = false): per span and observer row, a reference m (at most
 // 64 below the row's maximum in log2 units) and the sum of exp2(z - m).
 // pass 2 (MASS = true): per-head window-mean mass of every key and the
-// chunk's sink-isolated entropy partial sums.
-// Workgroup = (1024-key chunk, batch x KV group, 4-head group); the four
+// span's sink-isolated entropy partial sums.
+// Workgroup = (1024-key span, batch x KV group, 4-head group); the four
 // wavefronts (one query head each) share every K stage.  Stages are copied
 // RT_DEPTH - 1 ahead of the one being computed (four LDS buffers), so each
 // workgroup keeps three 16-KB copies in flight against HBM latency; the pass-2
@@ -183,14 +190,14 @@ __global__ __launch_bounds__(256) void obs_pass_kernel(
   __shared__ __attribute__((aligned(1024))) bf16 Ks[RT_DEPTH][RT_KT * D];
   __shared__ float mbuf[MASS ? 4 * RT_CK : 1];
   __shared__ int cs[SEG ? RT_CK : 1];
-  const int chunk = blockIdx.x, bg = blockIdx.y;
+  const int span = blockIdx.x, bg = blockIdx.y;
   const int b = bg / Hkv, g = bg % Hkv;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hg = lane >> 5;
   const int hl = blockIdx.z * 4 + w;
   const bool hvalid = hl < r;
   const int h = g * r + (hvalid ? hl : 0);
-  const int t_begin = chunk * RT_CK, t_end = min(L, t_begin + RT_CK);
+  const int t_begin = span * RT_CK, t_end = min(L, t_begin + RT_CK);
   const int nst = (t_end - t_begin + RT_KT - 1) / RT_KT;
   const bf16* Kg = K + (size_t)bg * ldk * D;
   const int pos0 = L - W;   // observer u sits at pos0 + u
@@ -234,7 +241,7 @@ __global__ __launch_bounds__(256) void obs_pass_kernel(
   // closes the open chunk c: both halves of the row to one reference
   auto flush = [&](int c) {
     if (c < 0) return;
-    const int seg = seg_base[c] + chunk - bounds[2 * c] / RT_CK;
+    const int seg = seg_base[c] + span - bounds[2 * c] / RT_CK;
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt) {
       const float M = xhalf_max(m[rt]);
@@ -253,7 +260,7 @@ __global__ __launch_bounds__(256) void obs_pass_kernel(
   for (int d = 0; d < RT_DEPTH - 1; ++d)
     if (d < nst) KPipe<D>::copy(Ks[d], Kg, t_begin + d * RT_KT, t_end - 1, w, lane);
 
-  // EDGE: the stage holds keys past the chunk or after an observer position
+  // EDGE: the stage holds keys past the span or after an observer position
   auto compute = [&](const bf16* ks, int t0, auto edge_tag) {
     constexpr bool EDGE = decltype(edge_tag)::value;
 #pragma unroll
@@ -301,7 +308,7 @@ __global__ __launch_bounds__(256) void obs_pass_kernel(
           // against it (a term above 2^64, or the first tile, m = kNegBig).
           // Otherwise m may sit below the true maximum: l then holds the sum
           // relative to m, which is all the combine needs (it rescales every
-          // chunk's (m, l) to a common reference), and fp32 keeps the ratios.
+          // span's (m, l) to a common reference), and fp32 keeps the ratios.
           float sum = 0.f;
 #pragma unroll
           for (int i = 0; i < 16; ++i) sum += fast_exp2(__builtin_fmaf(z[rt][i], sl2, -m[rt]));
@@ -415,7 +422,7 @@ __global__ __launch_bounds__(256) void obs_pass_kernel(
       const float Lr = xhalf_sum(l[rt] * fast_exp2(m[rt] - M));
       const int u = rt * 32 + l32;
       if (hg == 0 && u < W) {
-        const size_t o = (((size_t)b * Hq + h) * nch + chunk) * W + u;
+        const size_t o = (((size_t)b * Hq + h) * nch + span) * W + u;
         stat_m[o] = M;
         stat_l[o] = Lr;
       }
@@ -430,16 +437,16 @@ __global__ __launch_bounds__(256) void obs_pass_kernel(
     s1 = wave_sum(s1);
     s2 = wave_sum(s2);
     if (lane == 0) {
-      float* e = ent + (((size_t)b * Hq + h) * nch + chunk) * 2;
+      float* e = ent + (((size_t)b * Hq + h) * nch + span) * 2;
       e[0] = s1;
       e[1] = s2;
     }
   }
 }
 
-// the rows' common reference (the largest chunk reference) and 1/sum: one
+// the rows' common reference (the largest span reference) and 1/sum: one
 // workgroup per (batch, head); the W rows of the head each get 256 / W
-// threads that split the chunks
+// threads that split the spans
 __global__ __launch_bounds__(256) void obs_combine_kernel(const float* __restrict__ stat_m,
                                                           const float* __restrict__ stat_l,
                                                           int nch, int W,
@@ -486,7 +493,7 @@ __global__ __launch_bounds__(64) void head_weight_kernel(const float* __restrict
   const int lane = threadIdx.x;
   const bool on = lane < r;
   const int h = g * r + (on ? lane : 0);
-  // the chunk partial sums: LPH lanes per head, four loads in flight each
+  // the span partial sums: LPH lanes per head, four loads in flight each
   int rp = 1;
   while (rp < r) rp <<= 1;   // r <= 16
   const int LPH = 64 / rp;
