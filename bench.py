@@ -87,6 +87,25 @@ def executed_tiles(idx, cnt, CS, CB, LB, LS):
     return total
 
 
+def union_overlap(idx, cnt, Hkv):
+    """UOR of the GQA groups' block lists ([EP] Sec. 7): per (KV group,
+    segment), the blocks any head of the group selected over the most any one
+    head selected (1 <= UOR <= r); and the distinct blocks of the groups over
+    the heads' listed blocks (the share of block reads a group must fetch)."""
+    Hq, CS = cnt.shape
+    r = Hq // Hkv
+    uors, uni, tot = [], 0, 0
+    for g in range(Hkv):
+        for s in range(CS):
+            sets = [idx[h, s, :cnt[h, s]] for h in range(g * r, (g + 1) * r)]
+            u = np.unique(np.concatenate(sets)).size
+            uors.append(u / max(1, max(x.size for x in sets)))
+            uni += u
+            tot += sum(x.size for x in sets)
+    return {"mean": round(float(np.mean(uors)), 3), "max": round(float(np.max(uors)), 3),
+            "distinct_share": round(uni / max(1, tot), 4)}
+
+
 def scoring_bytes(cfg, k_max, elt):
     Hq, Hkv, d, N = cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.seq_len
     CS, CB = cfg.n_segments, cfg.n_blocks
@@ -289,6 +308,7 @@ def main():
     def mean_ms(a, b):
         return float(np.mean([ev[a].elapsed_time(ev[b]) for ev in all_evs]))
 
+    t_attn_median = float(np.median([ev[3].elapsed_time(ev[4]) for ev in all_evs]))
     t_score = mean_ms(0, 1)
     t_budget = mean_ms(1, 2)
     t_select = mean_ms(2, 3)
@@ -447,6 +467,8 @@ def main():
         "scoring_pass_gbps": round(scoring_gbs, 1),
         "scoring_pass_bytes": sbytes,
         "attn_ms": round(t_attn, 4),
+        "attn_ms_median": round(t_attn_median, 4),
+        "block_list_uor": union_overlap(g_idx, g_cnt, cfg.n_kv_heads),
         "attn_tflops_executed": round(attn_tflops, 2),
         "prefill_tflops_dense_equiv": round(dense_equiv, 2),
         "executed_tiles": tiles,
