@@ -31,6 +31,15 @@ __device__ __forceinline__ int acc_row(int i, int lane) {
   return 8 * (i >> 2) + 4 * (lane >> 5) + (i & 3);
 }
 
+// D(16x16) += A(16x32) * B(32x16), bf16 inputs, fp32 accumulate.
+// Lane l holds row (A) / column (B) l % 16 and 8 k-slots of group l / 16 (the
+// same slots in both operands, so any fixed assignment of k to slots gives the
+// same product).  Accumulator: lane l holds column l % 16, register i holds
+// row 4 * (l / 16) + i.
+__device__ __forceinline__ floatx4 mfma16(bf16x8 a, bf16x8 b, floatx4 c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
 // 2^x with one v_exp_f32.  Results below 2^-126 may flush to zero: every
 // caller exponentiates a logit minus a running maximum, where such terms are
 // far below the fp32 resolution of the sum they join.  exp2f() would add a
@@ -107,6 +116,15 @@ __device__ __forceinline__ void copy16_to_lds_at(const void* sbase, uint32_t vof
 }
 __device__ __forceinline__ void copy16_to_lds(const void* sbase, uint32_t voff, void* lds_base) {
   copy16_to_lds_at(sbase, voff, __builtin_amdgcn_readfirstlane(lds_u32(lds_base)));
+}
+// A pointer the compiler cannot prove wave-uniform, moved into SGPRs (the
+// value of lane 0; callers pass a pointer that is the same on every lane).
+template <typename T>
+__device__ __forceinline__ const T* uniform_ptr(const T* p) {
+  const uint64_t v = (uint64_t)(uintptr_t)p;
+  const uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v);
+  const uint32_t hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+  return (const T*)(uintptr_t)(((uint64_t)hi << 32) | lo);
 }
 // Wait until at most N of this wave's vector-memory operations are in flight.
 // Loads retire in issue order, so with only direct LDS copies outstanding this

@@ -10,25 +10,30 @@
 // (EntroPrefill Sec. 3.1).  The softmax statistics use the online max / sum
 // recurrence of EntroPrefill Sec. 8.1.
 //
-// gfx950 design:
-//  * K1 streams K once from HBM (16-byte loads along d, fp32 sums) and writes
-//    the block means as a bf16 hi/lo pair, so the probe logits can run on
-//    bf16 MFMA with ~2^-17 relative error (two MFMAs per product).
-//  * K2 splits the causal blocks of every (segment, KV group) into chunks of
-//    64 blocks; a workgroup stages one chunk's hi/lo block means in LDS once
-//    and scores the probe rows of all r heads of the group against it on
-//    v_mfma_f32_32x32x16_bf16.  Four kernels, no logits stored:
-//      probe_stats   blocks as M: a lane owns a probe row; the chunk's row
-//                    maximum and sum of exponentials;
-//      probe_combine the chunks' (max, sum) pairs folded into each row's
-//                    maximum and 1/sum;
-//      probe_mass    blocks as N: a lane owns a block; the probe-averaged mass
-//                    is a register sum, written as the block's score, with
-//                    the chunk's entropy partial sum;
-//      probe_entropy the partial sums of every (head, segment) added in chunk
-//                    order.
-//    Work items run on a 1-D grid with every chunk of a (segment, group) on
-//    one XCD, so its probe queries and block means are fetched into one L2.
+// gfx950 design: four kernels, no logits stored.
+//  * pool_keys streams K once from HBM: a workgroup of eight waves pools a
+//    chunk of 16 key blocks (a wave takes two, 16-byte nontemporal loads
+//    along d, 16 in flight per lane, fp32 sums reduced across the wave's row
+//    phases) and writes the block means as a bf16 hi/lo pair (k_bar ~= hi +
+//    lo to ~2^-17, so the logits run on bf16 MFMA with two products each).
+//  * probe_stats and probe_mass take (128-block piece, segment, KV group)
+//    work items.  The piece's hi/lo block means are copied straight from
+//    global memory into LDS (one round trip, shared by the r heads of the
+//    group) while each wave loads the probe queries of its head into
+//    registers; then v_mfma_f32_32x32x16_bf16 forms the piece's logits.
+//      probe_stats  blocks as M (a lane owns a probe row): each row's maximum
+//                   and sum of exponentials over the piece, one partial per
+//                   (row, piece);
+//      probe_mass   folds a row's partials (at most C_B / 128) into the row's
+//                   log2 offset M + log2 L, recomputes the logits with the
+//                   blocks as N (a lane owns a block, the probe mean is a
+//                   register sum) and writes the piece's block scores and its
+//                   entropy partial.
+//    Items are numbered group-major and every XCD takes a contiguous range,
+//    so a group's block means, probe queries and partials (~2 MB at 128k)
+//    stay in one XCD's L2.
+//  * probe_entropy adds the entropy partials of every (head, segment) in
+//    piece order.
 #include <algorithm>
 
 #include "egs_device.h"
@@ -36,82 +41,15 @@
 
 namespace egs {
 
-// ---------------------------------------------------------------------------
-// K1: kbar[g, j, :] = mean of keys j*LB .. (j+1)*LB-1 of KV head g.
-// One workgroup per (block, KV head); thread = (row phase, 8-wide d chunk).
-// ---------------------------------------------------------------------------
-template <typename T, int D>
-__global__ __launch_bounds__(256) void pool_keys_kernel(const T* __restrict__ K, int N,
-                                                        int LB, int CB,
-                                                        bf16* __restrict__ kb_hi,
-                                                        bf16* __restrict__ kb_lo) {
-  constexpr int CH = D / 8;        // 8-element chunks per key row
-  constexpr int RP = 256 / CH;     // key rows covered per pass
-  __shared__ float red[RP][D];
-  const int j = blockIdx.x, g = blockIdx.y;
-  const int tid = threadIdx.x, c = tid % CH, ro = tid / CH;
-  const T* base = K + ((size_t)g * N + (size_t)j * LB) * D + c * 8;
-  float acc[8];
-#pragma unroll
-  for (int e = 0; e < 8; ++e) acc[e] = 0.f;
-  // four rows in flight per step
-  for (int r0 = ro; r0 < LB; r0 += 4 * RP) {
-    float x[4][8];
-#pragma unroll
-    for (int u = 0; u < 4; ++u) {
-      const int r = r0 + u * RP;
-      if (r < LB) {
-        load8f(base + (size_t)r * D, x[u]);
-      } else {
-#pragma unroll
-        for (int e = 0; e < 8; ++e) x[u][e] = 0.f;
-      }
-    }
-#pragma unroll
-    for (int u = 0; u < 4; ++u)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) acc[e] += x[u][e];
-  }
-#pragma unroll
-  for (int e = 0; e < 8; ++e) red[ro][c * 8 + e] = acc[e];
-  __syncthreads();
-  for (int col = tid; col < D; col += 256) {
-    float s = 0.f;
-    for (int q = 0; q < RP; ++q) s += red[q][col];
-    const float mean = s / (float)LB;
-    const bf16 hi = f2bf(mean);
-    const bf16 lo = f2bf(mean - bf2f(hi));
-    const size_t o = ((size_t)g * CB + j) * D + col;
-    kb_hi[o] = hi;
-    kb_lo[o] = lo;
-  }
-}
-
-// ---------------------------------------------------------------------------
-// K2: probe observation rows and entropy, in 64-block chunks.
-//
-// Work item (chunk of SC_CK key blocks, segment s, KV group g); the r query
-// heads of the group share the chunk's pooled keys, staged once in LDS.
-//   probe_stats:   per probe row, the maximum and the sum of exp of its logits
-//                  over the chunk's causal blocks (online softmax statistics).
-//   probe_combine: one thread per (head, segment, probe row) folds the chunk
-//                  statistics into the row's maximum and 1/sum.
-//   probe_mass:    recomputes the chunk's logits with blocks as the MFMA N
-//                  dimension (a lane owns a block) and sums the normalised
-//                  probabilities over the probe rows: a_bar for the chunk's
-//                  blocks, plus the chunk's partial entropy sum.  Chunks past
-//                  the segment's causal range write the -1 sentinels.
-//   probe_entropy: one thread per (head, segment) adds the partial sums, in
-//                  chunk order, into E.
-// Every workgroup issues its global loads before it waits on any of them.
-// ---------------------------------------------------------------------------
-constexpr int SC_CK = 64;     // key blocks per chunk
-constexpr int SC_RT = 2;      // probe row tiles (32 rows) in registers at once (stats)
-constexpr int SC_RTM = 1;     // the same for the mass pass
+constexpr int PS_NB = 16;     // key blocks per pool_keys workgroup
+constexpr int PS_NW = 8;      // waves per pool_keys workgroup
+constexpr int PS_U = 16;      // 16-byte key loads in flight per lane while pooling
+constexpr int PC = 128;       // key blocks per probe piece
 
 struct ScoreLayout {
-  size_t kb_hi, kb_lo, stat_m, stat_l, row_m, row_inv, ent, total;
-  int nch;
+  size_t kb_hi, kb_lo, stat_m, stat_l, ent, total;
+  int npool;    // pool_keys chunks per KV group
+  int npc;      // probe pieces per segment (at most)
 };
 
 static size_t sc_align(size_t x) {
@@ -120,7 +58,8 @@ static size_t sc_align(size_t x) {
 
 static ScoreLayout score_layout(const PrefillDims& p) {
   ScoreLayout o;
-  o.nch = (p.CB + SC_CK - 1) / SC_CK;
+  o.npool = (p.CB + PS_NB - 1) / PS_NB;
+  o.npc = (p.CB + PC - 1) / PC;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -130,11 +69,9 @@ static ScoreLayout score_layout(const PrefillDims& p) {
   o.kb_hi = take((size_t)p.Hkv * p.CB * p.D * sizeof(bf16));
   o.kb_lo = take((size_t)p.Hkv * p.CB * p.D * sizeof(bf16));
   const size_t rows = (size_t)p.Hq * p.CS * p.P;
-  o.stat_m = take(rows * o.nch * sizeof(float));
-  o.stat_l = take(rows * o.nch * sizeof(float));
-  o.row_m = take(rows * sizeof(float));
-  o.row_inv = take(rows * sizeof(float));
-  o.ent = take((size_t)p.Hq * p.CS * o.nch * sizeof(float));
+  o.stat_m = take(rows * o.npc * sizeof(float));
+  o.stat_l = take(rows * o.npc * sizeof(float));
+  o.ent = take((size_t)p.Hq * p.CS * o.npc * sizeof(float));
   o.total = off;
   return o;
 }
@@ -186,60 +123,81 @@ struct QFrag<float> {
   __device__ static void split(const raw_t& v, bf16x8& hi, bf16x8& lo) { split8(v.x, hi, lo); }
 };
 
+// Add the elements of one 16-byte load (raw bits) to acc.
+__device__ __forceinline__ void add16(const u32x4& v, float* acc, const bf16*) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    acc[2 * e] += __uint_as_float(v[e] << 16);
+    acc[2 * e + 1] += __uint_as_float(v[e] & 0xFFFF0000u);
+  }
+}
+__device__ __forceinline__ void add16(const u32x4& v, float* acc, const float*) {
+#pragma unroll
+  for (int e = 0; e < 4; ++e) acc[e] += __uint_as_float(v[e]);
+}
+
+// ---------------------------------------------------------------------------
+// K1 pool_keys: one workgroup per (16-block chunk, KV group g);
+//   kbar[g, j, :] = mean of keys j*LB .. (j+1)*LB-1, stored as bf16 hi + lo.
+// Every chunk of one KV group runs on one XCD (workgroup id mod 8), in order.
+// ---------------------------------------------------------------------------
+template <typename T, int D, int NW>
+__global__ __launch_bounds__(64 * NW, 16 / NW) void pool_keys_kernel(
+    const T* __restrict__ K, int N, int LB, int CB, int Hkv, int nch, bf16* __restrict__ kb_hi,
+    bf16* __restrict__ kb_lo) {
+  constexpr int EPC = 16 / (int)sizeof(T);   // elements per 16-byte load
+  constexpr int CH = D / EPC;                // 16-byte chunks per key row
+  constexpr int RPH = 64 / CH;               // key rows covered by one wave load
+  static_assert(CH >= 1 && CH <= 64 && 64 % CH == 0, "row chunking");
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int items = Hkv * nch, per_xcd = (items + 7) / 8;
+  const int item = (blockIdx.x & 7) * per_xcd + (blockIdx.x >> 3);
+  if (item >= items) return;
+  const int g = item / nch, c = item % nch;
+  const int j0 = c * PS_NB, nb = min(PS_NB, CB - j0);
+  // wave w takes blocks w, w + NW, ...; lane = (row phase, 16-byte chunk).
+  // K is read once: nontemporal loads keep it from displacing reused data.
+  const int cc = lane % CH, rp = lane / CH;
+  const int nr = rp < LB ? (LB - rp + RPH - 1) / RPH : 0;
+  const float inv_lb = 1.0f / (float)LB;
+  for (int bi = w; bi < nb; bi += NW) {
+    float acc[EPC];
+#pragma unroll
+    for (int e = 0; e < EPC; ++e) acc[e] = 0.f;
+    const T* base = K + ((size_t)g * N + (size_t)(j0 + bi) * LB + rp) * D + cc * EPC;
+    for (int i0 = 0; i0 < nr; i0 += PS_U) {
+      u32x4 x[PS_U];
+#pragma unroll
+      for (int u = 0; u < PS_U; ++u) {
+        const int i = min(i0 + u, nr - 1);   // clamped: every load stays in the block
+        x[u] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4*>(base + (size_t)i * RPH * D));
+      }
+#pragma unroll
+      for (int u = 0; u < PS_U; ++u)
+        if (i0 + u < nr) add16(x[u], acc, (const T*)nullptr);
+    }
+#pragma unroll
+    for (int o = CH; o < 64; o <<= 1)
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) acc[e] += __shfl_xor(acc[e], o);
+    if (rp == 0) {
+      const size_t go = ((size_t)g * CB + j0 + bi) * D + cc * EPC;
+#pragma unroll
+      for (int e = 0; e < EPC; ++e) {
+        const float mean = acc[e] * inv_lb;
+        const bf16 hv = f2bf(mean);
+        kb_hi[go + e] = hv;
+        kb_lo[go + e] = f2bf(mean - bf2f(hv));
+      }
+    }
+  }
+}
+
 // XOR swizzle of the 16-byte chunks of a D-wide bf16 row in LDS
 template <int D>
 __device__ __forceinline__ int kbar_swz(int row) {
   return lds_swz<D * 2>(row);
-}
-
-// Stage the hi / lo pooled keys of blocks c0 .. c0 + nb - 1 (zero beyond) in
-// LDS, 16-byte chunks XOR-swizzled by row; all loads are issued first.
-template <int D>
-__device__ __forceinline__ void stage_kbar(bf16* kh, bf16* kl, const bf16* KH, const bf16* KL,
-                                           int c0, int nb) {
-  constexpr int KCH = D / 8;
-  constexpr int PER = (SC_CK * KCH + 255) / 256;
-  u32x4 vh[PER], vl[PER];
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int q = threadIdx.x + 256 * i;
-    const int row = q / KCH, c8 = q % KCH;
-    vh[i] = u32x4{0u, 0u, 0u, 0u};
-    vl[i] = u32x4{0u, 0u, 0u, 0u};
-    if (q < SC_CK * KCH && row < nb) {
-      const size_t o = (size_t)(c0 + row) * D + c8 * 8;
-      vh[i] = *reinterpret_cast<const u32x4*>(KH + o);
-      vl[i] = *reinterpret_cast<const u32x4*>(KL + o);
-    }
-  }
-#pragma unroll
-  for (int i = 0; i < PER; ++i) {
-    const int q = threadIdx.x + 256 * i;
-    if (q < SC_CK * KCH) {
-      const int row = q / KCH, c8 = q % KCH;
-      const int at = row * D + ((c8 ^ kbar_swz<D>(row)) * 8);
-      *reinterpret_cast<u32x4*>(kh + at) = vh[i];
-      *reinterpret_cast<u32x4*>(kl + at) = vl[i];
-    }
-  }
-}
-
-// 1-D grid -> (chunk, segment, KV group) with every chunk of one (segment,
-// group) pair on the same XCD (workgroup id mod 8), so the pair's probe
-// queries and pooled keys are fetched into one L2 only.  Within every run of
-// eight pairs XCD x takes pair 8m + ((x - m) mod 8), so the pairs rotate over
-// the XCDs and the causal segments' unequal work spreads evenly.  Returns
-// false for the padding ids of the last, partial group of eight pairs.
-__device__ __forceinline__ bool probe_item(int bid, int nch, int CS, int Hkv, int& ch, int& s,
-                                           int& g) {
-  const int xcd = bid & 7, k = bid >> 3;
-  ch = k % nch;
-  const int m = k / nch;
-  const int pair = 8 * m + ((xcd - m) & 7);
-  if (pair >= CS * Hkv) return false;
-  g = pair / CS;
-  s = pair % CS;
-  return true;
 }
 
 // 16 bf16 of pooled-key row `row`, d chunk (2c + hg), from the swizzled stage
@@ -248,218 +206,320 @@ __device__ __forceinline__ bf16x8 kbar_frag(const bf16* k, int row, int c, int h
   return load8(k + row * D + (((2 * c + hg) ^ kbar_swz<D>(row)) * 8));
 }
 
+// Direct global -> LDS copies of the hi / lo block means of blocks
+// c0 .. c0 + PC - 1 into the swizzled stage (4 waves).  Each copy lands at
+// a fixed LDS slot; the lane fetches the global chunk that belongs there.
+// Rows at or past nb repeat block c0 + nb - 1, whose logits every reader
+// masks or discards.  Completion: wait_vmem() and a workgroup barrier.
+template <int D>
+__device__ __forceinline__ void stage_piece(bf16* kh, bf16* kl, const bf16* KH, const bf16* KL,
+                                            int c0, int nb) {
+  constexpr int KCH = D / 8;                    // 16-byte chunks per row
+  constexpr int NI = (PC * KCH + 255) / 256;    // copies per lane per plane
+  const int lane = threadIdx.x & 63;
+  const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
+  const bf16* sh = uniform_ptr(KH + (size_t)c0 * D);
+  const bf16* sl = uniform_ptr(KL + (size_t)c0 * D);
+  const uint32_t dh = __builtin_amdgcn_readfirstlane(lds_u32(kh));
+  const uint32_t dl = __builtin_amdgcn_readfirstlane(lds_u32(kl));
+#pragma unroll
+  for (int ii = 0; ii < NI; ++ii) {
+    const int q = (w * NI + ii) * 64 + lane;    // destination chunk
+    if (w * NI + ii >= PC * KCH / 64) break;      // (wave-uniform) past the stage
+    const int row = q / KCH, slot = q % KCH;
+    const int src = min(row, nb - 1);
+    const uint32_t off = (uint32_t)((src * D + (slot ^ kbar_swz<D>(row)) * 8) * sizeof(bf16));
+    const uint32_t at = (uint32_t)((w * NI + ii) * 1024);
+    copy16_to_lds_at(sh, off, dh + at);
+    copy16_to_lds_at(sl, off, dl + at);
+  }
+}
+
+// 1-D grid -> (piece, segment, KV group): the items are numbered group-major
+// (group, segment, piece) and every XCD (workgroup id mod 8) takes one
+// contiguous eighth of them, so a group's pooled keys, probe queries and
+// partials are fetched into one L2 only.  Returns false for padding ids.
+__device__ __forceinline__ bool probe_item(int bid, int npc, int CS, int Hkv, int& ch, int& s,
+                                           int& g) {
+  const int items = Hkv * CS * npc, per_xcd = (items + 7) / 8;
+  const int item = (bid & 7) * per_xcd + (bid >> 3);
+  if (item >= items) return false;
+  ch = item % npc;
+  s = (item / npc) % CS;
+  g = item / (npc * CS);
+  return true;
+}
+
+// MFMA fragments of RTG 32-row probe tiles of head h, rows grp * 32 RTG ..:
+// lane l holds row (l % 32) of each tile and d slots 16 c + 8 (l / 32) .. + 7
+// (zero past the probe).
+template <typename TQ, int D, int RTG>
+__device__ __forceinline__ void load_probe(typename QFrag<TQ>::raw_t (&qr)[RTG][D / 16],
+                                           const TQ* Q, int h, int N, size_t u_begin, int P,
+                                           int grp) {
+  const int lane = threadIdx.x & 63, l32 = lane & 31, hg = lane >> 5;
+#pragma unroll
+  for (int t = 0; t < RTG; ++t) {
+    const int urow = grp * 32 * RTG + t * 32 + l32;
+    const bool ok = urow < P;
+    const TQ* qp = Q + ((size_t)h * N + u_begin + (ok ? urow : 0)) * D;
+#pragma unroll
+    for (int c = 0; c < D / 16; ++c) qr[t][c] = QFrag<TQ>::load(qp + 16 * c + 8 * hg, ok);
+  }
+}
+
+// ---------------------------------------------------------------------------
+// K2a probe_stats: work item (piece of PC key blocks, segment s, KV group g).
+// For each head of the group (one per wave at a time) and probe row u:
+//   m = max_j z_uj, l = sum_j 2^(z_uj - m) over the piece's causal blocks
+//   j < C_B(s) (z in log2 units), stored at stat[h, s, piece, u].
+// Blocks are the MFMA M dimension: a lane owns a probe row, a register a block.
+// ---------------------------------------------------------------------------
 template <typename TQ, int D>
-__global__ __launch_bounds__(256) void probe_stats_kernel(
+__global__ __launch_bounds__(256, 2) void probe_stats_kernel(
     const TQ* __restrict__ Q, const bf16* __restrict__ kb_hi, const bf16* __restrict__ kb_lo,
-    int Hq, int r, int N, int LS, int LB, int P, int CS, int CB, int nch, float scale_log2,
+    int Hq, int r, int N, int LS, int LB, int P, int CS, int CB, int npc, float scale_log2,
     float* __restrict__ stat_m, float* __restrict__ stat_l) {
   constexpr int NC = D / 16;
+  constexpr int BT = PC / 32;
+  constexpr int RTG = sizeof(TQ) == 2 ? 2 : 1;   // 32-row probe tiles per group
   typedef typename QFrag<TQ>::raw_t raw_t;
-  __shared__ __attribute__((aligned(16))) bf16 kh[SC_CK * D];
-  __shared__ __attribute__((aligned(16))) bf16 kl[SC_CK * D];
+  __shared__ __attribute__((aligned(16))) bf16 kh[PC * D];
+  __shared__ __attribute__((aligned(16))) bf16 kl[PC * D];
   int ch, s, g;
-  if (!probe_item(blockIdx.x, nch, CS, Hq / r, ch, s, g)) return;
+  if (!probe_item(blockIdx.x, npc, CS, Hq / r, ch, s, g)) return;
   const int cb = (s + 1) * (LS / LB);
-  const int c0 = ch * SC_CK;
+  const int c0 = ch * PC;
   if (c0 >= cb) return;
-  const int nb = min(SC_CK, cb - c0);
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int nb = min(PC, cb - c0);
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int l32 = lane & 31, hg = lane >> 5;
   const size_t u_begin = (size_t)(s + 1) * LS - P;
-  const int nrt = (P + 31) / 32;
-  // (head, row tile) work items of this wave, SC_RT row tiles per round
-  for (int it0 = w * SC_RT; it0 < r * nrt; it0 += 4 * SC_RT) {
-    raw_t qr[SC_RT][NC];
+  const int ngrp = (P + 32 * RTG - 1) / (32 * RTG);
+
+  stage_piece<D>(kh, kl, kb_hi + (size_t)g * CB * D, kb_lo + (size_t)g * CB * D, c0, nb);
+  raw_t qr[RTG][NC];
+  if (w < r) load_probe<TQ, D, RTG>(qr, Q, g * r + w, N, u_begin, P, 0);
+  wait_vmem();
+  __syncthreads();
+
+  for (int hl = w; hl < r; hl += 4) {
+    const int h = g * r + hl;
+    for (int grp = 0; grp < ngrp; ++grp) {
+      if (hl != w || grp != 0) load_probe<TQ, D, RTG>(qr, Q, h, N, u_begin, P, grp);
+      bf16x8 qh[RTG][NC], ql[RTG][NC];
 #pragma unroll
-    for (int t = 0; t < SC_RT; ++t) {
-      const int it = it0 + t;
-      const int hl = it / nrt, rt = it % nrt;
-      const int urow = rt * 32 + l32;
-      const bool ok = it < r * nrt && urow < P;
-      const TQ* qp = Q + ((size_t)(g * r + (ok ? hl : 0)) * N + u_begin + (ok ? urow : 0)) * D;
+      for (int t = 0; t < RTG; ++t)
 #pragma unroll
-      for (int c = 0; c < NC; ++c) qr[t][c] = QFrag<TQ>::load(qp + 16 * c + 8 * hg, ok);
-    }
-    if (it0 == w * SC_RT) {
-      stage_kbar<D>(kh, kl, kb_hi + (size_t)g * CB * D, kb_lo + (size_t)g * CB * D, c0, nb);
-      __syncthreads();
-    }
+        for (int c = 0; c < NC; ++c) QFrag<TQ>::split(qr[t][c], qh[t][c], ql[t][c]);
+      float m[RTG], l[RTG];
 #pragma unroll
-    for (int t = 0; t < SC_RT; ++t) {
-      const int it = it0 + t;
-      if (it >= r * nrt) break;
-      const int hl = it / nrt, rt = it % nrt;
-      const int urow = rt * 32 + l32;
-      bf16x8 qh[NC], ql[NC];
+      for (int t = 0; t < RTG; ++t) {
+        m[t] = -INFINITY;
+        l[t] = 0.f;
+      }
+      // block tiles outer, probe tiles inner: each LDS fragment is read once
 #pragma unroll
-      for (int c = 0; c < NC; ++c) QFrag<TQ>::split(qr[t][c], qh[c], ql[c]);
-      float m = kNegBig, l = 0.f;
-      for (int bt = 0; bt * 32 < nb; ++bt) {
-        floatx16 zt;
+      for (int bt = 0; bt < BT; ++bt) {
+        if (bt * 32 >= nb) break;
+        floatx16 z[RTG];
 #pragma unroll
-        for (int i = 0; i < 16; ++i) zt[i] = 0.f;
+        for (int t = 0; t < RTG; ++t)
+#pragma unroll
+          for (int i = 0; i < 16; ++i) z[t][i] = 0.f;
 #pragma unroll
         for (int c = 0; c < NC; ++c) {
           const bf16x8 ah = kbar_frag<D>(kh, bt * 32 + l32, c, hg);
           const bf16x8 al = kbar_frag<D>(kl, bt * 32 + l32, c, hg);
-          zt = mfma32(ah, qh[c], zt);
-          zt = mfma32(al, qh[c], zt);
-          if (QFrag<TQ>::kSplit) zt = mfma32(ah, ql[c], zt);
-        }
-        float tmax = kNegBig;
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          const float v = (bt * 32 + acc_row(i, lane) < nb) ? zt[i] * scale_log2 : -INFINITY;
-          zt[i] = v;
-          tmax = fmaxf(tmax, v);
+          for (int t = 0; t < RTG; ++t) {
+            z[t] = mfma32(ah, qh[t][c], z[t]);
+            z[t] = mfma32(al, qh[t][c], z[t]);
+            if (QFrag<TQ>::kSplit) z[t] = mfma32(ah, ql[t][c], z[t]);
+          }
         }
-        const float mn = fmaxf(m, tmax);
-        float sum = 0.f;
+        // z[t][i]: block c0 + bt*32 + acc_row(i, lane) against probe row l32 of tile t
 #pragma unroll
-        for (int i = 0; i < 16; ++i) sum += fast_exp2(zt[i] - mn);
-        l = l * fast_exp2(m - mn) + sum;
-        m = mn;
+        for (int t = 0; t < RTG; ++t) {
+          float tmax = -INFINITY;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) {
+            const float v = bt * 32 + acc_row(i, lane) < nb ? z[t][i] * scale_log2 : -INFINITY;
+            z[t][i] = v;
+            tmax = fmaxf(tmax, v);
+          }
+          tmax = xhalf_max(tmax);   // finite: the tile's first block is causal
+          const float mn = fmaxf(m[t], tmax);
+          float sum = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sum += fast_exp2(z[t][i] - mn);
+          l[t] = l[t] * fast_exp2(m[t] - mn) + xhalf_sum(sum);
+          m[t] = mn;
+        }
       }
-      const float M = xhalf_max(m);
-      const float Lr = xhalf_sum(l * fast_exp2(m - M));
-      if (hg == 0 && urow < P) {
-        const size_t o = (((size_t)(g * r + hl) * CS + s) * nch + ch) * P + urow;
-        stat_m[o] = M;
-        stat_l[o] = Lr;
+#pragma unroll
+      for (int t = 0; t < RTG; ++t) {
+        const int urow = grp * 32 * RTG + t * 32 + l32;
+        if (hg == 0 && urow < P) {
+          const size_t o = (((size_t)h * CS + s) * npc + ch) * P + urow;
+          stat_m[o] = m[t];
+          stat_l[o] = l[t];
+        }
       }
     }
-  }
-  // waves without work items still take part in the staging barrier
-  if (w * SC_RT >= r * nrt) {
-    stage_kbar<D>(kh, kl, kb_hi + (size_t)g * CB * D, kb_lo + (size_t)g * CB * D, c0, nb);
-    __syncthreads();
   }
 }
 
-// one thread per (head, segment, probe row): the row's maximum and 1/sum
-__global__ __launch_bounds__(256) void probe_combine_kernel(
-    const float* __restrict__ stat_m, const float* __restrict__ stat_l, int CS, int P, int nch,
-    int bps, int total, float* __restrict__ row_m, float* __restrict__ row_inv) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
-  if (i >= total) return;
-  const int u = i % P, hs = i / P, s = hs % CS;
-  const int nch_s = ((s + 1) * bps + SC_CK - 1) / SC_CK;
-  const float* sm = stat_m + (size_t)hs * nch * P + u;
-  const float* sl = stat_l + (size_t)hs * nch * P + u;
-  // chunks in rounds of eight, loads issued together (index clamped), the
-  // running maximum raised per round
-  float M = kNegBig, L = 0.f;
-  for (int c0 = 0; c0 < nch_s; c0 += 8) {
-    float m8[8], l8[8];
+// Fold up to RP_B partials (m, l) of one probe row, starting at partial p0,
+// into the running (M, L).  A row's partials lie P floats apart (lanes on
+// consecutive rows read consecutive floats); indices past n are clamped to
+// the last partial on load and ignored by the fold.
+constexpr int RP_B = 8;
+struct RowPartials {
+  float m[RP_B], l[RP_B];
+  __device__ void fetch(const float* sm, const float* sl, int p0, int n, int P) {
 #pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const size_t c = (size_t)min(c0 + j, nch_s - 1) * P;
-      m8[j] = sm[c];
-      l8[j] = sl[c];
+    for (int i = 0; i < RP_B; ++i) {
+      const size_t at = (size_t)min(p0 + i, n - 1) * P;
+      m[i] = sm[at];
+      l[i] = sl[at];
     }
+  }
+  __device__ void fold(int p0, int n, float& M, float& L) const {
     float bm = M;
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (c0 + j < nch_s) bm = fmaxf(bm, m8[j]);
-    L *= fast_exp2(M - bm);
+    for (int i = 0; i < RP_B; ++i)
+      if (p0 + i < n) bm = fmaxf(bm, m[i]);
+    float acc = L * fast_exp2(M - bm);
 #pragma unroll
-    for (int j = 0; j < 8; ++j)
-      if (c0 + j < nch_s) L += l8[j] * fast_exp2(m8[j] - bm);
+    for (int i = 0; i < RP_B; ++i)
+      if (p0 + i < n) acc += l[i] * fast_exp2(m[i] - bm);
     M = bm;
+    L = acc;
   }
-  row_m[i] = M;
-  row_inv[i] = L > 0.f ? 1.0f / L : 0.f;
-}
+};
 
+// ---------------------------------------------------------------------------
+// K2b probe_mass: work item (piece of PC key blocks, segment s, KV group g).
+// For each head of the group (one per wave at a time) and each group of RTG
+// 32-row probe tiles: the rows' partials are folded into the row's log2
+// offset M + log2 L (a lane owns a row), the logits of the piece are
+// recomputed with the blocks as the MFMA N dimension and the normalised
+// probabilities are summed over the probe rows in registers.  Writes a_bar
+// of the piece's causal blocks and the piece's entropy partial.
+// ---------------------------------------------------------------------------
 template <typename TQ, int D>
-__global__ __launch_bounds__(256) void probe_mass_kernel(
+__global__ __launch_bounds__(256, 2) void probe_mass_kernel(
     const TQ* __restrict__ Q, const bf16* __restrict__ kb_hi, const bf16* __restrict__ kb_lo,
-    int Hq, int r, int N, int LS, int LB, int P, int CS, int CB, int nch, float scale_log2,
-    int kind, float alpha, const float* __restrict__ row_m, const float* __restrict__ row_inv,
+    int Hq, int r, int N, int LS, int LB, int P, int CS, int CB, int npc, float scale_log2,
+    int kind, float alpha, const float* __restrict__ stat_m, const float* __restrict__ stat_l,
     float* __restrict__ ent, float* __restrict__ scores) {
   constexpr int NC = D / 16;
-  constexpr int BT = SC_CK / 32;
+  constexpr int BT = PC / 32;
+  constexpr int RTG = sizeof(TQ) == 2 ? 2 : 1;   // 32-row probe tiles per group
+  constexpr int RG = 32 * RTG;                   // probe rows per group
   typedef typename QFrag<TQ>::raw_t raw_t;
-  __shared__ __attribute__((aligned(16))) bf16 kh[SC_CK * D];
-  __shared__ __attribute__((aligned(16))) bf16 kl[SC_CK * D];
+  __shared__ __attribute__((aligned(16))) bf16 kh[PC * D];
+  __shared__ __attribute__((aligned(16))) bf16 kl[PC * D];
   int ch, s, g;
-  if (!probe_item(blockIdx.x, nch, CS, Hq / r, ch, s, g)) return;
+  if (!probe_item(blockIdx.x, npc, CS, Hq / r, ch, s, g)) return;
   const int cb = (s + 1) * (LS / LB);
-  const int c0 = ch * SC_CK;
-  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
+  const int c0 = ch * PC;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int l32 = lane & 31, hg = lane >> 5;
-  const int cend = min(CB, c0 + SC_CK);
   if (c0 >= cb) {   // beyond the causal range: sentinels only
+    const int cend = min(CB, c0 + PC);
     for (int hl = 0; hl < r; ++hl) {
       float* out = scores + ((size_t)(g * r + hl) * CS + s) * CB;
-      for (int j = c0 + tid; j < cend; j += 256) out[j] = -1.0f;
+      for (int j = c0 + (int)threadIdx.x; j < cend; j += 256) out[j] = -1.0f;
     }
     return;
   }
-  const int nb = min(SC_CK, cb - c0);
+  const int nb = min(PC, cb - c0);
+  const int nparts = (cb + PC - 1) / PC;   // probe_stats pieces of segment s
   const size_t u_begin = (size_t)(s + 1) * LS - P;
   const float invP = 1.0f / (float)P;
-  const int nrt = (P + 31) / 32;
-  bool staged = false;
-  // one head per wave at a time; its row tiles SC_RT at a time
+  const int ngrp = (P + RG - 1) / RG;
+  auto part_ptrs = [&](int h, int grp, const float*& sm, const float*& sl) {
+    const int urow = min(grp * RG + lane % RG, P - 1);
+    const size_t o = ((size_t)h * CS + s) * npc * P + urow;
+    sm = stat_m + o;
+    sl = stat_l + o;
+  };
+
+  // one round trip: the piece's block means, the first head's queries and
+  // its rows' first partials are all in flight together
+  stage_piece<D>(kh, kl, kb_hi + (size_t)g * CB * D, kb_lo + (size_t)g * CB * D, c0, nb);
+  raw_t qr[RTG][NC];
+  RowPartials rp;
+  if (w < r) {
+    const float *sm, *sl;
+    load_probe<TQ, D, RTG>(qr, Q, g * r + w, N, u_begin, P, 0);
+    part_ptrs(g * r + w, 0, sm, sl);
+    rp.fetch(sm, sl, 0, nparts, P);
+  }
+  wait_vmem();
+  __syncthreads();
+
   for (int hl = w; hl < r; hl += 4) {
     const int h = g * r + hl;
-    const size_t rbase = ((size_t)h * CS + s) * P;
     float acc[BT];
 #pragma unroll
     for (int bt = 0; bt < BT; ++bt) acc[bt] = 0.f;
-    for (int rt0 = 0; rt0 < nrt; rt0 += SC_RTM) {
-      raw_t qr[SC_RTM][NC];
-      float mown[SC_RTM], iown[SC_RTM];
-#pragma unroll
-      for (int t = 0; t < SC_RTM; ++t) {
-        const int urow = (rt0 + t) * 32 + l32;
-        const bool ok = rt0 + t < nrt && urow < P;
-        const TQ* qp = Q + ((size_t)h * N + u_begin + (ok ? urow : 0)) * D;
-#pragma unroll
-        for (int c = 0; c < NC; ++c) qr[t][c] = QFrag<TQ>::load(qp + 16 * c + 8 * hg, ok);
-        // rows past the probe keep M = 0 and 1/L = 0: their zero logits add nothing
-        mown[t] = ok ? row_m[rbase + urow] : 0.f;
-        iown[t] = ok ? row_inv[rbase + urow] : 0.f;
+    for (int grp = 0; grp < ngrp; ++grp) {
+      const float *sm, *sl;
+      part_ptrs(h, grp, sm, sl);
+      if (hl != w || grp != 0) {
+        load_probe<TQ, D, RTG>(qr, Q, h, N, u_begin, P, grp);
+        rp.fetch(sm, sl, 0, nparts, P);
       }
-      if (!staged) {
-        stage_kbar<D>(kh, kl, kb_hi + (size_t)g * CB * D, kb_lo + (size_t)g * CB * D, c0, nb);
-        __syncthreads();
-        staged = true;
+      float M = kNegBig, L = 0.f;
+      rp.fold(0, nparts, M, L);
+      for (int p0 = RP_B; p0 < nparts; p0 += RP_B) {
+        rp.fetch(sm, sl, p0, nparts, P);
+        rp.fold(p0, nparts, M, L);
       }
+      // a row's probabilities are 2^(z - off), off = M + log2 L; rows past
+      // the probe take off = +inf, so they add nothing
+      const bool own = grp * RG + (lane % RG) < P && L > 0.f;
+      const float off = own ? M + __log2f(L) : INFINITY;
+      // registers of the mass pass hold rows acc_row(i, lane): fetch their offsets
+      float ro[RTG][16];
+      bf16x8 qh[RTG][NC], ql[RTG][NC];
 #pragma unroll
-      for (int t = 0; t < SC_RTM; ++t) {
-        if (rt0 + t >= nrt) break;
-        // registers of the mass pass hold rows acc_row(i, lane): fetch their stats
-        float rm[16], ri[16];
+      for (int t = 0; t < RTG; ++t) {
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          rm[i] = __shfl(mown[t], acc_row(i, lane));
-          ri[i] = __shfl(iown[t], acc_row(i, lane));
-        }
-        bf16x8 qh[NC], ql[NC];
+        for (int i = 0; i < 16; ++i) ro[t][i] = __shfl(off, t * 32 + acc_row(i, lane));
 #pragma unroll
-        for (int c = 0; c < NC; ++c) QFrag<TQ>::split(qr[t][c], qh[c], ql[c]);
+        for (int c = 0; c < NC; ++c) QFrag<TQ>::split(qr[t][c], qh[t][c], ql[t][c]);
+      }
+      // block tiles outer, probe tiles inner: each LDS fragment is read once
 #pragma unroll
-        for (int bt = 0; bt < BT; ++bt) {
-          if (bt * 32 >= nb) break;
-          floatx16 z;
+      for (int bt = 0; bt < BT; ++bt) {
+        if (bt * 32 >= nb) break;
+        floatx16 z[RTG];
 #pragma unroll
-          for (int i = 0; i < 16; ++i) z[i] = 0.f;
+        for (int t = 0; t < RTG; ++t)
 #pragma unroll
-          for (int c = 0; c < NC; ++c) {
-            const bf16x8 bh = kbar_frag<D>(kh, bt * 32 + l32, c, hg);
-            const bf16x8 bl = kbar_frag<D>(kl, bt * 32 + l32, c, hg);
-            z = mfma32(qh[c], bh, z);
-            z = mfma32(qh[c], bl, z);
-            if (QFrag<TQ>::kSplit) z = mfma32(ql[c], bh, z);
+          for (int i = 0; i < 16; ++i) z[t][i] = 0.f;
+#pragma unroll
+        for (int c = 0; c < NC; ++c) {
+          const bf16x8 bh = kbar_frag<D>(kh, bt * 32 + l32, c, hg);
+          const bf16x8 bl = kbar_frag<D>(kl, bt * 32 + l32, c, hg);
+#pragma unroll
+          for (int t = 0; t < RTG; ++t) {
+            z[t] = mfma32(qh[t][c], bh, z[t]);
+            z[t] = mfma32(qh[t][c], bl, z[t]);
+            if (QFrag<TQ>::kSplit) z[t] = mfma32(ql[t][c], bh, z[t]);
           }
-          float colsum = 0.f;
+        }
+        float colsum = 0.f;
+#pragma unroll
+        for (int t = 0; t < RTG; ++t)
 #pragma unroll
           for (int i = 0; i < 16; ++i)
-            colsum += fast_exp2(__builtin_fmaf(z[i], scale_log2, -rm[i])) * ri[i];
-          acc[bt] += xhalf_sum(colsum);
-        }
+            colsum += fast_exp2(__builtin_fmaf(z[t][i], scale_log2, -ro[t][i]));
+        acc[bt] += xhalf_sum(colsum);
       }
     }
     float* out = scores + ((size_t)h * CS + s) * CB;
@@ -473,99 +533,75 @@ __global__ __launch_bounds__(256) void probe_mass_kernel(
         if (a > 0.f) epart += (kind == EGS_SHANNON) ? -a * logf(a) : powf(a, alpha);
       }
     }
-    for (int j = c0 + nb + lane; j < cend; j += 64) out[j] = -1.0f;
+    // blocks of the piece past the segment's causal range
+    for (int j = c0 + nb + lane; j < min(CB, c0 + PC); j += 64) out[j] = -1.0f;
     epart = wave_sum(epart);
-    if (lane == 0) ent[((size_t)h * CS + s) * nch + ch] = epart;
-  }
-  // waves without a head still take part in the staging barrier
-  if (!staged) {
-    stage_kbar<D>(kh, kl, kb_hi + (size_t)g * CB * D, kb_lo + (size_t)g * CB * D, c0, nb);
-    __syncthreads();
+    if (lane == 0) ent[((size_t)h * CS + s) * npc + ch] = epart;
   }
 }
 
-// one thread per (head, segment): E from the chunks' partial sums, in order
+// one thread per (head, segment): E from the pieces' partial sums, in order
 __global__ __launch_bounds__(256) void probe_entropy_kernel(const float* __restrict__ ent,
-                                                            int Hq, int CS, int nch, int bps,
+                                                            int Hq, int CS, int npc, int bps,
                                                             int kind, float alpha,
                                                             float* __restrict__ entropy) {
   const int i = blockIdx.x * 256 + threadIdx.x;
   if (i >= Hq * CS) return;
   const int s = i % CS;
-  const int nch_s = ((s + 1) * bps + SC_CK - 1) / SC_CK;
-  const float* e = ent + (size_t)i * nch;
+  const int npieces = ((s + 1) * bps + PC - 1) / PC;
+  const float* e = ent + (size_t)i * npc;
   float tot = 0.f;
-  for (int c = 0; c < nch_s; ++c) tot += e[c];
+  for (int c = 0; c < npieces; ++c) tot += e[c];
   entropy[i] = (kind == EGS_SHANNON) ? tot : logf(tot) / (1.0f - alpha);
 }
 
 // ---------------------------------------------------------------------------
-// launchers
+// launcher
 // ---------------------------------------------------------------------------
 template <typename T>
-static hipError_t pool_dispatch(const PrefillDims& p, const void* k, bf16* hi, bf16* lo,
-                                hipStream_t st) {
-  dim3 grid(p.CB, p.Hkv);
-  const T* K = static_cast<const T*>(k);
-#define EGS_POOL(DD) pool_keys_kernel<T, DD><<<grid, 256, 0, st>>>(K, p.N, p.LB, p.CB, hi, lo)
-  switch (p.D) {
-    case 16: EGS_POOL(16); break;
-    case 32: EGS_POOL(32); break;
-    case 64: EGS_POOL(64); break;
-    case 128: EGS_POOL(128); break;
-    default: return hipErrorInvalidValue;
-  }
-#undef EGS_POOL
-  return hipGetLastError();
-}
-
-template <typename TQ>
-static hipError_t probe_dispatch(const PrefillDims& p, const ScoreLayout& ly, const void* q,
-                                 char* ws, int kind, float alpha, float* scores,
+static hipError_t score_dispatch(const PrefillDims& p, const ScoreLayout& ly, const void* q,
+                                 const void* k, char* ws, int kind, float alpha, float* scores,
                                  float* entropy, hipStream_t st) {
-  const int grid = ((p.CS * p.Hkv + 7) / 8) * ly.nch * 8;
   const float sl2 = p.sm_scale * kLog2e;
-  const int bps = p.LS / p.LB;
-  const TQ* Q = static_cast<const TQ*>(q);
-  const bf16* H = reinterpret_cast<const bf16*>(ws + ly.kb_hi);
-  const bf16* L = reinterpret_cast<const bf16*>(ws + ly.kb_lo);
+  const T* Q = static_cast<const T*>(q);
+  const T* K = static_cast<const T*>(k);
+  bf16* H = reinterpret_cast<bf16*>(ws + ly.kb_hi);
+  bf16* L = reinterpret_cast<bf16*>(ws + ly.kb_lo);
   float* sm = reinterpret_cast<float*>(ws + ly.stat_m);
   float* sl = reinterpret_cast<float*>(ws + ly.stat_l);
-  float* rm = reinterpret_cast<float*>(ws + ly.row_m);
-  float* ri = reinterpret_cast<float*>(ws + ly.row_inv);
   float* en = reinterpret_cast<float*>(ws + ly.ent);
-  const int rows = p.Hq * p.CS * p.P;
+  const int g1 = (p.Hkv * ly.npool + 7) / 8 * 8;
+  const int g2 = (p.Hkv * p.CS * ly.npc + 7) / 8 * 8;
   hipError_t e;
-#define EGS_STATS(DD)                                                                      \
-  probe_stats_kernel<TQ, DD><<<grid, 256, 0, st>>>(Q, H, L, p.Hq, p.r, p.N, p.LS, p.LB,   \
-                                                    p.P, p.CS, p.CB, ly.nch, sl2, sm, sl)
-#define EGS_MASS(DD)                                                                      \
-  probe_mass_kernel<TQ, DD><<<grid, 256, 0, st>>>(Q, H, L, p.Hq, p.r, p.N, p.LS, p.LB,   \
-                                                   p.P, p.CS, p.CB, ly.nch, sl2, kind,     \
-                                                   alpha, rm, ri, en, scores)
-  switch (p.D) {
-    case 16: EGS_STATS(16); break;
-    case 32: EGS_STATS(32); break;
-    case 64: EGS_STATS(64); break;
-    case 128: EGS_STATS(128); break;
-    default: return hipErrorInvalidValue;
-  }
+#define EGS_POOL(DD)                                                                         \
+  pool_keys_kernel<T, DD, PS_NW><<<g1, 64 * PS_NW, 0, st>>>(K, p.N, p.LB, p.CB, p.Hkv,      \
+                                                            ly.npool, H, L)
+#define EGS_STATS(DD)                                                                        \
+  probe_stats_kernel<T, DD><<<g2, 256, 0, st>>>(Q, H, L, p.Hq, p.r, p.N, p.LS, p.LB, p.P,   \
+                                                 p.CS, p.CB, ly.npc, sl2, sm, sl)
+#define EGS_MASS(DD)                                                                         \
+  probe_mass_kernel<T, DD><<<g2, 256, 0, st>>>(Q, H, L, p.Hq, p.r, p.N, p.LS, p.LB, p.P,    \
+                                                p.CS, p.CB, ly.npc, sl2, kind, alpha, sm,  \
+                                                sl, en, scores)
+#define EGS_D_SWITCH(M)              \
+  switch (p.D) {                     \
+    case 16: M(16); break;           \
+    case 32: M(32); break;           \
+    case 64: M(64); break;           \
+    case 128: M(128); break;         \
+    default: return hipErrorInvalidValue; \
+  }                                  \
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  probe_combine_kernel<<<(rows + 255) / 256, 256, 0, st>>>(sm, sl, p.CS, p.P, ly.nch, bps, rows,
-                                                           rm, ri);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  switch (p.D) {
-    case 16: EGS_MASS(16); break;
-    case 32: EGS_MASS(32); break;
-    case 64: EGS_MASS(64); break;
-    case 128: EGS_MASS(128); break;
-    default: return hipErrorInvalidValue;
-  }
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  EGS_D_SWITCH(EGS_POOL)
+  EGS_D_SWITCH(EGS_STATS)
+  EGS_D_SWITCH(EGS_MASS)
+#undef EGS_D_SWITCH
+#undef EGS_POOL
 #undef EGS_STATS
 #undef EGS_MASS
-  probe_entropy_kernel<<<(p.Hq * p.CS + 255) / 256, 256, 0, st>>>(en, p.Hq, p.CS, ly.nch, bps,
-                                                                  kind, alpha, entropy);
+  probe_entropy_kernel<<<(p.Hq * p.CS + 255) / 256, 256, 0, st>>>(en, p.Hq, p.CS, ly.npc,
+                                                                  p.LS / p.LB, kind, alpha,
+                                                                  entropy);
   return hipGetLastError();
 }
 
@@ -574,14 +610,9 @@ hipError_t launch_entropy_score(const PrefillDims& p, const void* q, const void*
                                 hipStream_t st) {
   const ScoreLayout ly = score_layout(p);
   char* w = static_cast<char*>(ws);
-  bf16* hi = reinterpret_cast<bf16*>(w + ly.kb_hi);
-  bf16* lo = reinterpret_cast<bf16*>(w + ly.kb_lo);
-  hipError_t e = p.dtype == EGS_F32 ? pool_dispatch<float>(p, k, hi, lo, st)
-                                    : pool_dispatch<bf16>(p, k, hi, lo, st);
-  if (e != hipSuccess) return e;
   return p.dtype == EGS_F32
-             ? probe_dispatch<float>(p, ly, q, w, kind, alpha, scores, entropy, st)
-             : probe_dispatch<bf16>(p, ly, q, w, kind, alpha, scores, entropy, st);
+             ? score_dispatch<float>(p, ly, q, k, w, kind, alpha, scores, entropy, st)
+             : score_dispatch<bf16>(p, ly, q, k, w, kind, alpha, scores, entropy, st);
 }
 
 }  // namespace egs
