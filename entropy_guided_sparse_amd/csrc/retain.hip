@@ -30,7 +30,8 @@
 //  * Page-level retention (EntroPrefill Sec. 7) keeps whole pages: page maxima
 //    of the token scores, the same select over page scores, and unions over
 //    the heads of a group or the groups of a layer through an LDS bitmap.
-//  * Decode attention splits the kept range into 256-entry splits; the GQA
+//  * Decode attention splits the kept range into 192- to 512-entry splits
+//    (chosen per call so the last round of workgroups fills the CUs); the GQA
 //    group's heads share each 64-entry K / V stage in LDS (lane-per-entry dot
 //    products, lane-per-dim PV) and a combine kernel merges the splits with
 //    their log-sum-exp.
@@ -52,7 +53,8 @@ namespace egs {
 constexpr int RT_CK = 1024;   // keys per span (the pass 1 / pass 2 work unit)
 constexpr int RT_KT = 64;     // keys per LDS stage
 constexpr int SEL_T = 1024;   // threads of the select kernel
-constexpr int DA_SPL = 256;   // kept entries per decode-attention split
+constexpr int DA_SPL_MIN = 192;   // kept entries per decode-attention split: the
+constexpr int DA_SPL_MAX = 512;   // range the launcher chooses from (multiples of 64)
 
 struct RetainLayout {
   size_t stat_m, stat_l, row_m, row_inv, mass, ent, weight, mu, qsum, tstats, total;
@@ -997,7 +999,7 @@ hipError_t launch_kv_retain(const DecodeDims& p, const egs_retain_params& prm, c
 // ---------------------------------------------------------------------------
 // K8: decode attention over the kept entries
 // ---------------------------------------------------------------------------
-// One workgroup per (split of DA_SPL kept entries, batch x KV group); the GQA
+// One workgroup per (split of spl kept entries, batch x KV group); the GQA
 // group's query heads (one per wavefront, four at a time) share every 64-entry
 // K / V stage, copied straight into LDS two stages deep.
 //   QK: a lane owns one entry of the stage; the head's query is broadcast from
@@ -1010,7 +1012,8 @@ hipError_t launch_kv_retain(const DecodeDims& p, const egs_retain_params& prm, c
 template <int D>
 __global__ __launch_bounds__(256) void decode_attn_split_kernel(
     const bf16* __restrict__ Qn, const bf16* __restrict__ K, const bf16* __restrict__ V,
-    int Hq, int Hkv, int r, int n, int ldk, int nsplit, float sl2, float* __restrict__ part) {
+    int Hq, int Hkv, int r, int n, int ldk, int spl, int nsplit, float sl2,
+    float* __restrict__ part) {
   constexpr int KCH = D / 8;           // 16-byte chunks per row
   constexpr int ST = 64;               // entries per stage
   constexpr int PIECES = ST * D * 2 / 1024;
@@ -1023,7 +1026,7 @@ __global__ __launch_bounds__(256) void decode_attn_split_kernel(
   __shared__ float psh[4][ST];
   const int sp = blockIdx.x, bg = blockIdx.y, b = bg / Hkv, g = bg % Hkv;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
-  const int t_begin = sp * DA_SPL, t_end = min(n, t_begin + DA_SPL);
+  const int t_begin = sp * spl, t_end = min(n, t_begin + spl);
   const int nst = (t_end - t_begin + ST - 1) / ST;
   const bf16* Kg = K + (size_t)bg * ldk * D;
   const bf16* Vg = V + (size_t)bg * ldk * D;
@@ -1155,15 +1158,40 @@ __global__ __launch_bounds__(64) void decode_attn_combine_kernel(const float* __
   for (int e = 0; e < DPL; ++e) out[(size_t)bh * D + lane * DPL + e] = f2bf(o[e] * inv);
 }
 
+// Split size: the largest multiple of 64 in [DA_SPL_MIN, DA_SPL_MAX] whose
+// last round of workgroups still fills 90% of the 512 workgroup slots (256
+// CUs x 2, LDS-bound); else the one that leaves the fewest slots idle.  Long
+// caches take 512 (fewer partials to combine); the 4,356 kept entries of a
+// batch-8 step take 192 (23 splits x 64 rows: 2.9 rounds instead of 2.25).
+static int decode_split(const DecodeDims& p, int n_total) {
+  constexpr long kSlots = 512;
+  const long rows = (long)p.B * p.Hkv;
+  int best = DA_SPL_MAX;
+  double best_eff = -1.0;
+  for (int s = DA_SPL_MAX; s >= DA_SPL_MIN; s -= 64) {
+    const long wg = rows * ((n_total + s - 1) / s);
+    const long rounds = (wg + kSlots - 1) / kSlots;
+    if (wg * 10 >= rounds * kSlots * 9) return s;
+    const double eff = (double)wg / (double)(rounds * kSlots);
+    if (eff > best_eff) {
+      best_eff = eff;
+      best = s;
+    }
+  }
+  return best;
+}
+
 size_t decode_attn_workspace_bytes(const DecodeDims& p, int n_total) {
-  const int nsplit = (n_total + DA_SPL - 1) / DA_SPL;
+  const int spl = decode_split(p, n_total);
+  const int nsplit = (n_total + spl - 1) / spl;
   return align_up((size_t)p.B * p.Hq * nsplit * (p.D + 2) * 4);
 }
 
 hipError_t launch_decode_attn(const DecodeDims& p, const void* q_new, const void* k,
                               const void* v, int n_total, int ldk, void* out, void* ws,
                               hipStream_t st) {
-  const int nsplit = (n_total + DA_SPL - 1) / DA_SPL;
+  const int spl = decode_split(p, n_total);
+  const int nsplit = (n_total + spl - 1) / spl;
   const float sl2 = p.sm_scale * kLog2e;
   float* part = static_cast<float*>(ws);
   dim3 grid(nsplit, p.B * p.Hkv);
@@ -1172,10 +1200,10 @@ hipError_t launch_decode_attn(const DecodeDims& p, const void* q_new, const void
   const bf16* V = static_cast<const bf16*>(v);
   if (p.D == 128)
     decode_attn_split_kernel<128><<<grid, 256, 0, st>>>(Qn, K, V, p.Hq, p.Hkv, p.r, n_total,
-                                                        ldk, nsplit, sl2, part);
+                                                        ldk, spl, nsplit, sl2, part);
   else
     decode_attn_split_kernel<64><<<grid, 256, 0, st>>>(Qn, K, V, p.Hq, p.Hkv, p.r, n_total,
-                                                       ldk, nsplit, sl2, part);
+                                                       ldk, spl, nsplit, sl2, part);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.D == 128)
