@@ -702,7 +702,11 @@ __global__ __launch_bounds__(SEL_T) void retain_select_kernel(
     const float* __restrict__ mu, int L, int n_sink, int n_recent, int n_keep, int n_total,
     int32_t* __restrict__ keep_idx) {
   __shared__ int hist[4096];
-  __shared__ uint32_t keys[SEL_R];
+  // the round's keys, one pad word after every 16: a thread scans 16
+  // consecutive keys, so the lanes of a wave read 17 words apart (distinct
+  // banks) instead of 16 (a few banks, many-way conflicts)
+  __shared__ uint32_t keys[SEL_R + SEL_R / 16];
+  auto kslot = [](int j) { return j + (j >> 4); };
   __shared__ int ired[SEL_T / 64];
   __shared__ int sh_digit, sh_above, tot_sel, tot_eq;
   const int bg = blockIdx.x;
@@ -782,7 +786,7 @@ __global__ __launch_bounds__(SEL_T) void retain_select_kernel(
       for (int e = 0; e < SEL_R / SEL_T; ++e) kk[e] = orderable(mu_row[r0 + min(e * SEL_T + tid, rn - 1)]);
 #pragma unroll
       for (int e = 0; e < SEL_R / SEL_T; ++e)
-        if (e * SEL_T + tid < rn) keys[e * SEL_T + tid] = kk[e];
+        if (e * SEL_T + tid < rn) keys[kslot(e * SEL_T + tid)] = kk[e];
     }
     __syncthreads();
     const int j0 = tid * PER;
@@ -795,8 +799,9 @@ __global__ __launch_bounds__(SEL_T) void retain_select_kernel(
         if (!cand || keep_all) {
           ++n_sel;
         } else if (partial) {
-          n_sel += keys[j] > T;
-          n_eq += keys[j] == T;
+          const uint32_t kj = keys[kslot(j)];
+          n_sel += kj > T;
+          n_eq += kj == T;
         }
       }
     }
@@ -815,9 +820,9 @@ __global__ __launch_bounds__(SEL_T) void retain_select_kernel(
           take = true;
         } else if (!partial) {
           take = false;
-        } else if (keys[j] > T) {
+        } else if (keys[kslot(j)] > T) {
           take = true;
-        } else if (keys[j] == T) {
+        } else if (keys[kslot(j)] == T) {
           take = es < kr;
           ++es;
         } else {
