@@ -463,11 +463,27 @@ __global__ __launch_bounds__(256) void obs_combine_kernel(const float* __restric
   if (on) {
     const float* sm = stat_m + (size_t)bh * nch * W + u;
     const float* sl = stat_l + (size_t)bh * nch * W + u;
-    for (int c = part; c < nch; c += parts) {
-      const float mc = sm[(size_t)c * W], lc = sl[(size_t)c * W];
-      const float mn = fmaxf(M, mc);
-      Lr = Lr * fast_exp2(M - mn) + lc * fast_exp2(mc - mn);
-      M = mn;
+    // eight spans per round: their loads are issued together (indices
+    // clamped into range, the extra ones ignored), then folded in order
+    constexpr int NB = 8;
+    for (int c0 = part; c0 < nch; c0 += parts * NB) {
+      float mc[NB], lc[NB];
+#pragma unroll
+      for (int i = 0; i < NB; ++i) {
+        const size_t c = (size_t)min(c0 + i * parts, nch - 1);
+        mc[i] = sm[c * W];
+        lc[i] = sl[c * W];
+      }
+      float bm = M;
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+        if (c0 + i * parts < nch) bm = fmaxf(bm, mc[i]);
+      float acc = Lr * fast_exp2(M - bm);
+#pragma unroll
+      for (int i = 0; i < NB; ++i)
+        if (c0 + i * parts < nch) acc += lc[i] * fast_exp2(mc[i] - bm);
+      M = bm;
+      Lr = acc;
     }
   }
   pm[tid] = M;
