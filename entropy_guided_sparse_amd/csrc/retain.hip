@@ -1759,13 +1759,16 @@ __global__ __launch_bounds__(256) void latent_append_kernel(
     const bf16* __restrict__ q_new, const bf16* __restrict__ k_new,
     const bf16* __restrict__ v_new, bf16* __restrict__ q_win, bf16* __restrict__ k_cache,
     bf16* __restrict__ v_cache, int Hq, int Hkv, int r, int W, int pos, int ldk) {
-  __shared__ bf16 win[128 * D];
+  __shared__ __attribute__((aligned(16))) bf16 win[128 * D];
   const int bh = blockIdx.x, b = bh / Hq, h = bh % Hq, g = h / r;
   const int tid = threadIdx.x;
   bf16* wrow = q_win + (size_t)bh * W * D;
-  for (int i = tid; i < (W - 1) * D; i += 256) win[i] = wrow[D + i];
+  // rows 1 .. W-1 move down one row, staged through LDS (the ranges
+  // overlap), in 16-byte pieces (D is a multiple of 8)
+  const int nv = (W - 1) * D / 8;
+  for (int i = tid; i < nv; i += 256) store8(win + 8 * i, load8(wrow + D + 8 * i));
   __syncthreads();
-  for (int i = tid; i < (W - 1) * D; i += 256) wrow[i] = win[i];
+  for (int i = tid; i < nv; i += 256) store8(wrow + 8 * i, load8(win + 8 * i));
   for (int d = tid; d < D; d += 256) wrow[(size_t)(W - 1) * D + d] = q_new[(size_t)bh * D + d];
   if (h % r == 0) {
     const size_t bg = (size_t)b * Hkv + g;
@@ -1890,6 +1893,23 @@ __global__ __launch_bounds__(256) void page_max_kernel(const float* __restrict__
   if (i >= NP) return;
   const float* src = sc + (size_t)row * L;
   const int lo = i * S, hi = min(L, lo + S);
+  if ((S & 3) == 0 && (L & 3) == 0 && (reinterpret_cast<uintptr_t>(sc) & 15) == 0) {
+    // 16-byte loads, eight in flight (the page and the row start 16-byte
+    // aligned); clamped repeats do not change the maximum
+    const floatx4* v4 = reinterpret_cast<const floatx4*>(src + lo);
+    const int n4 = (hi - lo) / 4;
+    float m = -INFINITY;
+    for (int q0 = 0; q0 < n4; q0 += 8) {
+      floatx4 v[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = v4[min(q0 + j, n4 - 1)];
+#pragma unroll
+      for (int j = 0; j < 8; ++j)
+        m = fmaxf(fmaxf(m, fmaxf(v[j][0], v[j][1])), fmaxf(v[j][2], v[j][3]));
+    }
+    I[(size_t)row * NP + i] = m;
+    return;
+  }
   // eight loads in flight; clamped repeats do not change the maximum
   float m = src[lo];
   for (int t0 = lo + 1; t0 < hi; t0 += 8) {
