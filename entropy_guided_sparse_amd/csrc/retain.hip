@@ -1142,41 +1142,67 @@ __global__ __launch_bounds__(256) void decode_attn_split_kernel(
 }
 
 template <int D>
-__global__ __launch_bounds__(64) void decode_attn_combine_kernel(const float* __restrict__ part,
-                                                                 int nsplit, bf16* __restrict__ out) {
+__global__ __launch_bounds__(256) void decode_attn_combine_kernel(const float* __restrict__ part,
+                                                                  int nsplit, bf16* __restrict__ out) {
   constexpr int DPL = D / 64;
-  const int bh = blockIdx.x, lane = threadIdx.x;
+  constexpr int NB = 8;   // splits per round, their loads issued together
+  __shared__ float wm[4], wl[4], wo[4][D];
+  const int bh = blockIdx.x, lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const float* pp = part + (size_t)bh * nsplit * (D + 2);
-  // the splits' maxima, one per lane and round
+  // wave w folds the splits of quarter w against that quarter's maximum
+  const int qn = (nsplit + 3) / 4;
+  const int s_lo = min(nsplit, w * qn), s_hi = min(nsplit, s_lo + qn);
   float M = kNegBig;
-  for (int s0 = 0; s0 < nsplit; s0 += 64)
-    M = fmaxf(M, wave_max(s0 + lane < nsplit ? pp[(size_t)(s0 + lane) * (D + 2) + D] : kNegBig));
+  for (int s0 = s_lo; s0 < s_hi; s0 += 64)
+    M = fmaxf(M, wave_max(s0 + lane < s_hi ? pp[(size_t)(s0 + lane) * (D + 2) + D] : kNegBig));
   float Lr = 0.f, o[DPL];
 #pragma unroll
   for (int e = 0; e < DPL; ++e) o[e] = 0.f;
-  // four splits per round, their loads issued together (index clamped)
-  for (int s0 = 0; s0 < nsplit; s0 += 4) {
-    float sm[4], sl[4], so[4][DPL];
+  for (int s0 = s_lo; s0 < s_hi; s0 += NB) {
+    float sm[NB], sl[NB], so[NB][DPL];
 #pragma unroll
-    for (int j = 0; j < 4; ++j) {
-      const float* q = pp + (size_t)min(s0 + j, nsplit - 1) * (D + 2);
+    for (int j = 0; j < NB; ++j) {
+      const float* q = pp + (size_t)min(s0 + j, s_hi - 1) * (D + 2);   // clamped
       sm[j] = q[D];
       sl[j] = q[D + 1];
 #pragma unroll
       for (int e = 0; e < DPL; ++e) so[j][e] = q[lane * DPL + e];
     }
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      if (s0 + j < nsplit) {
+    for (int j = 0; j < NB; ++j)
+      if (s0 + j < s_hi) {
         const float f = fast_exp2(sm[j] - M);
         Lr += sl[j] * f;
 #pragma unroll
         for (int e = 0; e < DPL; ++e) o[e] += so[j][e] * f;
       }
   }
-  const float inv = 1.0f / Lr;
+  if (lane == 0) {
+    wm[w] = M;
+    wl[w] = Lr;
+  }
 #pragma unroll
-  for (int e = 0; e < DPL; ++e) out[(size_t)bh * D + lane * DPL + e] = f2bf(o[e] * inv);
+  for (int e = 0; e < DPL; ++e) wo[w][lane * DPL + e] = o[e];
+  __syncthreads();
+  if (w == 0) {
+    // the four quarters in order (an empty quarter holds kNegBig, 0)
+    float Mt = wm[0];
+#pragma unroll
+    for (int v = 1; v < 4; ++v) Mt = fmaxf(Mt, wm[v]);
+    float Lt = 0.f, ot[DPL];
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) ot[e] = 0.f;
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const float f = fast_exp2(wm[v] - Mt);
+      Lt += wl[v] * f;
+#pragma unroll
+      for (int e = 0; e < DPL; ++e) ot[e] += wo[v][lane * DPL + e] * f;
+    }
+    const float inv = 1.0f / Lt;
+#pragma unroll
+    for (int e = 0; e < DPL; ++e) out[(size_t)bh * D + lane * DPL + e] = f2bf(ot[e] * inv);
+  }
 }
 
 // Split size: the largest multiple of 64 in [DA_SPL_MIN, DA_SPL_MAX] whose
@@ -1228,10 +1254,10 @@ hipError_t launch_decode_attn(const DecodeDims& p, const void* q_new, const void
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   if (p.D == 128)
-    decode_attn_combine_kernel<128><<<p.B * p.Hq, 64, 0, st>>>(part, nsplit,
+    decode_attn_combine_kernel<128><<<p.B * p.Hq, 256, 0, st>>>(part, nsplit,
                                                                static_cast<bf16*>(out));
   else
-    decode_attn_combine_kernel<64><<<p.B * p.Hq, 64, 0, st>>>(part, nsplit,
+    decode_attn_combine_kernel<64><<<p.B * p.Hq, 256, 0, st>>>(part, nsplit,
                                                               static_cast<bf16*>(out));
   return hipGetLastError();
 }
