@@ -108,7 +108,15 @@ __global__ __launch_bounds__(256) void select_kernel(const float* __restrict__ s
   k = max(0, min(k, min(cb, k_max)));
   const float* row = scores + (size_t)hs * CB;
   int32_t* out = idx + (size_t)hs * k_max;
-  for (int j = tid; j < cb; j += 256) keys[j] = orderable(row[j]);
+  // four loads per thread per round, issued together (index clamped)
+  for (int j0 = 0; j0 < cb; j0 += 1024) {
+    float v[4];
+#pragma unroll
+    for (int u = 0; u < 4; ++u) v[u] = row[min(j0 + u * 256 + tid, cb - 1)];
+#pragma unroll
+    for (int u = 0; u < 4; ++u)
+      if (j0 + u * 256 + tid < cb) keys[j0 + u * 256 + tid] = orderable(v[u]);
+  }
   __syncthreads();
 
   uint32_t prefix = 0, mask = 0;
