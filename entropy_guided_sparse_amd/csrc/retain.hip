@@ -190,7 +190,6 @@ __global__ __launch_bounds__(256) void obs_pass_kernel(
   constexpr int NC = D / 16;
   constexpr int PW = KPipe<D>::PER_W;
   __shared__ __attribute__((aligned(1024))) bf16 Ks[RT_DEPTH][RT_KT * D];
-  __shared__ float mbuf[MASS ? 4 * RT_CK : 1];
   __shared__ int cs[SEG ? RT_CK : 1];
   const int span = blockIdx.x, bg = blockIdx.y;
   const int b = bg / Hkv, g = bg % Hkv;
@@ -385,7 +384,7 @@ __global__ __launch_bounds__(256) void obs_pass_kernel(
         colsum = xhalf_sum(colsum);
         if (hg == 0 && t < t_end) {
           const float a = colsum * invW;
-          mbuf[w * RT_CK + (t - t_begin)] = a;
+          mass[((size_t)b * Hq + h) * L + t] = a;
           if (t >= n_sink && a > 0.f) {
             s1 += a;
             // one v_log_f32: a ln a, or a^alpha = 2^(alpha log2 a)
@@ -430,12 +429,6 @@ __global__ __launch_bounds__(256) void obs_pass_kernel(
       }
     }
   } else {
-    // this wave's own masses: written and read by the same wavefront
-    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
-    __builtin_amdgcn_wave_barrier();
-    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
-    float* mrow = mass + ((size_t)b * Hq + h) * L;
-    for (int t = t_begin + lane; t < t_end; t += 64) mrow[t] = mbuf[w * RT_CK + (t - t_begin)];
     s1 = wave_sum(s1);
     s2 = wave_sum(s2);
     if (lane == 0) {
