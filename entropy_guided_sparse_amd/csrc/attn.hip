@@ -42,7 +42,7 @@ namespace egs {
 
 constexpr int AT_KT = 64;     // keys per LDS stage and per V^T tile
 constexpr int AT_LCAP = 512;  // block-list entries staged in LDS at a time
-constexpr int PV_AHEAD = 3;   // V^T fragments read ahead of their MFMA
+constexpr int PV_AHEAD = 4;   // V^T fragments read ahead of their MFMA
 
 // The compiler schedules nothing across this point.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
