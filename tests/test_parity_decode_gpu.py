@@ -204,3 +204,34 @@ def test_retain_all_scores_tied(api):
     o_keep, o_mu, _ = O.kv_retain_slice(synth.bf16_bits_to_f32(q_obs)[0], np.zeros((L, d)),
                                         n_sink, n_recent, n_keep)
     np.testing.assert_array_equal(o_keep, want)
+
+
+# The launcher splits the kept entries into pieces of 192 to 512 entries, the
+# size chosen from n_total and batch x KV groups (64 here); these n_total reach
+# every size it can pick: 1 and 4000 -> 512, 193 -> 192, 257 -> 256, 321 -> 320,
+# 2561 -> 384, 3137 -> 448.
+@pytest.mark.parametrize("n_total", [1, 193, 257, 321, 2561, 3137, 4000])
+def test_decode_attention_every_split_size(api, n_total):
+    B, Hq, Hkv, d = 8, 32, 8, 128
+    log(f"[decode attention splits] B={B} Hq={Hq} Hkv={Hkv} d={d} n_total={n_total}")
+    rng = np.random.default_rng(1000 + n_total)
+    qb = synth.round_to_bf16(rng.standard_normal((B, Hq, d)).astype(np.float32))
+    kb = synth.round_to_bf16(rng.standard_normal((B, Hkv, n_total, d)).astype(np.float32))
+    vb = synth.round_to_bf16(rng.standard_normal((B, Hkv, n_total, d)).astype(np.float32))
+    # a few entries with large logits so that each head's softmax is peaked
+    kf = synth.bf16_bits_to_f32(kb).copy()
+    qf = synth.bf16_bits_to_f32(qb)
+    for b in range(B):
+        for g in range(Hkv):
+            t = int(rng.integers(n_total))
+            kf[b, g, t] += 3.0 * qf[b, g * (Hq // Hkv)]
+    kb = synth.round_to_bf16(kf)
+    shape = api.DecodeShape(B, Hq, Hkv, d, max(n_total, 1), 1, 0, 0, 0)
+    out = api.sparse_decode_attn(shape, dev_tensor(qb, "bf16"), dev_tensor(kb, "bf16"),
+                                 dev_tensor(vb, "bf16"))
+    torch.cuda.synchronize()
+    ref = O.sparse_decode_attn(synth.bf16_bits_to_f32(qb), synth.bf16_bits_to_f32(kb),
+                               synth.bf16_bits_to_f32(vb))
+    ma, rel = attn_errors(out.float().cpu().numpy(), ref)
+    log(f"  max|d|={ma:.3e} relL2={rel:.3e}")
+    assert ma <= ATTN_MAX_ABS and rel <= ATTN_REL_L2
