@@ -157,3 +157,45 @@ def test_streaming_paths_agree_with_the_stacked_rows():
     z[T - W + u + 1:] = -np.inf
     p = np.exp(z - z.max())
     np.testing.assert_allclose(A[4, u], p / p.sum(), atol=1e-15)
+
+
+def test_priorities_hand_example_with_smoothing():
+    # EntroPrefill Sec. 3.2 worked by hand (reading: p is mu on the candidate
+    # tokens renormalised, uniform null pi_i = n_i / N).
+    # mu = (0.2, 0.4, 0.24, 0.08, 0.08), candidates c_0 = {1, 2}, c_1 = {3, 4}:
+    # Z = 0.8, p = (0.5, 0.3 | 0.1, 0.1), N = 4, n = (2, 2), pi = (1/2, 1/2),
+    # M = (0.8, 0.2).  With eps_s = 0.1, eps_s pi_i / n_i = 0.025 and
+    # eps_s pi_i = 0.05:
+    #   chunk 0: p_hat = (0.525, 0.325) / 0.85 = (21/34, 13/34),
+    #            l = 0.85 / (1.1 * 0.5) = 17/11, sum p_hat^2 = 610/1156,
+    #            kappa = ln(610/1156) / ln 2;
+    #   chunk 1: p_hat = (1/2, 1/2), l = 0.25 / 0.55 = 5/11, kappa = -1.
+    # Without smoothing chunk 0 would have p_hat = (5/8, 3/8) and l = 8/5.
+    mu = np.array([0.2, 0.4, 0.24, 0.08, 0.08])
+    chunks = [(1, 3), (3, 5)]
+    lam = 0.5
+    S, ell, kap, M = O.prune_priorities(mu, chunks, eps_s=0.1, lam=lam)
+    k0 = math.log(610 / 1156) / math.log(2.0)
+    np.testing.assert_allclose(M, [0.8, 0.2], atol=1e-15)
+    np.testing.assert_allclose(ell, [17 / 11, 5 / 11], atol=1e-15)
+    np.testing.assert_allclose(kap, [k0, -1.0], atol=1e-15)
+    np.testing.assert_allclose(S, [math.log(17 / 11) + lam * k0, math.log(5 / 11) - lam],
+                               atol=1e-15)
+
+
+def test_priorities_hand_example_unequal_chunks():
+    # A one-token chunk beside a three-token chunk (kappa = 0 for n = 1):
+    # mu = (0.6, 0.1, 0.2, 0.1) all candidates, c_0 = {0}, c_1 = {1, 2, 3};
+    # N = 4, pi = (1/4, 3/4), M = (0.6, 0.4).  eps_s = 0.2:
+    #   chunk 0: l = (0.6 + 0.05) / (1.2 * 0.25) = 13/6, S = ln(13/6);
+    #   chunk 1: eps_s pi_1 = 0.15, per token 0.05;
+    #            p_hat = (0.15, 0.25, 0.15) / 0.55 = (3, 5, 3)/11,
+    #            l = 0.55 / (1.2 * 0.75) = 11/18, sum p_hat^2 = 43/121,
+    #            kappa = ln(43/121) / ln 3.
+    mu = np.array([0.6, 0.1, 0.2, 0.1])
+    S, ell, kap, M = O.prune_priorities(mu, [(0, 1), (1, 4)], eps_s=0.2, lam=2.0)
+    k1 = math.log(43 / 121) / math.log(3.0)
+    np.testing.assert_allclose(M, [0.6, 0.4], atol=1e-15)
+    np.testing.assert_allclose(ell, [13 / 6, 11 / 18], atol=1e-15)
+    np.testing.assert_allclose(kap, [0.0, k1], atol=1e-15)
+    np.testing.assert_allclose(S, [math.log(13 / 6), math.log(11 / 18) + 2.0 * k1], atol=1e-15)

@@ -125,3 +125,62 @@ def test_decode_attention_keep_all_is_dense_sdpa():
         torch.from_numpy(qn)[:, :, None], torch.from_numpy(np.repeat(kk, 2, axis=1)),
         torch.from_numpy(np.repeat(vv, 2, axis=1)))[:, :, 0].numpy()
     np.testing.assert_allclose(o, ref, atol=1e-13)
+
+
+def test_head_weights_hand_examples():
+    # EntroPrefill Sec. 3.1 head weights worked by hand.  r = 2, zeta = 1/2.
+    # tau = 1, H = (0, ln 2): v = (1, 1/2) / (3/2) = (2/3, 1/3), so
+    # w = 1/4 + (1/2)(2/3, 1/3) = (7/12, 5/12).
+    np.testing.assert_allclose(O.head_weights([0.0, math.log(2.0)], 0.5, 1.0),
+                               [7 / 12, 5 / 12], atol=1e-15)
+    # tau = 2, H = (0, ln 4): the temperature divides, exp(-ln 4 / 2) = 1/2,
+    # so v and w are again (2/3, 1/3) and (7/12, 5/12).  (Multiplying by tau
+    # would give v = (16/17, 1/17); a positive sign would favour head 1.)
+    np.testing.assert_allclose(O.head_weights([0.0, math.log(4.0)], 0.5, 2.0),
+                               [7 / 12, 5 / 12], atol=1e-15)
+    # r = 4, zeta = 0.2, tau = 1/2, H = (ln 3, 0, ln 3, ln 3) / 2:
+    # exp(-H / tau) = (1/3, 1, 1/3, 1/3), sum 2, v = (1/6, 1/2, 1/6, 1/6),
+    # w = 0.05 + 0.8 v = (11/60, 9/20, 11/60, 11/60).
+    h3 = math.log(3.0) / 2
+    np.testing.assert_allclose(O.head_weights([h3, 0.0, h3, h3], 0.2, 0.5),
+                               [11 / 60, 9 / 20, 11 / 60, 11 / 60], atol=1e-15)
+
+
+def test_head_weight_lower_bound_of_sec_3_1():
+    # EntroPrefill Sec. 3.1: a head whose entropy lies at least Delta below each
+    # of its s - 1 siblings gets w >= zeta/r + (1 - zeta)/(1 + (s - 1) e^{-Delta/tau})
+    # (divide the denominator of its softmax weight by its own term; every
+    # sibling's term is then at most e^{-Delta/tau}).  Equality holds when every
+    # sibling sits exactly Delta above it.
+    rng = np.random.default_rng(11)
+    for _ in range(300):
+        r = int(rng.integers(2, 9))
+        zeta = float(rng.uniform(0.0, 1.0))
+        tau = float(rng.uniform(0.1, 5.0))
+        delta = float(rng.uniform(0.0, 3.0))
+        hs = int(rng.integers(0, r))
+        Hs = float(rng.uniform(0.0, 4.0))
+        H = Hs + delta + rng.exponential(1.0, r) * (rng.random() < 0.7)
+        H[hs] = Hs
+        bound = zeta / r + (1 - zeta) / (1 + (r - 1) * math.exp(-delta / tau))
+        w = O.head_weights(H, zeta, tau)
+        assert w[hs] >= bound - 1e-13
+        H_eq = np.full(r, Hs + delta)
+        H_eq[hs] = Hs
+        assert abs(O.head_weights(H_eq, zeta, tau)[hs] - bound) < 1e-13
+
+
+def test_head_weights_high_temperature_limit():
+    # As tau grows the tempered softmax flattens: w -> 1/r for any entropies
+    # (|w_h - 1/r| <= (1 - zeta) (e^{spread/tau} - 1) for spread = max H - min H).
+    rng = np.random.default_rng(12)
+    for r in (2, 4, 7):
+        H = rng.uniform(0.0, 6.0, r)
+        spread = float(H.max() - H.min())
+        for tau in (1e3, 1e6):
+            w = O.head_weights(H, 0.3, tau)
+            assert np.all(np.abs(w - 1.0 / r) <= 0.7 * math.expm1(spread / tau) + 1e-15)
+        # and at small tau all the non-floor weight goes to the lowest entropy
+        w = O.head_weights(H, 0.3, 1e-3)
+        lo = int(np.argmin(H))
+        np.testing.assert_allclose(w, 0.3 / r + 0.7 * (np.arange(r) == lo), atol=1e-12)
