@@ -547,6 +547,8 @@ egs_status egs_latent_decode_step(const egs_decode_shape* shape, const egs_retai
                                            len, cap, stream);
   if (e != hipSuccess) return hip_status(e, "latent append launch");
   const int n = len + 1;
+  if (egs::decode_attn_workspace_bytes(p, n) > ly.retain - ly.attn)
+    return fail(EGS_EWORKSPACE, "internal: decode partials for %d entries exceed their region", n);
   e = egs::launch_decode_attn(p, q_new, k_cache, v_cache, n, cap, out, w + ly.attn, stream);
   if (e != hipSuccess) return hip_status(e, "latent decode attention launch");
   const int gen = state->generated + 1;

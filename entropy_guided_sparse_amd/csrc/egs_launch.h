@@ -107,6 +107,7 @@ hipError_t launch_kv_retain(const DecodeDims& p, const egs_retain_params& prm,
 // K8: decode attention over the first n_total entries of every (batch, KV
 // group) row of k / v, rows ldk entries apart (split over the kept range).
 size_t decode_attn_workspace_bytes(const DecodeDims& p, int n_total);
+size_t decode_attn_workspace_bytes_upto(const DecodeDims& p, int cap);
 hipError_t launch_decode_attn(const DecodeDims& p, const void* q_new, const void* k,
                               const void* v, int n_total, int ldk, void* out, void* ws,
                               hipStream_t st);

@@ -1227,6 +1227,14 @@ size_t decode_attn_workspace_bytes(const DecodeDims& p, int n_total) {
   return align_up((size_t)p.B * p.Hq * nsplit * (p.D + 2) * 4);
 }
 
+// The split count is not monotone in n (a shorter list can take a smaller
+// split), so a buffer reused for every length up to `cap` is sized for the
+// smallest split the launcher can choose: ceil(cap / DA_SPL_MIN) partials.
+size_t decode_attn_workspace_bytes_upto(const DecodeDims& p, int cap) {
+  const int nsplit = (cap + DA_SPL_MIN - 1) / DA_SPL_MIN;
+  return align_up((size_t)p.B * p.Hq * nsplit * (p.D + 2) * 4);
+}
+
 hipError_t launch_decode_attn(const DecodeDims& p, const void* q_new, const void* k,
                               const void* v, int n_total, int ldk, void* out, void* ws,
                               hipStream_t st) {
@@ -1829,7 +1837,7 @@ LatentLayout latent_layout(const DecodeDims& p) {
     off += align_up(bytes);
     return at;
   };
-  o.attn = take(decode_attn_workspace_bytes(p, p.L));
+  o.attn = take(decode_attn_workspace_bytes_upto(p, p.L));
   o.retain = take(retain_workspace_bytes(p));
   o.keep = take((size_t)p.B * p.Hkv * o.ntot_max * sizeof(int32_t));
   o.ks = take((size_t)p.B * p.Hkv * o.ntot_max * p.D * sizeof(bf16));

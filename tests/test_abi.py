@@ -309,3 +309,21 @@ def test_prune_certificate_errors(L):
     assert call(m0=-1) == L.EGS_EINVAL
     assert call(mass=None) == L.EGS_EINVAL
     assert call(wsb=ws - 1) == L.EGS_EWORKSPACE
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,cap", [(8, 32, 8, 8192), (1, 4, 1, 131136), (2, 8, 2, 2218)])
+def test_latent_workspace_holds_every_length(L, B, Hq, Hkv, cap):
+    # A latent step runs decode attention over n = length + 1 <= capacity
+    # entries with the split the launcher picks for n, which is not monotone in
+    # n.  The step's workspace must hold the partials of every such n on top of
+    # the retention scratch and the kept rows (regions are laid out back to back).
+    sc = _dshape(L, batch=B, n_q_heads=Hq, n_kv_heads=Hkv, cache_len=cap, n_obs=64, n_sink=4,
+                 n_recent=256, n_keep=4096)
+    total = L.LIB.egs_latent_decode_workspace(ctypes.byref(sc))
+    assert total > 0
+    ntot = min(cap, 4 + 256 + 4096)
+    rest = (L.LIB.egs_kv_retain_workspace(ctypes.byref(sc))
+            + B * Hkv * ntot * (4 + 2 * 2 * sc.head_dim))
+    worst = max(L.LIB.egs_sparse_decode_attn_workspace(ctypes.byref(sc), n)
+                for n in range(64, cap + 1))
+    assert worst + rest <= total

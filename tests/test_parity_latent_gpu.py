@@ -29,14 +29,25 @@ def _bf16(x):
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).bfloat16()
 
 
-@pytest.mark.parametrize("n_delay,interval,T", [(96, 64, 170), (10, 0, 40)])
-def test_latent_decode_loop(api, n_delay, interval, T):
+# (B, Hq, Hkv, prompt length, spare capacity, n_keep, N_D, interval, tokens).
+# The batch-8 case runs near 4,480 entries in an 8,192-row cache: there the
+# attention split the launcher picks (192 entries, 24 splits per row) yields
+# more partials than the cache's full length would (512, 16 splits), so the
+# step's workspace must be sized for every length up to the capacity.
+CASES = [(2, 8, 2, 2048, 0, 512, 96, 64, 170),
+         (2, 8, 2, 2048, 0, 512, 10, 0, 40),
+         (8, 32, 8, 4466, 8192 - 4466 - 24, 4096, 16, 0, 24)]
+
+
+@pytest.mark.parametrize("B,Hq,Hkv,L0,spare,n_keep,n_delay,interval,T", CASES)
+def test_latent_decode_loop(api, B, Hq, Hkv, L0, spare, n_keep, n_delay, interval, T):
     L_ = api.L
-    B, Hq, Hkv, d, L0, W = 2, 8, 2, 128, 2048, 64
-    n_sink, n_recent, n_keep = 4, 256, 512
+    d, W = 128, 64
+    n_sink, n_recent = 4, 256
     cfg = synth.DecodeConfig("latent", B, Hq, Hkv, d, L0, W, n_sink, n_recent, n_keep)
     inp = synth.make_decode(cfg, seed=5)
-    log(f"[latent] B={B} Hq={Hq} L0={L0} T={T} n_delay={n_delay} interval={interval}")
+    log(f"[latent] B={B} Hq={Hq} L0={L0} cap={L0 + T + spare} T={T} n_delay={n_delay} "
+        f"interval={interval}")
     rng = np.random.default_rng(6)
     # generated tokens: Gaussian, with queries drawn towards random prompt keys
     steps = []
@@ -49,7 +60,7 @@ def test_latent_decode_loop(api, n_delay, interval, T):
         k = rng.standard_normal((B, Hkv, d))
         v = rng.standard_normal((B, Hkv, d))
         steps.append(tuple(_bf16(x) for x in (q, k, v)))
-    C = L0 + T
+    C = L0 + T + spare
     shape = api.DecodeShape(B, Hq, Hkv, d, C, W, n_sink, n_recent, n_keep)
     prm = api.RetainParams(entropy_kind=L_.EGS_SHANNON, zeta=0.5, tau=1.0)
     k_cache = torch.zeros((B, Hkv, C, d), dtype=torch.bfloat16, device="cuda")

@@ -324,3 +324,22 @@ def test_maxmin_observation_rows(api, case):
         cfg = synth.small_prefill_config(**kw)
     kind = api.L.EGS_RENYI if case.endswith("renyi") else api.L.EGS_SHANNON
     run_maxmin(api, cfg, seed=7, kind=kind)
+
+
+@pytest.mark.parametrize("LB,N,LS", [(64, 65536, 8192), (128, 131072, 16384)])
+def test_mfma_lists_longer_than_one_lds_stage(api, LB, N, LS):
+    # FIXED 60% of the causal blocks: the last segment lists 615 of its 1,024
+    # blocks and the one before it 538 of 896, more than the 512 entries the
+    # MFMA attention kernel stages in LDS at a time, so every query block of
+    # those segments walks its list across a refill (EntropyInfer Alg. 3 lets
+    # budgets reach 3 B_h, App. A eq. (3)).  Sampled query blocks of both
+    # segments, every head, against the oracle on the GPU's lists.
+    cfg = synth.small_prefill_config(name="long-lists", n_q_heads=4, n_kv_heads=2,
+                                     head_dim=128, seq_len=N, block_size=LB, segment_size=LS,
+                                     probe_len=64)
+    CB, bps = N // LB, LS // LB
+    blocks = [(h, b) for h in range(4)
+              for b in (CB - 1, CB - bps, CB - bps // 2, CB - bps - 1)]
+    res = run_pipeline(api, cfg, _policy(api, api.L.EGS_BUDGET_FIXED, frac=0.6), seed=4,
+                       attn_blocks=blocks)
+    assert res["cnt"][:, -1].min() == 615 and res["cnt"][:, -2].min() == 538

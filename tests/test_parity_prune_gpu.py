@@ -2,7 +2,9 @@
 C ABI: row-chunk masses and priorities against the oracle's float64 values,
 and the removal decisions bit-exact against the oracle's greedy proposer run
 on the GPU's own float32 priorities and masses, in float32 (floating point
-decides the integer outputs, so both sides decide in the same precision)."""
+decides the integer outputs, so both sides decide in the same precision);
+and against the oracle's own float64 priorities and masses under a band rule
+(the scan order and every decision equal unless within a rounding band)."""
 import numpy as np
 import pytest
 import torch
@@ -20,6 +22,19 @@ def api():
         pytest.skip("no HIP device")
     from entropy_guided_sparse_amd import api as A
     return A
+
+
+# Priorities: S = ln l + lambda kappa of float32 chunk sums of the pooled
+# measure; measured within 3e-6 of the oracle's float64 values.  5e-5 keeps
+# ~15x margin over that and stays below the 1e-4 band in which the scan order
+# of two chunks may swap.
+PRIO_ATOL = 5e-5
+# Scan decisions are compared with the oracle's own float64 values: two chunks
+# may be scanned in either order when their priorities lie within ORDER_BAND,
+# and a decision may go either way when a row sum lands within MASS_BAND of
+# its budget (row masses are float32 sums, measured within 3e-6).
+ORDER_BAND = 1e-4
+MASS_BAND = 5e-5
 
 
 def _chunks(rng, T, W, k, lo=64):
@@ -51,16 +66,55 @@ def _run(api, Hq, Hkv, T, W, chunks, eps_s, lam, eps, m0, target, seed=0, n_sink
     log(f"  row mass max|d|={dm:.3e} priority max|d|={dS:.3e} removed={int(g_rem.sum())} "
         f"tokens={g_tok}")
     assert dm <= 1e-4
-    assert dS <= 2e-3
+    assert dS <= PRIO_ATOL
     n = np.array([e - b for (b, e) in chunks])
     o_rem, o_tok = O.prune_greedy(g_S.astype(np.float64), n, g_m.T, eps, m0, target,
                                   dtype=np.float32)
     np.testing.assert_array_equal(g_rem, o_rem)
     assert g_tok == o_tok
+    _oracle_scan_agrees(r_S, n, r_m, eps, m0, target, g_rem, g_S)
     # feasibility of the GPU's set on the oracle's own masses (within rounding)
     assert np.all(r_m[:, g_rem].sum(axis=1) <= eps + 1e-4)
     assert g_rem.sum() <= max(len(chunks) - m0, 0)
     return g_rem, g_tok
+
+
+def _oracle_scan_agrees(S, n, m, eps, m0, target, g_rem, g_S):
+    """Band rule for the greedy scan against the oracle's own float64 values.
+
+    Order: the GPU's scan order (its priorities, ties by larger n, then index)
+    may invert two chunks only where the oracle's priorities lie within
+    ORDER_BAND.  Decisions: walking that order with the oracle's float64 row
+    masses, every decision must equal the oracle's, except where a row sum
+    after adding the chunk lies within MASS_BAND of eps; there the walk takes
+    the GPU's decision and goes on.  Returns the number of such steps."""
+    S = np.asarray(S, dtype=np.float64)
+    m = np.asarray(m, dtype=np.float64)
+    k = len(S)
+    order = sorted(range(k), key=lambda i: (float(g_S[i]), -int(n[i]), i))
+    So = S[order]
+    # no inversion beyond the band: every later chunk's oracle priority is at
+    # least the running maximum so far minus the band
+    assert np.all(So >= np.maximum.accumulate(So) - ORDER_BAND), "scan order inverted"
+    cur = np.zeros(m.shape[0])
+    tokens = count = 0
+    near = 0
+    for p, i in enumerate(order):
+        if tokens >= target or count + 1 > k - m0:
+            assert not g_rem[order[p:]].any(), ("removed after the scan stopped", p)
+            break
+        nxt = cur + m[:, i]
+        take = bool(np.all(nxt <= eps))
+        if np.any(np.abs(nxt - eps) <= MASS_BAND):
+            near += 1
+            take = bool(g_rem[i])
+        assert g_rem[i] == take, ("scan step", p, "chunk", i)
+        if take:
+            cur = nxt
+            tokens += int(n[i])
+            count += 1
+    log(f"  oracle float64 scan: all {k} decisions equal ({near} within the mass band)")
+    return near
 
 
 @pytest.mark.parametrize("case", ["basic", "tight_rows", "loose_rows", "count_bound",
@@ -141,12 +195,19 @@ def test_chunk_prune_full_context(api):
         dm = max(dm, float(np.abs(g_m[h * W:(h + 1) * W] - r_m).max()))
     log(f"  priority max|d|={dS:.3e} sampled row mass max|d|={dm:.3e} "
         f"removed={int(g_rem.sum())} tokens={g_tok}")
-    assert dS <= 2e-3 and dm <= 1e-4
+    assert dS <= PRIO_ATOL and dm <= 1e-4
     n = chunks[:, 1] - chunks[:, 0]
     o_rem, o_tok = O.prune_greedy(g_S.astype(np.float64), n, g_m, eps, m0, target,
                                   dtype=np.float32)
     np.testing.assert_array_equal(g_rem, o_rem)
     assert g_tok == o_tok == int(n[g_rem].sum())
+    # the oracle's own decisions need every row's masses; they are formed here
+    # head by head from the oracle's rows (the GPU's masses are not used)
+    r_all = np.concatenate([O.prune_row_chunk_mass(O.prune_head_rows(inp.q_obs[0], inp.k[0],
+                                                                     h)[None], cl)
+                            for h in range(Hq)], axis=0)
+    assert float(np.abs(g_m - r_all).max()) <= 1e-4
+    _oracle_scan_agrees(r_S, n, r_all, eps, m0, target, g_rem, g_S)
     assert np.all(g_m[:, g_rem].astype(np.float64).sum(axis=1) <= eps + 1e-5)
     # chunks never hold more than a row's whole mass (protected tokens hold the rest)
     assert np.all(g_m.astype(np.float64).sum(axis=1) <= 1.0 + 1e-4)
