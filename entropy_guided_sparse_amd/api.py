@@ -163,6 +163,30 @@ def entropy_score(shape: PrefillShape, q: torch.Tensor, k: torch.Tensor, kind: i
     return block_scores, entropy
 
 
+def entropy_score_static(shape: PrefillShape, q: torch.Tensor, k: torch.Tensor,
+                         kind: int = L.EGS_SHANNON, renyi_alpha: float = 2.0,
+                         pool: int = L.EGS_POOL_MEAN_PROBE,
+                         block_scores: Optional[torch.Tensor] = None,
+                         entropy: Optional[torch.Tensor] = None):
+    """entropy_score on the library's static device scratch (no workspace);
+    the outputs are allocated here unless passed in."""
+    s = shape
+    dev = q.device
+    _need(q, "q", (s.n_q_heads, s.seq_len, s.head_dim), s.dtype)
+    _need(k, "k", (s.n_kv_heads, s.seq_len, s.head_dim), s.dtype, dev)
+    sc = s.c()
+    if block_scores is None:
+        block_scores = _empty((s.n_q_heads, s.n_segments, s.n_blocks), torch.float32, dev)
+    if entropy is None:
+        entropy = _empty((s.n_q_heads, s.n_segments), torch.float32, dev)
+    _need(block_scores, "block_scores", (s.n_q_heads, s.n_segments, s.n_blocks), torch.float32, dev)
+    _need(entropy, "entropy", (s.n_q_heads, s.n_segments), torch.float32, dev)
+    L.check(L.LIB.egs_entropy_score_static(ctypes.byref(sc), pool, kind, renyi_alpha, _ptr(q),
+                                           _ptr(k), _ptr(block_scores), _ptr(entropy),
+                                           _stream(dev)))
+    return block_scores, entropy
+
+
 def allocate_budget(shape: PrefillShape, policy: BudgetPolicy, entropy: torch.Tensor,
                     head_is_rigid: Optional[torch.Tensor] = None,
                     budget: Optional[torch.Tensor] = None):

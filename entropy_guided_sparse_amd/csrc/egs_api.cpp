@@ -168,27 +168,39 @@ size_t egs_entropy_score_workspace(const egs_prefill_shape* shape) {
   return egs::score_workspace_bytes(p);
 }
 
+// argument checks shared by egs_entropy_score and its static-scratch form;
+// a Renyi order of 1 is Shannon
+static egs_status check_score(const egs_prefill_shape* shape, int32_t pool_kind,
+                              int32_t entropy_kind, float renyi_alpha, const void* q,
+                              const void* k, const float* block_scores, const float* entropy,
+                              PrefillDims* p, int* kind) {
+  egs_status st = check_prefill(shape, p);
+  if (st != EGS_OK) return st;
+  if (pool_kind != EGS_POOL_MEAN_PROBE && pool_kind != EGS_POOL_MAXMIN)
+    return fail(EGS_EINVAL, "unknown pool_kind %d", pool_kind);
+  *kind = entropy_kind;
+  if (*kind != EGS_SHANNON && *kind != EGS_RENYI)
+    return fail(EGS_EINVAL, "unknown entropy_kind %d", entropy_kind);
+  if (*kind == EGS_RENYI) {
+    if (!(std::isfinite(renyi_alpha) && renyi_alpha > 0.f))
+      return fail(EGS_EINVAL, "renyi_alpha must be finite and > 0");
+    if (renyi_alpha == 1.0f) *kind = EGS_SHANNON;
+  }
+  if ((st = need(q, "q", 16)) != EGS_OK) return st;
+  if ((st = need(k, "k", 16)) != EGS_OK) return st;
+  if ((st = need(block_scores, "block_scores", 4)) != EGS_OK) return st;
+  return need(entropy, "entropy", 4);
+}
+
 egs_status egs_entropy_score(const egs_prefill_shape* shape, int32_t pool_kind,
                              int32_t entropy_kind, float renyi_alpha, const void* q,
                              const void* k, float* block_scores, float* entropy,
                              void* workspace, size_t workspace_bytes, hipStream_t stream) {
   PrefillDims p;
-  egs_status st = check_prefill(shape, &p);
+  int kind;
+  egs_status st = check_score(shape, pool_kind, entropy_kind, renyi_alpha, q, k, block_scores,
+                              entropy, &p, &kind);
   if (st != EGS_OK) return st;
-  if (pool_kind != EGS_POOL_MEAN_PROBE && pool_kind != EGS_POOL_MAXMIN)
-    return fail(EGS_EINVAL, "unknown pool_kind %d", pool_kind);
-  int kind = entropy_kind;
-  if (kind != EGS_SHANNON && kind != EGS_RENYI)
-    return fail(EGS_EINVAL, "unknown entropy_kind %d", entropy_kind);
-  if (kind == EGS_RENYI) {
-    if (!(std::isfinite(renyi_alpha) && renyi_alpha > 0.f))
-      return fail(EGS_EINVAL, "renyi_alpha must be finite and > 0");
-    if (renyi_alpha == 1.0f) kind = EGS_SHANNON;
-  }
-  if ((st = need(q, "q", 16)) != EGS_OK) return st;
-  if ((st = need(k, "k", 16)) != EGS_OK) return st;
-  if ((st = need(block_scores, "block_scores", 4)) != EGS_OK) return st;
-  if ((st = need(entropy, "entropy", 4)) != EGS_OK) return st;
   if ((st = need(workspace, "workspace", kWsAlign)) != EGS_OK) return st;
   const size_t wsb = egs::score_workspace_bytes(p);
   if (workspace_bytes < wsb)
@@ -201,6 +213,25 @@ egs_status egs_entropy_score(const egs_prefill_shape* shape, int32_t pool_kind,
   return hip_status(egs::launch_entropy_score(p, q, k, kind, renyi_alpha, block_scores, entropy,
                                               workspace, stream),
                     "entropy_score launch");
+}
+
+egs_status egs_entropy_score_static(const egs_prefill_shape* shape, int32_t pool_kind,
+                                    int32_t entropy_kind, float renyi_alpha, const void* q,
+                                    const void* k, float* block_scores, float* entropy,
+                                    hipStream_t stream) {
+  PrefillDims p;
+  int kind;
+  egs_status st = check_score(shape, pool_kind, entropy_kind, renyi_alpha, q, k, block_scores,
+                              entropy, &p, &kind);
+  if (st != EGS_OK) return st;
+  const size_t wsb = egs::score_workspace_bytes(p);
+  if (wsb > EGS_STATIC_SCRATCH_BYTES)
+    return fail(EGS_EWORKSPACE, "the shape needs %zu bytes of scratch, above the static %zu",
+                wsb, (size_t)EGS_STATIC_SCRATCH_BYTES);
+  return hip_status(egs::launch_entropy_score_static(p, pool_kind == EGS_POOL_MAXMIN, q, k,
+                                                     kind, renyi_alpha, block_scores, entropy,
+                                                     stream),
+                    "entropy_score (static scratch) launch");
 }
 
 egs_status egs_allocate_budget(const egs_prefill_shape* shape, const egs_budget_policy* policy,

@@ -77,6 +77,11 @@ size_t score_workspace_bytes(const PrefillDims& p);
 hipError_t launch_entropy_score(const PrefillDims& p, const void* q, const void* k, int kind,
                                 float alpha, float* scores, float* entropy, void* ws,
                                 hipStream_t st);
+// egs_entropy_score on the library's static device scratch
+// (EGS_STATIC_SCRATCH_BYTES per GPU; the caller has checked the size)
+hipError_t launch_entropy_score_static(const PrefillDims& p, bool maxmin, const void* q,
+                                       const void* k, int kind, float alpha, float* scores,
+                                       float* entropy, hipStream_t st);
 // The same outputs from the max / min representatives (maxmin.hip); its
 // workspace need is included in score_workspace_bytes.
 size_t maxmin_workspace_bytes(const PrefillDims& p);

@@ -39,6 +39,8 @@
 #include "egs_device.h"
 #include "egs_launch.h"
 
+#include <mutex>
+
 namespace egs {
 
 constexpr int PS_NB = 16;     // key blocks per pool_keys workgroup
@@ -613,6 +615,49 @@ hipError_t launch_entropy_score(const PrefillDims& p, const void* q, const void*
   return p.dtype == EGS_F32
              ? score_dispatch<float>(p, ly, q, k, w, kind, alpha, scores, entropy, st)
              : score_dispatch<bf16>(p, ly, q, k, w, kind, alpha, scores, entropy, st);
+}
+
+// ---------------------------------------------------------------------------
+// Static scratch for egs_entropy_score_static: callers that cannot allocate
+// get the workspace from this device array instead (each GPU holds its own
+// copy from the code object's load until the process ends).  In host code
+// `scratch` names a host-side stand-in, never the device memory: its device
+// address is taken once per device with hipGetSymbolAddress, with that device
+// current, and only that address is handed to kernels.
+// ---------------------------------------------------------------------------
+static __device__ __align__(256) unsigned char scratch[EGS_STATIC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+hipError_t static_scratch(void** out) {
+  int dev = -1;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (g_scratch_ptr[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return hipSuccess;
+}
+}  // namespace
+
+hipError_t launch_entropy_score_static(const PrefillDims& p, bool maxmin, const void* q,
+                                       const void* k, int kind, float alpha, float* scores,
+                                       float* entropy, hipStream_t st) {
+  void* ws = nullptr;
+  const hipError_t e = static_scratch(&ws);
+  if (e != hipSuccess) return e;
+  return maxmin ? launch_entropy_score_maxmin(p, q, k, kind, alpha, scores, entropy, ws, st)
+                : launch_entropy_score(p, q, k, kind, alpha, scores, entropy, ws, st);
 }
 
 }  // namespace egs

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define EGS_ABI_VERSION 4
+#define EGS_ABI_VERSION 5
 
 typedef enum {
   EGS_OK = 0,
@@ -148,6 +148,27 @@ egs_status egs_entropy_score(const egs_prefill_shape* shape, int32_t pool_kind,
                              float* block_scores, float* entropy,
                              void* workspace, size_t workspace_bytes,
                              hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * egs_entropy_score without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, serving loops that
+ * forbid hipMalloc).  Same arguments, checks, kernels and results as
+ * egs_entropy_score; the scratch is a fixed device array of
+ * EGS_STATIC_SCRATCH_BYTES inside the library, one per GPU, held until the
+ * process ends.  A shape whose egs_entropy_score_workspace() exceeds that
+ * size returns EGS_EWORKSPACE before anything is launched (the 131072-token,
+ * 32 / 8-head layer needs 22 MiB).  The call allocates nothing: no hipMalloc,
+ * no hipFree, no allocating library routine.  Every call on one GPU shares
+ * that GPU's array: calls that overlap on one GPU (other streams, other host
+ * threads) race and must be serialised by the caller.  No part of the array
+ * has to start at zero; it keeps the last call's contents.
+ * ------------------------------------------------------------------------- */
+#define EGS_STATIC_SCRATCH_BYTES ((size_t)64 << 20)
+egs_status egs_entropy_score_static(const egs_prefill_shape* shape, int32_t pool_kind,
+                                    int32_t entropy_kind, float renyi_alpha,
+                                    const void* q, const void* k,
+                                    float* block_scores, float* entropy,
+                                    hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Steps 6-7: classify heads and allocate per-(head, segment) budgets.

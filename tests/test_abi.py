@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.LIB.egs_abi_version() == 4
+    assert L.LIB.egs_abi_version() == 5
     for st in range(5):
         assert L.LIB.egs_status_string(st).decode().startswith("EGS_")
 
@@ -327,3 +327,24 @@ def test_latent_workspace_holds_every_length(L, B, Hq, Hkv, cap):
     worst = max(L.LIB.egs_sparse_decode_attn_workspace(ctypes.byref(sc), n)
                 for n in range(64, cap + 1))
     assert worst + rest <= total
+
+
+def test_entropy_score_static_rejects_large_shapes(L):
+    # the static scratch holds EGS_STATIC_SCRATCH_BYTES; a 262144-token layer
+    # with 32 / 8 heads needs more and is refused before any launch
+    big = _shape(L, n_q_heads=32, n_kv_heads=8, head_dim=128, seq_len=262144, block_size=128,
+                 segment_size=8192)
+    assert L.LIB.egs_entropy_score_workspace(ctypes.byref(big)) > L.EGS_STATIC_SCRATCH_BYTES
+    assert L.LIB.egs_entropy_score_static(ctypes.byref(big), 0, 0, 2.0, FAKE, FAKE, FAKE, FAKE,
+                                          None) == L.EGS_EWORKSPACE
+    ok = _shape(L, n_q_heads=32, n_kv_heads=8, head_dim=128, seq_len=131072, block_size=128,
+                segment_size=8192)
+    assert L.LIB.egs_entropy_score_workspace(ctypes.byref(ok)) <= L.EGS_STATIC_SCRATCH_BYTES
+    # the same argument checks as egs_entropy_score
+    sc = _shape(L)
+    assert L.LIB.egs_entropy_score_static(ctypes.byref(sc), 7, 0, 2.0, FAKE, FAKE, FAKE, FAKE,
+                                          None) == L.EGS_EINVAL
+    assert L.LIB.egs_entropy_score_static(ctypes.byref(sc), 0, 1, -1.0, FAKE, FAKE, FAKE, FAKE,
+                                          None) == L.EGS_EINVAL
+    assert L.LIB.egs_entropy_score_static(ctypes.byref(sc), 0, 0, 2.0, None, FAKE, FAKE, FAKE,
+                                          None) == L.EGS_EINVAL
