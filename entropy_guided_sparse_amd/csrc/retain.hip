@@ -50,6 +50,13 @@
 
 namespace egs {
 
+// The compiler schedules nothing across this point.
+__device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
+// Keeps the computation of x before this point: an empty volatile asm that
+// reads and writes x is ordered against the scheduling fences, so work that
+// only feeds a later sum cannot drift past the next fence.
+__device__ __forceinline__ void pin_vgpr(float& x) { asm volatile("" : "+v"(x)); }
+
 constexpr int RT_CK = 1024;   // keys per span (the pass 1 / pass 2 work unit)
 constexpr int RT_KT = 64;     // keys per LDS stage
 constexpr int SEL_T = 1024;   // threads of the select kernel
@@ -372,15 +379,34 @@ __global__ __launch_bounds__(256) void obs_pass_kernel(
           for (int rt = 0; rt < RT; ++rt) z[rt] = mfma32(qf[rt][c], bk, z[rt]);
         }
         const int t = tk + l32;
-        float colsum = 0.f;
+        // summed in the order of the pipelined interior path (runs of 16 / NC
+        // terms, a tree over the runs, then the row tiles), so that equal
+        // masses come out bit-equal in every span
+        constexpr int EPS = 16 / NC;
+        float part[RT][NC];
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            float pv = fast_exp2(__builtin_fmaf(z[rt][i], sl2, -rm[rt][i]));
-            if (edge && t > pos0 + rt * 32 + acc_row(i, lane)) pv = 0.f;
-            colsum += pv;
+          for (int c = 0; c < NC; ++c) {
+            float acc = 0.f;
+#pragma unroll
+            for (int q = 0; q < EPS; ++q) {
+              const int i = c * EPS + q;
+              float pv = fast_exp2(__builtin_fmaf(z[rt][i], sl2, -rm[rt][i]));
+              if (edge && t > pos0 + rt * 32 + acc_row(i, lane)) pv = 0.f;
+              acc += pv;
+            }
+            part[rt][c] = acc;
           }
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+          for (int n = NC; n > 1; n >>= 1)
+#pragma unroll
+            for (int i = 0; i < n / 2; ++i) part[rt][i] += part[rt][i + n / 2];
+        float colsum = part[0][0];
+#pragma unroll
+        for (int rt = 1; rt < RT; ++rt) colsum += part[rt][0];
         colsum = xhalf_sum(colsum);
         if (hg == 0 && t < t_end) {
           const float a = colsum * invW;
@@ -395,9 +421,12 @@ __global__ __launch_bounds__(256) void obs_pass_kernel(
       }
     }
   };
-  // stage st sits in buffer st % RT_DEPTH; iteration st copies stage
-  // st + RT_DEPTH - 1 into the buffer stage st - 1 used
-  for (int st = 0; st < nst; ++st) {
+  // Stage st sits in buffer st % RT_DEPTH.  At the top of stage st a wave
+  // waits for its copies of stage st (the copies of the stages after it stay
+  // in flight; pass 2's mass stores are not counted, which only ever makes
+  // the wait longer), meets the others at the barrier and copies stage
+  // st + RT_DEPTH - 1 into the buffer stage st - 1 used.
+  auto stage_top = [&](int st) {
     const int ahead = min(RT_DEPTH - 2, nst - 1 - st);   // copies issued after stage st's
     if (ahead >= 2) wait_vmem_upto<2 * PW>();
     else if (ahead == 1) wait_vmem_upto<PW>();
@@ -406,12 +435,172 @@ __global__ __launch_bounds__(256) void obs_pass_kernel(
     if (st + RT_DEPTH - 1 < nst)
       KPipe<D>::copy(Ks[(st + RT_DEPTH - 1) % RT_DEPTH], Kg, t_begin + (st + RT_DEPTH - 1) * RT_KT,
                      t_end - 1, w, lane);
-    if (hvalid) {
-      const int t0 = t_begin + st * RT_KT;
-      if (t0 + RT_KT - 1 >= t_end || t0 + RT_KT - 1 > pos0)
-        compute(Ks[st % RT_DEPTH], t0, std::true_type{});
-      else
-        compute(Ks[st % RT_DEPTH], t0, std::false_type{});
+  };
+  // Interior spans: every key of a whole span precedes the first observer
+  // (and, in pass 2, the sinks), so no tile needs a mask.  There the tile
+  // loop is software-pipelined: the MFMAs of tile j + 1 issue in between the
+  // VALU work of tile j (its exponentials and sums), which otherwise waits
+  // for them and then runs alone.
+  constexpr bool kPipe = !SEG && RT <= 2;
+  const bool interior = kPipe && t_end - t_begin == RT_CK && t_end - 1 <= pos0 &&
+                        (!MASS || t_begin >= n_sink);
+  if (interior) {
+    constexpr int NST = RT_CK / RT_KT;
+    // One region: the logits of tile kt of a stage (keys as M in pass 1, as
+    // N in pass 2) into zn, and the exponentials of the previous tile zc.
+    // The region runs in NC slices split by scheduling fences: slice c
+    // issues the MFMAs of d chunk c and then 16 / NC exponentials of every
+    // row tile of zc, so the VALU works while the MFMAs of the slice run.
+    // Pass 1 returns the tile's row sums against the running reference in
+    // sm; pass 2 the lane's column sum of probabilities in sm[0].
+    constexpr int EPS = 16 / NC;   // exponentials per row tile and slice
+    auto region = [&](const bf16* ks, int kt, floatx16 (&zn)[RT], const floatx16 (&zc)[RT],
+                      float (&sm)[RT]) {
+      bf16x8 fr[NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) fr[c] = KPipe<D>::frag(ks, kt * 32 + l32, c, hg);
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) zn[rt][i] = 0.f;
+      float part[RT][NC];
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          zn[rt] = MASS ? mfma32(qf[rt][c], fr[c], zn[rt]) : mfma32(fr[c], qf[rt][c], zn[rt]);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) {
+          float acc = 0.f;
+#pragma unroll
+          for (int q = 0; q < EPS; ++q) {
+            const int i = c * EPS + q;
+            acc += fast_exp2(__builtin_fmaf(zc[rt][i], sl2, MASS ? -rm[rt][i] : -m[rt]));
+          }
+          part[rt][c] = acc;
+          pin_vgpr(part[rt][c]);
+        }
+        sched_fence();
+      }
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+#pragma unroll
+        for (int n = NC; n > 1; n >>= 1)
+#pragma unroll
+          for (int i = 0; i < n / 2; ++i) part[rt][i] += part[rt][i + n / 2];
+      }
+      if constexpr (MASS) {
+        float t = part[0][0];
+#pragma unroll
+        for (int rt = 1; rt < RT; ++rt) t += part[rt][0];
+        sm[0] = t;
+      } else {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) sm[rt] = part[rt][0];
+      }
+    };
+    // the same exponentials with no MFMAs beside them (the span's last tile)
+    auto tail = [&](const floatx16 (&zc)[RT], float (&sm)[RT]) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        float acc = 0.f;
+#pragma unroll
+        for (int i = 0; i < 16; ++i)
+          acc += fast_exp2(__builtin_fmaf(zc[rt][i], sl2, MASS ? -rm[rt][i] : -m[rt]));
+        sm[rt] = acc;
+      }
+      if constexpr (MASS) {
+#pragma unroll
+        for (int rt = 1; rt < RT; ++rt) sm[0] += sm[rt];
+      }
+    };
+    // the first tile of the span: its logits alone
+    auto first = [&](const bf16* ks, floatx16 (&zn)[RT]) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int i = 0; i < 16; ++i) zn[rt][i] = 0.f;
+#pragma unroll
+      for (int c = 0; c < NC; ++c) {
+        const bf16x8 a = KPipe<D>::frag(ks, l32, c, hg);
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt)
+          zn[rt] = MASS ? mfma32(qf[rt][c], a, zn[rt]) : mfma32(a, qf[rt][c], zn[rt]);
+      }
+    };
+    // pass 1: fold a tile's row sums into (m, l); a sum above 2^64 (rare)
+    // raises the reference first
+    auto fold1 = [&](const floatx16 (&z)[RT], float (&sm)[RT]) {
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt) {
+        if (!(sm[rt] <= 0x1p64f)) {
+          float tmax = z[rt][0];
+#pragma unroll
+          for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, z[rt][i]);
+          const float mn = fmaxf(m[rt], tmax * sl2);
+          float sum = 0.f;
+#pragma unroll
+          for (int i = 0; i < 16; ++i) sum += fast_exp2(__builtin_fmaf(z[rt][i], sl2, -mn));
+          l[rt] *= fast_exp2(m[rt] - mn);
+          m[rt] = mn;
+          sm[rt] = sum;
+        }
+        l[rt] += sm[rt];
+      }
+    };
+    // pass 2: the window-mean mass of the lane's key (both halves of the
+    // wave hold it) and its sink-isolated entropy terms, counted by the low half
+    auto mass2 = [&](float colsum) -> float {
+      const float a = xhalf_sum(colsum) * invW;
+      const float lg = __log2f(a);
+      const float term = kind == EGS_SHANNON ? a * lg * kLn2 : fast_exp2(alpha * lg);
+      const bool on = hg == 0 && a > 0.f;
+      s1 += on ? a : 0.f;
+      s2 += on ? term : 0.f;
+      return a;
+    };
+    float* mrow = MASS ? mass + ((size_t)b * Hq + h) * L : nullptr;
+    floatx16 za[RT], zb[RT];
+    stage_top(0);
+    if (hvalid) first(Ks[0], za);
+    for (int st = 0; st < NST; ++st) {
+      float a0 = 0.f, a1 = 0.f;
+      if (hvalid) {
+        // tile 1 of stage st on the MFMA unit, tile 0 on the VALU
+        float sm[RT];
+        region(Ks[st % RT_DEPTH], 1, zb, za, sm);
+        if constexpr (MASS) a0 = mass2(sm[0]);
+        else fold1(za, sm);
+      }
+      if (st + 1 < NST) {
+        stage_top(st + 1);
+        if (hvalid) {
+          // tile 0 of stage st + 1 on the MFMA unit, tile 1 of stage st on the VALU
+          float sm[RT];
+          region(Ks[(st + 1) % RT_DEPTH], 0, za, zb, sm);
+          if constexpr (MASS) a1 = mass2(sm[0]);
+          else fold1(zb, sm);
+        }
+      } else if (hvalid) {
+        float sm[RT];
+        tail(zb, sm);
+        if constexpr (MASS) a1 = mass2(sm[0]);
+        else fold1(zb, sm);
+      }
+      // one store per stage: the low half of the wave writes tile 0's keys,
+      // the high half tile 1's
+      if (MASS && hvalid) mrow[t_begin + st * RT_KT + hg * 32 + l32] = hg ? a1 : a0;
+    }
+  } else {
+    for (int st = 0; st < nst; ++st) {
+      stage_top(st);
+      if (hvalid) {
+        const int t0 = t_begin + st * RT_KT;
+        if (t0 + RT_KT - 1 >= t_end || t0 + RT_KT - 1 > pos0)
+          compute(Ks[st % RT_DEPTH], t0, std::true_type{});
+        else
+          compute(Ks[st % RT_DEPTH], t0, std::false_type{});
+      }
     }
   }
   if (!hvalid) return;
