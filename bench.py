@@ -36,6 +36,8 @@ def parse_args():
     ap.add_argument("--entropy", default="shannon", choices=["shannon", "renyi2"])
     ap.add_argument("--no-decode", action="store_true", help="time the prefill layer only")
     ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-workloads", action="store_true",
+                    help="skip the other prefill workloads (32k, Qwen 64k, the other entropy)")
     ap.add_argument("--cpu-seconds", type=float, default=12.0,
                     help="approximate CPU time spent on the oracle sample")
     ap.add_argument("--json-out", default=None)
@@ -146,6 +148,76 @@ def measured_traffic(cfg_name):
     return int(rec["bytes_per_launch"])
 
 
+def back_to_back(torch, fn, flush, reps):
+    """Median GPU time (ms) of fn() with no event inside it; a 512 MiB write
+    before each repetition evicts the Infinity Cache, so K streams from HBM."""
+    times = []
+    for rep in range(reps + 1):
+        flush.fill_(rep & 0x7F)
+        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        ev0.record()
+        fn()
+        ev1.record()
+        times.append((ev0, ev1))
+    torch.cuda.synchronize()
+    return float(np.median([a.elapsed_time(b) for a, b in times[1:]]))
+
+
+def prefill_workload(api, torch, dev, cfg, inp, kind, steps, flush, dev_qkv=None):
+    """One prefill layer of `cfg` on its own: the fused scoring call and the
+    attention, each timed back to back (median of `steps`, Infinity Cache
+    evicted before each repetition); executed tiles from the GPU's lists."""
+    L = api.L
+    if dev_qkv is None:
+        to = lambda x: torch.from_numpy(np.ascontiguousarray(x)).view(torch.bfloat16).to(dev)
+        q, k, v = to(inp.q_store), to(inp.k_store), to(inp.v_store)
+    else:
+        q, k, v = dev_qkv
+    shape = api.PrefillShape(cfg.n_q_heads, cfg.n_kv_heads, cfg.head_dim, cfg.seq_len,
+                             cfg.block_size, cfg.segment_size, cfg.probe_len, torch.bfloat16)
+    pol = prefill_policy(api, cfg)
+    Hq, CS, CB, LB, LS, d = (cfg.n_q_heads, cfg.n_segments, cfg.n_blocks, cfg.block_size,
+                             cfg.segment_size, cfg.head_dim)
+    k_max = k_max_for(pol, api, CB, LB)
+    import ctypes
+    sc = shape.c()
+    ws = torch.empty(L.LIB.egs_entropy_score_workspace(ctypes.byref(sc)), dtype=torch.uint8,
+                     device=dev)
+    aws = torch.empty(max(256, L.LIB.egs_sparse_prefill_attn_workspace(ctypes.byref(sc))),
+                      dtype=torch.uint8, device=dev)
+    res = api.score_select(shape, pol, q, k, k_max, kind=kind, renyi_alpha=2.0, workspace=ws)
+    out = torch.empty_like(q)
+
+    def scoring():
+        api.score_select(shape, pol, q, k, k_max, kind=kind, renyi_alpha=2.0, out=res,
+                         workspace=ws)
+
+    def attention():
+        api.sparse_prefill_attn(shape, q, k, v, res["block_idx"], res["block_cnt"], out=out,
+                                workspace=aws)
+
+    scoring()
+    attention()
+    torch.cuda.synchronize()
+    tiles = executed_tiles(res["block_idx"].cpu().numpy(), res["block_cnt"].cpu().numpy(),
+                           CS, CB, LB, LS)
+    t_s = back_to_back(torch, scoring, flush, steps)
+    t_a = back_to_back(torch, attention, flush, steps)
+    sbytes = scoring_bytes(cfg, k_max, 2)
+    flops = tiles * 4.0 * LB * LB * d
+    gbs = sbytes / (t_s * 1e-3) / 1e9
+    tf = flops / (t_a * 1e-3) / 1e12
+    del q, k, v, out, ws, aws, res
+    return {"entropy": "renyi2" if kind == L.EGS_RENYI else "shannon",
+            "ms_per_layer": round(t_s + t_a, 3), "scoring_us": round(t_s * 1e3, 1),
+            "attention_ms": round(t_a, 3),
+            "scoring_gbps": round(gbs, 1), "scoring_hbm_frac": round(gbs / PEAK_HBM_GBS, 4),
+            "attention_tflops_executed": round(tf, 1),
+            "attention_mfma_frac": round(tf / PEAK_BF16_TFLOPS, 4),
+            "effective_tflops": round(flops / ((t_s + t_a) * 1e-3) / 1e12, 1),
+            "tile_density": round(tiles / (Hq * CB * (CB + 1) // 2), 4)}
+
+
 def calib_copy(torch, dev, mib):
     """One elementwise copy of `mib` MiB (read mib, write mib): torch.neg on fp32."""
     n = mib * (1 << 20) // 4
@@ -158,17 +230,62 @@ def calib_copy(torch, dev, mib):
     del x, y
 
 
-def cpu_baseline(cfg, inp, idx, cnt, seconds):
-    """Oracle attention on a seeded sample of (head, query block) pairs."""
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(cfg, inp, idx, cnt, seconds, pol=None, k_max=None, decode_cfg=None,
+                 gpu_ms=None):
+    """The float64 oracle on the host cores, stage by stage, on the step's
+    inputs: scoring, budgets and selection on the whole prefill layer; the
+    attention on a seeded sample of (head, query block) pairs; retention and
+    decode attention on one (batch, KV group) slice of the decode workload.
+    Sampled stages are scaled to the whole workload by their share of it."""
     sys.path.insert(0, os.path.dirname(os.path.abspath(__file__)))
     from oracle import egs_oracle as O
+    from entropy_guided_sparse_amd import synth
     try:
         from threadpoolctl import threadpool_info
         cores = max([i.get("num_threads", 1) for i in threadpool_info()] or [1])
     except Exception:
         cores = os.cpu_count() or 1
-    rng = np.random.default_rng(0)
     Hq, CB, LB, LS, d = cfg.n_q_heads, cfg.n_blocks, cfg.block_size, cfg.segment_size, cfg.head_dim
+    stages = {}
+
+    def stage(name, sec, sample, scale=1.0):
+        est = sec * scale
+        st = {"seconds": round(sec, 3), "sample": sample, "workload_seconds": round(est, 3)}
+        if gpu_ms and gpu_ms.get(name):
+            st["gpu_ms"] = round(gpu_ms[name], 4)
+            st["gpu_speedup"] = round(est / (gpu_ms[name] * 1e-3), 1)
+        stages[name] = st
+
+    if pol is not None:
+        t0 = time.perf_counter()
+        r_scores, r_E = O.entropy_score(inp.q, inp.k, LS, LB, cfg.probe_len)
+        t1 = time.perf_counter()
+        pk = dict(frac=pol.frac, frac_rigid=pol.frac_rigid, frac_dynamic=pol.frac_dynamic,
+                  frac_min=pol.frac_min, frac_max=pol.frac_max,
+                  entropy_threshold=pol.entropy_threshold, base_tokens=pol.base_tokens,
+                  alg3_alpha=pol.alg3_alpha, alg3_delta_t=pol.alg3_delta_t)
+        _, r_budget = O.allocate_budget(r_E, LS, LB, pol.mode, **pk)
+        t2 = time.perf_counter()
+        O.select_blocks(r_scores, r_budget, LS, LB, k_max=k_max)
+        t3 = time.perf_counter()
+        stage("scoring", t1 - t0, "whole layer (pooling, probe rows, entropy)")
+        stage("budget", t2 - t1, "whole layer")
+        stage("select", t3 - t2, "whole layer")
+        if gpu_ms:
+            stages["scoring"]["gpu_ms_covers"] = "the fused scoring call: steps 1-8"
+
+    # attention: seeded random (head, query block) pairs, scaled by FLOPs
+    rng = np.random.default_rng(0)
     flops = 0.0
     n = 0
     t0 = time.perf_counter()
@@ -179,11 +296,31 @@ def cpu_baseline(cfg, inp, idx, cnt, seconds):
         flops += 4.0 * LB * LB * d * nblk
         n += 1
     dt = time.perf_counter() - t0
+    total_flops = 4.0 * LB * LB * d * executed_tiles(idx, cnt, cfg.n_segments, CB, LB, LS)
+    stage("attention", dt, f"{n} seeded random (head, query-block) pairs using the GPU's "
+          "block lists; scaled by executed-tile FLOPs", total_flops / flops)
+
+    if decode_cfg is not None:
+        dc = decode_cfg
+        dinp = synth.make_decode(dc, seed=0, batch=1)
+        r = dc.n_q_heads // dc.n_kv_heads
+        t0 = time.perf_counter()
+        keep, mu, H = O.kv_retain_slice(dinp.q_obs[0, :r], dinp.k[0, 0], dc.n_sink, dc.n_recent,
+                                        dc.n_keep)
+        t1 = time.perf_counter()
+        O.sparse_decode_attn(dinp.q_new[0:1, :r], dinp.k[0:1, 0:1, keep],
+                             dinp.v[0:1, 0:1, keep])
+        t2 = time.perf_counter()
+        slices = dc.batch * dc.n_kv_heads
+        stage("kv_retain", t1 - t0, f"one (batch, KV group) slice of {slices}", slices)
+        stage("decode_attn", t2 - t1, f"one (batch, KV group) slice of {slices}", slices)
+        del dinp
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores),
-            "kind": "oracle",
+            "cpu_model": cpu_model(), "cpu_count": os.cpu_count(), "kind": "oracle",
             "sample": f"float64 oracle sparse attention on {n} seeded random (head, query-block) "
                       f"pairs of the same {cfg.name} layer using the GPU's block lists, "
-                      f"{dt:.1f} s; executed-block FLOPs / time"}
+                      f"{dt:.1f} s; executed-block FLOPs / time",
+            "stages": stages}
 
 
 def main():
@@ -230,14 +367,17 @@ def main():
     attn_ws = torch.empty(max(256, L.LIB.egs_sparse_prefill_attn_workspace(ctypes.byref(sc))),
                           dtype=torch.uint8, device=dev)
 
+    sel_out = {"block_scores": scores, "entropy": E, "head_is_rigid": rigid, "budget": budget,
+               "block_idx": idx, "block_cnt": cnt}
+
     def prefill(evs):
+        # steps 1-8 in one call (the same outputs as entropy_score,
+        # allocate_budget and select_blocks), then the sparse attention
         evs[0].record()
-        api.entropy_score(shape, q, k, kind=kind, renyi_alpha=2.0, block_scores=scores,
-                          entropy=E, workspace=ws)
+        api.score_select(shape, pol, q, k, k_max, kind=kind, renyi_alpha=2.0, out=sel_out,
+                         workspace=ws)
         evs[1].record()
-        api.allocate_budget(shape, pol, E, head_is_rigid=rigid, budget=budget)
         evs[2].record()
-        api.select_blocks(shape, scores, budget, k_max, block_idx=idx, block_cnt=cnt)
         evs[3].record()
         api.sparse_prefill_attn(shape, q, k, v, idx, cnt, out=out, workspace=attn_ws)
         evs[4].record()
@@ -310,12 +450,9 @@ def main():
 
     t_attn_median = float(np.median([ev[3].elapsed_time(ev[4]) for ev in all_evs]))
     t_score = mean_ms(0, 1)
-    t_budget = mean_ms(1, 2)
-    t_select = mean_ms(2, 3)
     t_attn = mean_ms(3, 4)
     t_prefill = mean_ms(0, 4)
-    kernel_us = {"entropy_score": 1e3 * t_score, "allocate_budget": 1e3 * t_budget,
-                 "select_blocks": 1e3 * t_select, "sparse_prefill_attn": 1e3 * t_attn}
+    kernel_us = {"score_select": 1e3 * t_score, "sparse_prefill_attn": 1e3 * t_attn}
     t_decode = None
     if decode is not None:
         kernel_us["kv_retain"] = 1e3 * mean_ms(4, 5)
@@ -324,7 +461,7 @@ def main():
 
     elt = 2 if cfg.dtype == "bf16" else 4
     sbytes = scoring_bytes(cfg, k_max, elt)
-    t_scoring = t_score + t_budget + t_select
+    t_scoring = t_score
     scoring_gbs = sbytes / (t_scoring * 1e-3) / 1e9
     exec_flops = tiles * tile_flops
     attn_tflops = exec_flops / (t_attn * 1e-3) / 1e12
@@ -337,21 +474,20 @@ def main():
     # repetition evicts K from the 256 MB Infinity Cache, so K streams from
     # HBM as it does in the step, where the decode leg runs in between.
     flush = torch.empty(512 << 20, dtype=torch.uint8, device=dev)
-    solo = []
-    for rep in range(args.steps + 1):
-        flush.fill_(rep & 0x7F)
-        ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        ev0.record()
+
+    def three_calls():
         api.entropy_score(shape, q, k, kind=kind, renyi_alpha=2.0, block_scores=scores,
                           entropy=E, workspace=ws)
         api.allocate_budget(shape, pol, E, head_is_rigid=rigid, budget=budget)
         api.select_blocks(shape, scores, budget, k_max, block_idx=idx, block_cnt=cnt)
-        ev1.record()
-        solo.append((ev0, ev1))
-    torch.cuda.synchronize()
-    t_scoring_solo = float(np.median([a.elapsed_time(b) for a, b in solo[1:]]))
+
+    def fused_call():
+        api.score_select(shape, pol, q, k, k_max, kind=kind, renyi_alpha=2.0, out=sel_out,
+                         workspace=ws)
+
+    t_scoring_solo = back_to_back(torch, fused_call, flush, args.steps)
+    t_scoring_3 = back_to_back(torch, three_calls, flush, args.steps)
     scoring_solo_gbs = sbytes / (t_scoring_solo * 1e-3) / 1e9
-    del flush, solo
 
     # the paper-literal max / min observation rows ([EI] Alg. 1-2), timed on
     # their own after the step loop (they are not part of the step)
@@ -459,6 +595,24 @@ def main():
                  "removed_tokens": int(ptok.item())}
         del pws
 
+    # the other prefill workloads, each on its own (not part of the step)
+    workloads = {}
+    if not args.no_workloads:
+        workloads[f"{cfg.name}-renyi2" if kind == L.EGS_SHANNON else f"{cfg.name}-shannon"] = \
+            prefill_workload(api, torch, dev, cfg, None,
+                             L.EGS_RENYI if kind == L.EGS_SHANNON else L.EGS_SHANNON,
+                             args.steps, flush, dev_qkv=(q, k, v))
+        for wname in ("llama3-8b-32k", "qwen-64k"):
+            if wname == cfg.name:
+                continue
+            wc = synth.PREFILL_CONFIGS[wname]
+            winp = synth.make_prefill(wc, seed=0)
+            workloads[wname] = prefill_workload(api, torch, dev, wc, winp, L.EGS_SHANNON,
+                                                args.steps, flush)
+            del winp
+            torch.cuda.empty_cache()
+    del flush
+
     traffic = measured_traffic(cfg.name)
     if args.calib_copy_mib > 0:
         calib_copy(torch, dev, args.calib_copy_mib)
@@ -488,6 +642,7 @@ def main():
         "scoring_pass_us": round(t_scoring_solo * 1e3, 2),
         "scoring_pass_gbps": round(scoring_solo_gbs, 1),
         "scoring_pass_bytes": sbytes,
+        "scoring_pass_three_calls_us": round(t_scoring_3 * 1e3, 2),
         "scoring_pass_in_step_us": round(t_scoring * 1e3, 2),
         "scoring_pass_in_step_gbps": round(scoring_gbs, 1),
         "attn_ms": round(t_attn, 4),
@@ -517,14 +672,38 @@ def main():
         kv_bytes = dc.batch * dc.n_kv_heads * dc.cache_len * dc.head_dim * 2
         res["decode_ms"] = round(t_decode, 4)
         res["decode_kv_retain_gbps"] = round(kv_bytes / (kernel_us["kv_retain"] * 1e-6) / 1e9, 1)
+        # kv_retain against both bounds: K read once (plus the observers) for
+        # HBM, one pass of window logits 2 W d L Hq B for MFMA (the second,
+        # recomputing pass is implementation work and not counted)
+        qo_bytes = dc.batch * dc.n_q_heads * dc.n_obs * dc.head_dim * 2
+        kr_flops = 2.0 * dc.n_obs * dc.head_dim * dc.cache_len * dc.n_q_heads * dc.batch
+        kr_s = kernel_us["kv_retain"] * 1e-6
+        res["kv_retain_roofline"] = {
+            "hbm": {"achieved": round((kv_bytes + qo_bytes) / kr_s / 1e9, 1),
+                    "peak": PEAK_HBM_GBS, "unit": "GB/s",
+                    "frac": round((kv_bytes + qo_bytes) / kr_s / 1e9 / PEAK_HBM_GBS, 4),
+                    "bytes": kv_bytes + qo_bytes},
+            "mfma": {"achieved": round(kr_flops / kr_s / 1e12, 1), "peak": PEAK_BF16_TFLOPS,
+                     "unit": "TFLOP/s",
+                     "frac": round(kr_flops / kr_s / 1e12 / PEAK_BF16_TFLOPS, 4),
+                     "flops": kr_flops}}
         res["decode_n_total"] = decode["n_total"]
         res["page_retain_us"] = page_us
         res["latent_decode"] = latent
         res["chunk_prune"] = prune
         res["page_retain_config"] = {"page_size": pg_S, "n_keep_pages": pg_K,
                                      "scores": "kv_retain group scores, batch 8, 8 groups, 128k"}
+    if workloads:
+        res["workloads"] = workloads
     if not args.no_cpu_baseline:
-        res["cpu_baseline"] = cpu_baseline(cfg, inp, g_idx, g_cnt, args.cpu_seconds)
+        res["cpu_baseline"] = cpu_baseline(cfg, inp, g_idx, g_cnt, args.cpu_seconds, pol=pol,
+                                           k_max=k_max,
+                                           decode_cfg=decode["cfg"] if decode else None,
+                                           gpu_ms={"scoring": t_scoring_solo,
+                                                   "attention": t_attn,
+                                                   "kv_retain": kernel_us.get("kv_retain", 0) / 1e3,
+                                                   "decode_attn":
+                                                       kernel_us.get("sparse_decode_attn", 0) / 1e3})
     line = json.dumps(res)
     print(line, flush=True)
     if args.json_out:

@@ -19,7 +19,7 @@ EGS_POOL_MEAN_PROBE, EGS_POOL_MAXMIN = 0, 1
 EGS_BUDGET_FIXED, EGS_BUDGET_TWO_LEVEL, EGS_BUDGET_PROPORTIONAL, EGS_BUDGET_ALG3 = range(4)
 EGS_PAGE_GROUP, EGS_PAGE_LAYER_UNION, EGS_PAGE_HEAD_UNION = 0, 1, 2
 EGS_STATIC_SCRATCH_BYTES = 64 << 20
-ABI_VERSION = 5
+ABI_VERSION = 6
 
 
 class PrefillShapeC(ctypes.Structure):
@@ -79,6 +79,9 @@ SIGNATURES = {
                                        _P, _P, _P, _P]),
     "egs_allocate_budget": (_ST, [_PS, ctypes.POINTER(BudgetPolicyC), _P, _P, _P, _P]),
     "egs_select_blocks": (_ST, [_PS, _P, _P, ctypes.c_int32, _P, _P, _P]),
+    "egs_score_select": (_ST, [_PS, ctypes.c_int32, ctypes.c_int32, ctypes.c_float,
+                               ctypes.POINTER(BudgetPolicyC), _P, _P, ctypes.c_int32, _P, _P, _P,
+                               _P, _P, _P, _P, ctypes.c_size_t, _P]),
     "egs_sparse_prefill_attn_workspace": (ctypes.c_size_t, [_PS]),
     "egs_sparse_prefill_attn": (_ST, [_PS, _P, _P, _P, _P, _P, ctypes.c_int32, _P, _P, _P,
                                       ctypes.c_size_t, _P]),

@@ -226,6 +226,39 @@ def select_blocks(shape: PrefillShape, block_scores: torch.Tensor, budget: torch
     return block_idx, block_cnt
 
 
+def score_select(shape: PrefillShape, policy: BudgetPolicy, q: torch.Tensor, k: torch.Tensor,
+                 k_max: int, kind: int = L.EGS_SHANNON, renyi_alpha: float = 2.0,
+                 pool: int = L.EGS_POOL_MEAN_PROBE, out: Optional[dict] = None,
+                 workspace: Optional[torch.Tensor] = None):
+    """entropy_score -> allocate_budget -> select_blocks in one call.  Returns
+    dict(block_scores, entropy, head_is_rigid, budget, block_idx, block_cnt);
+    `out` may supply any of these tensors."""
+    s = shape
+    dev = q.device
+    _need(q, "q", (s.n_q_heads, s.seq_len, s.head_dim), s.dtype)
+    _need(k, "k", (s.n_kv_heads, s.seq_len, s.head_dim), s.dtype, dev)
+    Hq, CS, CB = s.n_q_heads, s.n_segments, s.n_blocks
+    want = {"block_scores": ((Hq, CS, CB), torch.float32), "entropy": ((Hq, CS), torch.float32),
+            "head_is_rigid": ((Hq,), torch.int8), "budget": ((Hq, CS), torch.int32),
+            "block_idx": ((Hq, CS, k_max), torch.int32), "block_cnt": ((Hq, CS), torch.int32)}
+    res = dict(out or {})
+    for name, (shp, dt) in want.items():
+        if res.get(name) is None:
+            res[name] = _empty(shp, dt, dev)
+        _need(res[name], name, shp, dt, dev)
+    sc, pc = s.c(), policy.c()
+    wsb = L.LIB.egs_entropy_score_workspace(ctypes.byref(sc))
+    if workspace is None:
+        workspace = _workspace(wsb, dev)
+    L.check(L.LIB.egs_score_select(ctypes.byref(sc), pool, kind, renyi_alpha, ctypes.byref(pc),
+                                   _ptr(q), _ptr(k), k_max, _ptr(res["block_scores"]),
+                                   _ptr(res["entropy"]), _ptr(res["head_is_rigid"]),
+                                   _ptr(res["budget"]), _ptr(res["block_idx"]),
+                                   _ptr(res["block_cnt"]), _ptr(workspace), workspace.numel(),
+                                   _stream(dev)))
+    return res
+
+
 def sparse_prefill_attn(shape: PrefillShape, q, k, v, block_idx, block_cnt,
                         out: Optional[torch.Tensor] = None, lse: Optional[torch.Tensor] = None,
                         return_lse: bool = False, workspace: Optional[torch.Tensor] = None):

@@ -234,12 +234,8 @@ egs_status egs_entropy_score_static(const egs_prefill_shape* shape, int32_t pool
                     "entropy_score (static scratch) launch");
 }
 
-egs_status egs_allocate_budget(const egs_prefill_shape* shape, const egs_budget_policy* policy,
-                               const float* entropy, int8_t* head_is_rigid, int32_t* budget,
-                               hipStream_t stream) {
-  PrefillDims p;
-  egs_status st = check_prefill(shape, &p);
-  if (st != EGS_OK) return st;
+// budget policy checks shared by egs_allocate_budget and egs_score_select
+static egs_status check_policy(const egs_budget_policy* policy) {
   if (policy == nullptr) return fail(EGS_EINVAL, "policy is NULL");
   const egs_budget_policy& pol = *policy;
   if (pol.mode < EGS_BUDGET_FIXED || pol.mode > EGS_BUDGET_ALG3)
@@ -267,11 +263,62 @@ egs_status egs_allocate_budget(const egs_prefill_shape* shape, const egs_budget_
         return fail(EGS_EINVAL, "ALG3 needs base_tokens > 0, finite alpha / delta_t, e_t > 0");
       break;
   }
+  return EGS_OK;
+}
+
+egs_status egs_allocate_budget(const egs_prefill_shape* shape, const egs_budget_policy* policy,
+                               const float* entropy, int8_t* head_is_rigid, int32_t* budget,
+                               hipStream_t stream) {
+  PrefillDims p;
+  egs_status st = check_prefill(shape, &p);
+  if (st != EGS_OK) return st;
+  if ((st = check_policy(policy)) != EGS_OK) return st;
   if ((st = need(entropy, "entropy", 4)) != EGS_OK) return st;
   if ((st = need(head_is_rigid, "head_is_rigid", 1)) != EGS_OK) return st;
   if ((st = need(budget, "budget", 4)) != EGS_OK) return st;
-  return hip_status(egs::launch_budget(p, pol, entropy, head_is_rigid, budget, stream),
+  return hip_status(egs::launch_budget(p, *policy, entropy, head_is_rigid, budget, stream),
                     "budget launch");
+}
+
+egs_status egs_score_select(const egs_prefill_shape* shape, int32_t pool_kind,
+                            int32_t entropy_kind, float renyi_alpha,
+                            const egs_budget_policy* policy, const void* q, const void* k,
+                            int32_t k_max, float* block_scores, float* entropy,
+                            int8_t* head_is_rigid, int32_t* budget, int32_t* block_idx,
+                            int32_t* block_cnt, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream) {
+  PrefillDims p;
+  int kind;
+  egs_status st = check_score(shape, pool_kind, entropy_kind, renyi_alpha, q, k, block_scores,
+                              entropy, &p, &kind);
+  if (st != EGS_OK) return st;
+  if ((st = check_policy(policy)) != EGS_OK) return st;
+  if (k_max < 1 || k_max > p.CB)
+    return fail(EGS_EINVAL, "k_max (%d) must be in [1, C_B = %d]", k_max, p.CB);
+  if ((st = need(head_is_rigid, "head_is_rigid", 1)) != EGS_OK) return st;
+  if ((st = need(budget, "budget", 4)) != EGS_OK) return st;
+  if ((st = need(block_idx, "block_idx", 4)) != EGS_OK) return st;
+  if ((st = need(block_cnt, "block_cnt", 4)) != EGS_OK) return st;
+  if ((st = need(workspace, "workspace", kWsAlign)) != EGS_OK) return st;
+  const size_t wsb = egs::score_workspace_bytes(p);
+  if (workspace_bytes < wsb)
+    return fail(EGS_EWORKSPACE, "workspace of %zu bytes is below the %zu required",
+                workspace_bytes, wsb);
+  hipError_t e;
+  egs::EntropyParts parts{nullptr, 0, 1};
+  if (pool_kind == EGS_POOL_MAXMIN) {
+    e = egs::launch_entropy_score_maxmin(p, q, k, kind, renyi_alpha, block_scores, entropy,
+                                         workspace, stream);
+  } else {
+    e = egs::launch_entropy_score(p, q, k, kind, renyi_alpha, block_scores, nullptr, workspace,
+                                  stream);
+    parts = egs::entropy_parts(p, workspace);
+  }
+  if (e != hipSuccess) return hip_status(e, "score_select scoring launch");
+  return hip_status(egs::launch_budget_select(p, *policy, parts, kind, renyi_alpha, entropy,
+                                              block_scores, k_max, head_is_rigid, budget,
+                                              block_idx, block_cnt, stream),
+                    "score_select budget / select launch");
 }
 
 egs_status egs_select_blocks(const egs_prefill_shape* shape, const float* block_scores,

@@ -82,6 +82,15 @@ hipError_t launch_entropy_score(const PrefillDims& p, const void* q, const void*
 hipError_t launch_entropy_score_static(const PrefillDims& p, bool maxmin, const void* q,
                                        const void* k, int kind, float alpha, float* scores,
                                        float* entropy, hipStream_t st);
+// With entropy == nullptr, launch_entropy_score stops after the mass pass;
+// the per-(head, segment, piece) entropy partial sums are then in the
+// workspace at entropy_parts(p, ws).part, [Hq, C_S, npc] floats, piece c of
+// segment s covering blocks c * pc .. (the first ceil(C_B(s) / pc) count).
+struct EntropyParts {
+  const float* part;
+  int npc, pc;
+};
+EntropyParts entropy_parts(const PrefillDims& p, const void* ws);
 // The same outputs from the max / min representatives (maxmin.hip); its
 // workspace need is included in score_workspace_bytes.
 size_t maxmin_workspace_bytes(const PrefillDims& p);
@@ -96,6 +105,14 @@ hipError_t launch_budget(const PrefillDims& p, const egs_budget_policy& pol,
 hipError_t launch_select(const PrefillDims& p, const float* scores,
                          const int32_t* budget, int k_max, int32_t* idx,
                          int32_t* cnt, hipStream_t st);
+// K3 + K4 in one launch, after the scoring kernels: every (head, segment)
+// workgroup forms its head's entropies (from the partials when parts.part is
+// set, writing `entropy`; else reading `entropy`), class and budgets with the
+// arithmetic of launch_budget, then selects as launch_select.
+hipError_t launch_budget_select(const PrefillDims& p, const egs_budget_policy& pol,
+                                EntropyParts parts, int kind, float alpha, float* entropy,
+                                const float* scores, int k_max, int8_t* rigid,
+                                int32_t* budget, int32_t* idx, int32_t* cnt, hipStream_t st);
 // K5: block-sparse causal GQA attention (workspace: the packed V^T tiles).
 size_t sparse_attn_workspace_bytes(const PrefillDims& p);
 hipError_t launch_sparse_attn(const PrefillDims& p, const void* q, const void* k,

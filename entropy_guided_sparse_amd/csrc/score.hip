@@ -560,6 +560,8 @@ __global__ __launch_bounds__(256) void probe_entropy_kernel(const float* __restr
 // ---------------------------------------------------------------------------
 // launcher
 // ---------------------------------------------------------------------------
+// entropy == nullptr: stop after the mass pass, leaving the per-piece entropy
+// partials in the workspace for a later kernel to finish
 template <typename T>
 static hipError_t score_dispatch(const PrefillDims& p, const ScoreLayout& ly, const void* q,
                                  const void* k, char* ws, int kind, float alpha, float* scores,
@@ -601,6 +603,7 @@ static hipError_t score_dispatch(const PrefillDims& p, const ScoreLayout& ly, co
 #undef EGS_POOL
 #undef EGS_STATS
 #undef EGS_MASS
+  if (entropy == nullptr) return hipSuccess;
   probe_entropy_kernel<<<(p.Hq * p.CS + 255) / 256, 256, 0, st>>>(en, p.Hq, p.CS, ly.npc,
                                                                   p.LS / p.LB, kind, alpha,
                                                                   entropy);
@@ -615,6 +618,15 @@ hipError_t launch_entropy_score(const PrefillDims& p, const void* q, const void*
   return p.dtype == EGS_F32
              ? score_dispatch<float>(p, ly, q, k, w, kind, alpha, scores, entropy, st)
              : score_dispatch<bf16>(p, ly, q, k, w, kind, alpha, scores, entropy, st);
+}
+
+EntropyParts entropy_parts(const PrefillDims& p, const void* ws) {
+  const ScoreLayout ly = score_layout(p);
+  EntropyParts e;
+  e.part = reinterpret_cast<const float*>(static_cast<const char*>(ws) + ly.ent);
+  e.npc = ly.npc;
+  e.pc = PC;
+  return e;
 }
 
 // ---------------------------------------------------------------------------

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define EGS_ABI_VERSION 5
+#define EGS_ABI_VERSION 6
 
 typedef enum {
   EGS_OK = 0,
@@ -199,6 +199,26 @@ egs_status egs_select_blocks(const egs_prefill_shape* shape,
                              const float* block_scores, const int32_t* budget,
                              int32_t k_max, int32_t* block_idx,
                              int32_t* block_cnt, hipStream_t stream);
+
+/* ---------------------------------------------------------------------------
+ * Steps 1-8 in one call: egs_entropy_score, egs_allocate_budget and
+ * egs_select_blocks with the same arguments, checks and bit-identical
+ * outputs ([EI] Sec. 4.2, Alg. 3 and App. A eqs. (1)-(2)), enqueued as
+ * fewer kernels: the entropies, head classes and budgets are formed inside
+ * the selection kernel (each (head, segment) workgroup recomputes its head's
+ * entropies from the scoring pass's partial sums), so no separate entropy or
+ * budget launch follows the scoring kernels.
+ *   workspace: >= egs_entropy_score_workspace(shape) bytes, 256-byte aligned.
+ *   Outputs as the three calls: block_scores, entropy, head_is_rigid, budget,
+ *   block_idx, block_cnt.
+ * ------------------------------------------------------------------------- */
+egs_status egs_score_select(const egs_prefill_shape* shape, int32_t pool_kind,
+                            int32_t entropy_kind, float renyi_alpha,
+                            const egs_budget_policy* policy, const void* q, const void* k,
+                            int32_t k_max, float* block_scores, float* entropy,
+                            int8_t* head_is_rigid, int32_t* budget, int32_t* block_idx,
+                            int32_t* block_cnt, void* workspace, size_t workspace_bytes,
+                            hipStream_t stream);
 
 /* ---------------------------------------------------------------------------
  * Steps 9-10: block-sparse causal GQA attention over the selected blocks.

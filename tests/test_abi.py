@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.LIB.egs_abi_version() == 5
+    assert L.LIB.egs_abi_version() == 6
     for st in range(5):
         assert L.LIB.egs_status_string(st).decode().startswith("EGS_")
 
@@ -348,3 +348,25 @@ def test_entropy_score_static_rejects_large_shapes(L):
                                           None) == L.EGS_EINVAL
     assert L.LIB.egs_entropy_score_static(ctypes.byref(sc), 0, 0, 2.0, None, FAKE, FAKE, FAKE,
                                           None) == L.EGS_EINVAL
+
+
+def test_score_select_errors(L):
+    sc = _shape(L)
+    ws = L.LIB.egs_entropy_score_workspace(ctypes.byref(sc))
+    good = L.BudgetPolicyC(mode=L.EGS_BUDGET_FIXED, frac=0.25, entropy_threshold=0.5)
+
+    def call(pol=good, k_max=8, wsb=ws, pool=0, kind=0, q=FAKE, rig=FAKE):
+        return L.LIB.egs_score_select(ctypes.byref(sc), pool, kind, 2.0,
+                                      None if pol is None else ctypes.byref(pol), q, FAKE, k_max,
+                                      FAKE, FAKE, rig, FAKE, FAKE, FAKE, FAKE, wsb, None)
+
+    assert call(pol=None) == L.EGS_EINVAL
+    assert call(pol=L.BudgetPolicyC(mode=9, entropy_threshold=0.5)) == L.EGS_EINVAL
+    assert call(pol=L.BudgetPolicyC(mode=L.EGS_BUDGET_FIXED, frac=-1.0)) == L.EGS_EINVAL
+    assert call(k_max=0) == L.EGS_EINVAL
+    assert call(k_max=33) == L.EGS_EINVAL            # C_B = 32
+    assert call(wsb=ws - 1) == L.EGS_EWORKSPACE
+    assert call(pool=5) == L.EGS_EINVAL
+    assert call(q=None) == L.EGS_EINVAL
+    assert call(rig=None) == L.EGS_EINVAL
+    assert "rigid" in L.LIB.egs_last_error().decode()
