@@ -60,12 +60,15 @@ __device__ __forceinline__ void pin_vgpr(float& x) { asm volatile("" : "+v"(x));
 constexpr int RT_CK = 1024;   // keys per span (the pass 1 / pass 2 work unit)
 constexpr int RT_KT = 64;     // keys per LDS stage
 constexpr int SEL_T = 1024;   // threads of the select kernel
+constexpr int SEL_CH = 16384; // keys per chunk of the split top-k
 constexpr int DA_SPL_MIN = 192;   // kept entries per decode-attention split: the
 constexpr int DA_SPL_MAX = 512;   // range the launcher chooses from (multiples of 64)
 
 struct RetainLayout {
-  size_t stat_m, stat_l, row_m, row_inv, mass, ent, weight, mu, qsum, tstats, total;
-  int nch;   // 1024-key spans of the cache
+  size_t stat_m, stat_l, row_m, row_inv, mass, ent, weight, mu, qsum, tstats;
+  size_t sel_hist, sel_state, sel_cnt, total;
+  int nch;    // 1024-key spans of the cache
+  int nsel;   // key chunks of the split top-k (histogram and compaction)
 };
 
 static size_t align_up(size_t x) {
@@ -92,6 +95,11 @@ static RetainLayout retain_layout(const DecodeDims& p) {
   o.mu = take((size_t)p.B * p.Hkv * p.L * 4);
   o.qsum = take((size_t)p.B * p.Hkv * p.D * 4);
   o.tstats = take((size_t)p.B * 2 * 4);
+  o.nsel = (p.L + SEL_CH - 1) / SEL_CH;
+  const size_t slices = (size_t)p.B * p.Hkv;
+  o.sel_hist = take(slices * o.nsel * 4096 * 4);
+  o.sel_state = take(slices * 4 * 4);
+  o.sel_cnt = take(slices * o.nsel * 2 * 4);
   o.total = off;
   return o;
 }
@@ -471,9 +479,12 @@ __global__ __launch_bounds__(256) void obs_pass_kernel(
           zn[rt] = MASS ? mfma32(qf[rt][c], fr[c], zn[rt]) : mfma32(fr[c], qf[rt][c], zn[rt]);
 #pragma unroll
         for (int rt = 0; rt < RT; ++rt) {
-          float acc = 0.f;
+          // the run's terms are positive, so starting from the first term
+          // gives the same sum as starting from zero
+          float acc = fast_exp2(__builtin_fmaf(zc[rt][c * EPS], sl2,
+                                               MASS ? -rm[rt][c * EPS] : -m[rt]));
 #pragma unroll
-          for (int q = 0; q < EPS; ++q) {
+          for (int q = 1; q < EPS; ++q) {
             const int i = c * EPS + q;
             acc += fast_exp2(__builtin_fmaf(zc[rt][i], sl2, MASS ? -rm[rt][i] : -m[rt]));
           }
@@ -499,19 +510,37 @@ __global__ __launch_bounds__(256) void obs_pass_kernel(
         for (int rt = 0; rt < RT; ++rt) sm[rt] = part[rt][0];
       }
     };
-    // the same exponentials with no MFMAs beside them (the span's last tile)
+    // the same exponentials, summed in the same order, with no MFMAs beside
+    // them (the span's last tile)
     auto tail = [&](const floatx16 (&zc)[RT], float (&sm)[RT]) {
+      float part[RT][NC];
 #pragma unroll
-      for (int rt = 0; rt < RT; ++rt) {
-        float acc = 0.f;
+      for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
-        for (int i = 0; i < 16; ++i)
-          acc += fast_exp2(__builtin_fmaf(zc[rt][i], sl2, MASS ? -rm[rt][i] : -m[rt]));
-        sm[rt] = acc;
-      }
+        for (int c = 0; c < NC; ++c) {
+          float acc = fast_exp2(__builtin_fmaf(zc[rt][c * EPS], sl2,
+                                               MASS ? -rm[rt][c * EPS] : -m[rt]));
+#pragma unroll
+          for (int q = 1; q < EPS; ++q) {
+            const int i = c * EPS + q;
+            acc += fast_exp2(__builtin_fmaf(zc[rt][i], sl2, MASS ? -rm[rt][i] : -m[rt]));
+          }
+          part[rt][c] = acc;
+        }
+#pragma unroll
+      for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+        for (int n = NC; n > 1; n >>= 1)
+#pragma unroll
+          for (int i = 0; i < n / 2; ++i) part[rt][i] += part[rt][i + n / 2];
       if constexpr (MASS) {
+        float t = part[0][0];
 #pragma unroll
-        for (int rt = 1; rt < RT; ++rt) sm[0] += sm[rt];
+        for (int rt = 1; rt < RT; ++rt) t += part[rt][0];
+        sm[0] = t;
+      } else {
+#pragma unroll
+        for (int rt = 0; rt < RT; ++rt) sm[rt] = part[rt][0];
       }
     };
     // the first tile of the span: its logits alone
@@ -1043,6 +1072,255 @@ __global__ __launch_bounds__(SEL_T) void retain_select_kernel(
   }
 }
 
+// ---------------------------------------------------------------------------
+// The same top-n_keep and compaction split over many workgroups (the kv_retain
+// rows are long: one workgroup per row leaves most of the chip idle).  Per
+// row, state = {prefix, mask, kr, flags}.  Three radix passes of 12 / 12 / 8
+// bits: rsel_hist counts one digit over a chunk of the candidates into its
+// own 4096-bin histogram in global memory (no atomics across workgroups),
+// rsel_digit sums the chunks' histograms and fixes the digit; then
+// rsel_count counts the kept and tied entries of every chunk of [0, L) and
+// rsel_write places the chunk's entries after the earlier chunks' counts.
+// ---------------------------------------------------------------------------
+__device__ __forceinline__ void rsel_pass_bits(int pass, int& sh, int& nb) {
+  sh = pass == 0 ? 20 : (pass == 1 ? 8 : 0);
+  nb = pass == 2 ? 256 : 4096;
+}
+
+__global__ __launch_bounds__(SEL_T) void rsel_hist_kernel(const float* __restrict__ mu, int L,
+                                                          int c_lo, int c_hi, int nsel,
+                                                          int pass,
+                                                          const int32_t* __restrict__ state,
+                                                          int32_t* __restrict__ gh) {
+  __shared__ int hist[4096];
+  const int c = blockIdx.x, row = blockIdx.y, tid = threadIdx.x;
+  int sh, nb;
+  rsel_pass_bits(pass, sh, nb);
+  uint32_t prefix = 0, mask = 0;
+  if (pass > 0) {
+    prefix = (uint32_t)state[row * 4];
+    mask = (uint32_t)state[row * 4 + 1];
+  }
+  for (int i = tid; i < 4096; i += SEL_T) hist[i] = 0;
+  __syncthreads();
+  const int per = (c_hi - c_lo + nsel - 1) / nsel;
+  const int t_lo = c_lo + c * per, t_hi = min(c_hi, t_lo + per);
+  const float* m = mu + (size_t)row * L;
+  for (int t0 = t_lo; t0 < t_hi; t0 += SEL_T * SEL_U) {
+    uint32_t kv[SEL_U];
+    // unconditional clamped loads, all in flight before the first use
+#pragma unroll
+    for (int u = 0; u < SEL_U; ++u) kv[u] = orderable(m[min(t0 + u * SEL_T + tid, t_hi - 1)]);
+#pragma unroll
+    for (int u = 0; u < SEL_U; ++u)
+      if (t0 + u * SEL_T + tid < t_hi && (kv[u] & mask) == prefix)
+        atomicAdd(&hist[(kv[u] >> sh) & (uint32_t)(nb - 1)], 1);
+  }
+  __syncthreads();
+  int32_t* out = gh + ((size_t)row * nsel + c) * 4096;
+  for (int i = tid; i < nb; i += SEL_T) out[i] = hist[i];
+}
+
+__global__ __launch_bounds__(SEL_T) void rsel_digit_kernel(int nsel, int n_keep, int pass,
+                                                           const int32_t* __restrict__ gh,
+                                                           int32_t* __restrict__ state) {
+  __shared__ int ired[SEL_T / 64];
+  __shared__ int sh_digit, sh_above;
+  const int row = blockIdx.x, tid = threadIdx.x;
+  int sh, nb;
+  rsel_pass_bits(pass, sh, nb);
+  uint32_t prefix = 0, mask = 0;
+  int kr = n_keep;
+  if (pass > 0) {
+    prefix = (uint32_t)state[row * 4];
+    mask = (uint32_t)state[row * 4 + 1];
+    kr = state[row * 4 + 2];
+  }
+  // thread tid owns digits nb-1-4*tid .. nb-4-4*tid (descending), summed over the chunks
+  const int d0 = nb - 1 - 4 * tid;
+  const bool own = d0 >= 3;
+  int cnt4[4] = {0, 0, 0, 0};
+  if (own) {
+    const int32_t* h = gh + (size_t)row * nsel * 4096;
+    for (int c = 0; c < nsel; ++c)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) cnt4[q] += h[(size_t)c * 4096 + d0 - q];
+  }
+  const int tot = cnt4[0] + cnt4[1] + cnt4[2] + cnt4[3];
+  const int excl = block_excl_scan_1024(tot, ired);
+  if (own && excl < kr && kr <= excl + tot) {
+    int run = excl, dd = d0 - 3;
+#pragma unroll
+    for (int q = 0; q < 3; ++q) {
+      if (run + cnt4[q] >= kr) {
+        dd = d0 - q;
+        break;
+      }
+      run += cnt4[q];
+    }
+    sh_digit = dd;
+    sh_above = run;
+  }
+  __syncthreads();
+  if (tid == 0) {
+    state[row * 4] = (int32_t)(prefix | ((uint32_t)sh_digit << sh));
+    state[row * 4 + 1] = (int32_t)(mask | ((uint32_t)(nb - 1) << sh));
+    state[row * 4 + 2] = kr - sh_above;
+  }
+}
+
+// per chunk of [0, L): entries kept for sure (non-candidates when partial,
+// every entry when keep_all, keys above T) and keys equal to T
+__global__ __launch_bounds__(SEL_T) void rsel_count_kernel(const float* __restrict__ mu, int L,
+                                                           int c_lo, int c_hi, int keep_all,
+                                                           int partial,
+                                                           const int32_t* __restrict__ state,
+                                                           int32_t* __restrict__ cnt) {
+  __shared__ int ired[SEL_T / 64];
+  const int c = blockIdx.x, row = blockIdx.y, tid = threadIdx.x, nsel = gridDim.x;
+  const uint32_t T = partial ? (uint32_t)state[row * 4] : 0u;
+  const int r0 = c * SEL_CH, rn = min(SEL_CH, L - r0);
+  const float* m = mu + (size_t)row * L + r0;
+  int n_sel = 0, n_eq = 0;
+  constexpr int PER = SEL_CH / SEL_T;
+  uint32_t kk[PER];
+#pragma unroll
+  for (int e = 0; e < PER; ++e) kk[e] = orderable(m[min(e * SEL_T + tid, rn - 1)]);
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int j = e * SEL_T + tid, t = r0 + j;
+    if (j < rn) {
+      const bool cand = t >= c_lo && t < c_hi;
+      if (!cand || keep_all) {
+        ++n_sel;
+      } else if (partial) {
+        n_sel += kk[e] > T;
+        n_eq += kk[e] == T;
+      }
+    }
+  }
+  const int packed = block_sum_1024((n_sel << 16) | n_eq, ired);
+  if (tid == 0) {
+    cnt[((size_t)row * nsel + c) * 2] = packed >> 16;
+    cnt[((size_t)row * nsel + c) * 2 + 1] = packed & 0xFFFF;
+  }
+}
+
+__global__ __launch_bounds__(SEL_T) void rsel_write_kernel(const float* __restrict__ mu, int L,
+                                                           int c_lo, int c_hi, int keep_all,
+                                                           int partial, int n_total,
+                                                           const int32_t* __restrict__ state,
+                                                           const int32_t* __restrict__ cnt,
+                                                           int32_t* __restrict__ keep_idx) {
+  __shared__ uint32_t keys[SEL_CH + SEL_CH / 16];
+  auto kslot = [](int j) { return j + (j >> 4); };
+  __shared__ int ired[SEL_T / 64];
+  __shared__ int sh_base_sel, sh_base_eq;
+  const int c = blockIdx.x, row = blockIdx.y, tid = threadIdx.x, nsel = gridDim.x;
+  const uint32_t T = partial ? (uint32_t)state[row * 4] : 0u;
+  const int kr = partial ? state[row * 4 + 2] : 0;
+  if (tid == 0) {
+    int bs = 0, be = 0;
+    for (int q = 0; q < c; ++q) {
+      bs += cnt[((size_t)row * nsel + q) * 2];
+      be += cnt[((size_t)row * nsel + q) * 2 + 1];
+    }
+    sh_base_sel = bs;
+    sh_base_eq = be;
+  }
+  const int r0 = c * SEL_CH, rn = min(SEL_CH, L - r0);
+  const float* m = mu + (size_t)row * L + r0;
+  {
+    uint32_t kk[SEL_CH / SEL_T];
+#pragma unroll
+    for (int e = 0; e < SEL_CH / SEL_T; ++e) kk[e] = orderable(m[min(e * SEL_T + tid, rn - 1)]);
+#pragma unroll
+    for (int e = 0; e < SEL_CH / SEL_T; ++e)
+      if (e * SEL_T + tid < rn) keys[kslot(e * SEL_T + tid)] = kk[e];
+  }
+  __syncthreads();
+  constexpr int PER = SEL_CH / SEL_T;
+  const int j0 = tid * PER;
+  int n_sel = 0, n_eq = 0;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int j = j0 + e, t = r0 + j;
+    if (j < rn) {
+      const bool cand = t >= c_lo && t < c_hi;
+      if (!cand || keep_all) {
+        ++n_sel;
+      } else if (partial) {
+        const uint32_t kj = keys[kslot(j)];
+        n_sel += kj > T;
+        n_eq += kj == T;
+      }
+    }
+  }
+  const int packed = block_excl_scan_1024((n_sel << 16) | n_eq, ired);
+  int es = sh_base_eq + (packed & 0xFFFF);
+  int pos = sh_base_sel + (packed >> 16) + min(es, kr);
+  int32_t* out = keep_idx + (size_t)row * n_total;
+#pragma unroll
+  for (int e = 0; e < PER; ++e) {
+    const int j = j0 + e, t = r0 + j;
+    if (j < rn) {
+      const bool cand = t >= c_lo && t < c_hi;
+      bool take;
+      if (!cand || keep_all) {
+        take = true;
+      } else if (!partial) {
+        take = false;
+      } else if (keys[kslot(j)] > T) {
+        take = true;
+      } else if (keys[kslot(j)] == T) {
+        take = es < kr;
+        ++es;
+      } else {
+        take = false;
+      }
+      if (take) {
+        if (pos < n_total) out[pos] = t;
+        ++pos;
+      }
+    }
+  }
+}
+
+// the kv_retain top-k: the split kernels for long rows, the one-workgroup
+// kernel otherwise
+static hipError_t launch_retain_topk(const DecodeDims& p, const RetainLayout& lay, char* ws,
+                                     const float* mu, int32_t* keep_idx, hipStream_t st) {
+  const int rows = p.B * p.Hkv;
+  if (p.L < 4 * SEL_CH) {
+    retain_select_kernel<<<rows, SEL_T, 0, st>>>(mu, p.L, p.n_sink, p.n_recent, p.n_keep,
+                                                 p.n_total, keep_idx);
+    return hipGetLastError();
+  }
+  int32_t* gh = reinterpret_cast<int32_t*>(ws + lay.sel_hist);
+  int32_t* state = reinterpret_cast<int32_t*>(ws + lay.sel_state);
+  int32_t* cnt = reinterpret_cast<int32_t*>(ws + lay.sel_cnt);
+  const int c_lo = p.n_sink, c_hi = p.L - p.n_recent;
+  const bool keep_all = (long long)p.n_sink + p.n_recent + p.n_keep >= p.L;
+  const bool partial = !keep_all && p.n_keep > 0;
+  hipError_t e;
+  if (partial) {
+    for (int pass = 0; pass < 3; ++pass) {
+      rsel_hist_kernel<<<dim3(lay.nsel, rows), SEL_T, 0, st>>>(mu, p.L, c_lo, c_hi, lay.nsel,
+                                                               pass, state, gh);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+      rsel_digit_kernel<<<rows, SEL_T, 0, st>>>(lay.nsel, p.n_keep, pass, gh, state);
+      if ((e = hipGetLastError()) != hipSuccess) return e;
+    }
+  }
+  rsel_count_kernel<<<dim3(lay.nsel, rows), SEL_T, 0, st>>>(mu, p.L, c_lo, c_hi, keep_all ? 1 : 0,
+                                                            partial ? 1 : 0, state, cnt);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  rsel_write_kernel<<<dim3(lay.nsel, rows), SEL_T, 0, st>>>(mu, p.L, c_lo, c_hi,
+                                                            keep_all ? 1 : 0, partial ? 1 : 0,
+                                                            p.n_total, state, cnt, keep_idx);
+  return hipGetLastError();
+}
+
 // copy the kept K / V rows: one thread per 16 bytes
 template <int D>
 __global__ __launch_bounds__(256) void gather_kv_kernel(const bf16* __restrict__ K,
@@ -1180,9 +1458,7 @@ hipError_t launch_kv_retain(const DecodeDims& p, const egs_retain_params& prm, c
         (float)prm.info_alpha, p.Hq, p.Hkv, p.r, p.L, mu, scores);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  retain_select_kernel<<<p.B * p.Hkv, SEL_T, 0, st>>>(mu, p.L, p.n_sink, p.n_recent, p.n_keep,
-                                                       p.n_total, keep_idx);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  if ((e = launch_retain_topk(p, lay, ws, mu, keep_idx, st)) != hipSuccess) return e;
   if (k_out != nullptr) {
     const long long units = (long long)p.B * p.Hkv * p.n_total * (p.D / 8);
     const unsigned blocks = (unsigned)((units + 255) / 256);

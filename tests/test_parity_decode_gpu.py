@@ -235,3 +235,36 @@ def test_decode_attention_every_split_size(api, n_total):
     ma, rel = attn_errors(out.float().cpu().numpy(), ref)
     log(f"  max|d|={ma:.3e} relL2={rel:.3e}")
     assert ma <= ATTN_MAX_ABS and rel <= ATTN_REL_L2
+
+
+@pytest.mark.parametrize("L,n_keep", [(65536, 300), (70001, 5000), (70001, 0), (66000, 66000)])
+def test_retain_split_topk_edges(api, L, n_keep):
+    """Cache rows of 65,536 entries and more take the select split over many
+    workgroups (per-chunk digit histograms, then chunked compaction).  Zero
+    keys tie every candidate exactly, so the keep set is the sinks, the first
+    n_keep candidates by index and the recent window; n_keep = 0 keeps sinks
+    and recent only, and n_keep >= L keeps everything (as the oracle)."""
+    B, Hq, Hkv, d, W = 1, 4, 1, 128, 64
+    n_sink, n_recent = 4, 256
+    log(f"[retain split top-k] L={L} keep={n_keep}")
+    rng = np.random.default_rng(13)
+    q_obs = synth.round_to_bf16(rng.standard_normal((B, Hq, W, d)).astype(np.float32))
+    k = np.zeros((B, Hkv, L, d), dtype=np.int16)
+    v = synth.round_to_bf16(rng.standard_normal((B, Hkv, L, d)).astype(np.float32))
+    shape = api.DecodeShape(B, Hq, Hkv, d, L, W, n_sink, n_recent, n_keep)
+    res = api.kv_retain(shape, api.RetainParams(), dev_tensor(q_obs, "bf16"),
+                        dev_tensor(k, "bf16"), dev_tensor(v, "bf16"))
+    torch.cuda.synchronize()
+    keep = res["keep_idx"].cpu().numpy()[0, 0]
+    if n_sink + n_recent + n_keep >= L:
+        want = np.arange(L)
+    else:
+        want = np.array(list(range(n_sink)) + list(range(n_sink, n_sink + n_keep)) +
+                        list(range(L - n_recent, L)))
+    np.testing.assert_array_equal(keep, want)
+    o_keep, _, _ = O.kv_retain_slice(synth.bf16_bits_to_f32(q_obs)[0], np.zeros((L, d)),
+                                     n_sink, n_recent, n_keep)
+    np.testing.assert_array_equal(o_keep, want)
+    # the kept rows are gathered bit for bit
+    got_v = res["v_out"].cpu().view(torch.int16).numpy().view(np.uint16)[0, 0]
+    np.testing.assert_array_equal(got_v, v[0, 0][want].view(np.uint16))
