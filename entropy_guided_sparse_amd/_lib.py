@@ -19,7 +19,7 @@ EGS_POOL_MEAN_PROBE, EGS_POOL_MAXMIN = 0, 1
 EGS_BUDGET_FIXED, EGS_BUDGET_TWO_LEVEL, EGS_BUDGET_PROPORTIONAL, EGS_BUDGET_ALG3 = range(4)
 EGS_PAGE_GROUP, EGS_PAGE_LAYER_UNION, EGS_PAGE_HEAD_UNION = 0, 1, 2
 EGS_STATIC_SCRATCH_BYTES = 64 << 20
-ABI_VERSION = 6
+ABI_VERSION = 7
 
 
 class PrefillShapeC(ctypes.Structure):

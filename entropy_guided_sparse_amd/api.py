@@ -331,18 +331,39 @@ def kv_retain(shape: DecodeShape, params: RetainParams, q_obs, k_cache, v_cache,
             "scores": sco}
 
 
+def chunk_bounds_device(chunk_bounds, dev, limit: Optional[int] = None, nonempty: bool = True):
+    """The chunk bounds [k, 2] int32 as a device tensor.  A device tensor is
+    used as given (the library checks it on the device); host bounds are
+    checked here first (ascending, disjoint and ending at or before `limit`
+    when given, non-empty), with the library's error class and messages."""
+    import numpy as np
+    if isinstance(chunk_bounds, torch.Tensor) and chunk_bounds.device.type == "cuda":
+        b = chunk_bounds
+        if b.dtype != torch.int32 or not b.is_contiguous() or b.dim() != 2 or b.shape[1] != 2:
+            raise ValueError("chunk_bounds must be a contiguous int32 [k, 2] tensor")
+        return b
+    b = np.ascontiguousarray(np.asarray(chunk_bounds, dtype=np.int32).reshape(-1, 2))
+    prev = 0
+    for i, (lo, hi) in enumerate(b.tolist()):
+        if (limit is not None and (lo < prev or hi > limit)) or (nonempty and hi <= lo):
+            raise L.EgsError(L.EGS_EINVAL, f"EGS_EINVAL: chunk {i} = [{lo}, {hi}) is not "
+                             f"ascending, disjoint, non-empty and before the observers "
+                             f"(T - W = {limit})")
+        prev = hi
+    return torch.from_numpy(b).to(dev)
+
+
 def chunk_prune(shape: DecodeShape, q_obs, k, chunk_bounds, eps_s: float, lam: float,
                 eps: float, m0: int, target: int, zeta: float = 0.5, tau: float = 1.0,
                 want_row_mass: bool = False, workspace: Optional[torch.Tensor] = None):
     """Removal flags [k] int8, removed tokens [1] int32, priorities [k] and
-    (optionally) the row-chunk masses [k, Hq*W]; chunk_bounds is a host array
-    [k, 2] of int32 (begin, end)."""
-    import numpy as np
+    (optionally) the row-chunk masses [k, Hq*W]; chunk_bounds [k, 2] int32
+    (begin, end), on the host or the device."""
     s = shape
     dev = q_obs.device
     _need(q_obs, "q_obs", (s.n_q_heads, s.n_obs, s.head_dim), s.dtype)
     _need(k, "k", (s.n_kv_heads, s.cache_len, s.head_dim), s.dtype, dev)
-    b = np.ascontiguousarray(np.asarray(chunk_bounds, dtype=np.int32).reshape(-1, 2))
+    b = chunk_bounds_device(chunk_bounds, dev, limit=s.cache_len - s.n_obs)
     nk = b.shape[0]
     removed = _empty((nk,), torch.int8, dev)
     tokens = _empty((1,), torch.int32, dev)
@@ -354,7 +375,7 @@ def chunk_prune(shape: DecodeShape, q_obs, k, chunk_bounds, eps_s: float, lam: f
     if workspace is None:
         workspace = _workspace(wsb, dev)
     L.check(L.LIB.egs_chunk_prune(ctypes.byref(sc), ctypes.byref(pc), _ptr(q_obs), _ptr(k),
-                                  b.ctypes.data_as(ctypes.c_void_p), nk, _ptr(removed),
+                                  _ptr(b), nk, _ptr(removed),
                                   _ptr(tokens), _ptr(prio), _ptr(row_mass), _ptr(workspace),
                                   workspace.numel(), _stream(dev)))
     return removed, tokens, prio, row_mass
@@ -363,12 +384,11 @@ def chunk_prune(shape: DecodeShape, q_obs, k, chunk_bounds, eps_s: float, lam: f
 def prune_certificate(chunk_bounds, row_mass, row_price, eps: float, m0: int, t: float,
                       workspace: Optional[torch.Tensor] = None):
     """U(y, t) of a removal as a float64 device tensor [1]; row_mass [k, R]
-    and row_price [R] are float32 device tensors, chunk_bounds a host array
-    [k, 2] of int32."""
-    import numpy as np
-    b = np.ascontiguousarray(np.asarray(chunk_bounds, dtype=np.int32).reshape(-1, 2))
-    nk = b.shape[0]
+    and row_price [R] are float32 device tensors, chunk_bounds [k, 2] int32
+    on the host or the device."""
     dev = row_mass.device
+    b = chunk_bounds_device(chunk_bounds, dev)
+    nk = b.shape[0]
     if row_mass.dtype != torch.float32 or not row_mass.is_contiguous() or row_mass.dim() != 2 \
             or row_mass.shape[0] != nk:
         raise ValueError(f"row_mass must be contiguous float32 [{nk}, R]")
@@ -377,7 +397,7 @@ def prune_certificate(chunk_bounds, row_mass, row_price, eps: float, m0: int, t:
     out = _empty((1,), torch.float64, dev)
     if workspace is None:
         workspace = _workspace(L.LIB.egs_prune_certificate_workspace(nk), dev)
-    L.check(L.LIB.egs_prune_certificate(b.ctypes.data_as(ctypes.c_void_p), nk, R,
+    L.check(L.LIB.egs_prune_certificate(_ptr(b), nk, R,
                                         _ptr(row_mass), _ptr(row_price), eps, m0, t, _ptr(out),
                                         _ptr(workspace), workspace.numel(), _stream(dev)))
     return out

@@ -509,15 +509,7 @@ egs_status egs_chunk_prune(const egs_decode_shape* shape, const egs_prune_params
   if (q.m0 < 0 || q.target < 0) return fail(EGS_EINVAL, "m0 and target must be >= 0");
   if (!(q.zeta > 0.0 && q.zeta <= 1.0)) return fail(EGS_EINVAL, "zeta must be in (0, 1]");
   if (!(std::isfinite(q.tau) && q.tau > 0.0)) return fail(EGS_EINVAL, "tau must be > 0");
-  if (chunk_bounds == nullptr) return fail(EGS_EINVAL, "chunk_bounds is NULL");
-  int prev = 0;
-  for (int i = 0; i < n_chunks; ++i) {
-    const int b = chunk_bounds[2 * i], e = chunk_bounds[2 * i + 1];
-    if (b < prev || e <= b || e > p.L - p.W)
-      return fail(EGS_EINVAL, "chunk %d = [%d, %d) is not ascending, disjoint and before the "
-                  "observers (T - W = %d)", i, b, e, p.L - p.W);
-    prev = e;
-  }
+  if ((st = need(chunk_bounds, "chunk_bounds", 4)) != EGS_OK) return st;
   if ((st = need(q_obs, "q_obs", 16)) != EGS_OK) return st;
   if ((st = need(k, "k", 16)) != EGS_OK) return st;
   if ((st = need(removed, "removed", 1)) != EGS_OK) return st;
@@ -561,12 +553,8 @@ egs_status egs_prune_certificate(const int32_t* chunk_bounds, int32_t n_chunks, 
   if (!(std::isfinite(eps) && eps >= 0.0)) return fail(EGS_EINVAL, "eps must be >= 0");
   if (!(std::isfinite(t) && t >= 0.0)) return fail(EGS_EINVAL, "t must be >= 0");
   if (m0 < 0) return fail(EGS_EINVAL, "m0 must be >= 0");
-  if (chunk_bounds == nullptr) return fail(EGS_EINVAL, "chunk_bounds is NULL");
-  for (int i = 0; i < n_chunks; ++i)
-    if (chunk_bounds[2 * i + 1] <= chunk_bounds[2 * i])
-      return fail(EGS_EINVAL, "chunk %d = [%d, %d) is empty", i, chunk_bounds[2 * i],
-                  chunk_bounds[2 * i + 1]);
   egs_status st;
+  if ((st = need(chunk_bounds, "chunk_bounds", 4)) != EGS_OK) return st;
   if ((st = need(row_mass, "row_mass", 4)) != EGS_OK) return st;
   if ((st = need(row_price, "row_price", 4)) != EGS_OK) return st;
   if ((st = need(certificate, "certificate", 8)) != EGS_OK) return st;

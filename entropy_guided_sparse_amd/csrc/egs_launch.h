@@ -42,17 +42,17 @@ struct PruneArgs {
   int m0, target;
 };
 struct PruneLayout {
-  size_t retain, cid, bounds, segb, stats, mtab, seg_v, seg_m, total;
+  size_t retain, cid, bounds, bounds_ok, segb, stats, mtab, seg_v, seg_m, total;
 };
 constexpr int kMaxPruneChunks = 4096;
 constexpr int kMaxPruneRows = 8192;
 PruneLayout prune_layout(const DecodeDims& p, int k);
 size_t certificate_workspace_bytes(int k);
-hipError_t launch_prune_certificate(const int32_t* bounds_host, int k, int R, const float* m,
+hipError_t launch_prune_certificate(const int32_t* bounds, int k, int R, const float* m,
                                     const float* y, double eps, int m0, double t, double* out,
                                     void* workspace, hipStream_t st);
 hipError_t launch_chunk_prune(const DecodeDims& p, const PruneArgs& a, const void* q_obs,
-                              const void* k, const int32_t* bounds_host, int8_t* removed,
+                              const void* k, const int32_t* bounds, int8_t* removed,
                               int32_t* removed_tokens, float* prio, float* row_mass, void* workspace,
                               hipStream_t st);
 

@@ -1738,6 +1738,29 @@ hipError_t launch_decode_attn(const DecodeDims& p, const void* q_new, const void
 constexpr int PR_MAX_CHUNKS = 4096;
 constexpr int PR_MAX_ROWS = 8192;
 
+// The caller's chunk bounds (device memory) checked and copied: chunks must be
+// ascending, disjoint, non-empty and end at or before limit = T - W.  The copy
+// is clamped into that shape whatever the input, so every later index stays
+// in range; ok[0] records whether the input already had it (the scan reports
+// a failure through removed_tokens = -1 when it did not).  One thread: k is
+// at most a few thousand.
+__global__ __launch_bounds__(64) void chunk_bounds_kernel(const int32_t* __restrict__ in, int k,
+                                                          int limit, int32_t* __restrict__ out,
+                                                          int32_t* __restrict__ ok) {
+  if (threadIdx.x != 0) return;
+  int prev = 0, valid = 1;
+  for (int i = 0; i < k; ++i) {
+    const int b = in[2 * i], e = in[2 * i + 1];
+    if (b < prev || e <= b || e > limit) valid = 0;
+    const int bc = min(max(b, prev), limit);
+    const int ec = min(max(e, bc), limit);
+    out[2 * i] = bc;
+    out[2 * i + 1] = ec;
+    prev = ec;
+  }
+  ok[0] = valid;
+}
+
 // chunk id of every position (-1 outside the chunks); bounds [k][2] ascending
 __global__ __launch_bounds__(256) void chunk_of_kernel(const int32_t* __restrict__ bounds, int k,
                                                        int T, int32_t* __restrict__ cid) {
@@ -1892,7 +1915,16 @@ template <int RPT>
 __global__ __launch_bounds__(SEL_T) void prune_select_kernel(
     const float* __restrict__ stats, const int32_t* __restrict__ bounds, int k, int R,
     const float* __restrict__ m, float eps_s, float lam, float eps, int m0, int target,
-    float* __restrict__ prio, int8_t* __restrict__ removed, int32_t* __restrict__ removed_tokens) {
+    const int32_t* __restrict__ bounds_ok, float* __restrict__ prio,
+    int8_t* __restrict__ removed, int32_t* __restrict__ removed_tokens) {
+  if (bounds_ok[0] == 0) {   // the caller's chunks were not valid: nothing is removed
+    for (int i = threadIdx.x; i < k; i += SEL_T) {
+      removed[i] = 0;
+      prio[i] = __builtin_nanf("");
+    }
+    if (threadIdx.x == 0) *removed_tokens = -1;
+    return;
+  }
   __shared__ float key_s[PR_MAX_CHUNKS];
   __shared__ int key_n[PR_MAX_CHUNKS];
   __shared__ int key_i[PR_MAX_CHUNKS];
@@ -2082,6 +2114,7 @@ PruneLayout prune_layout(const DecodeDims& p, int k) {
   o.retain = take(retain_workspace_bytes(p));
   o.cid = take((size_t)p.L * sizeof(int32_t));
   o.bounds = take((size_t)2 * k * sizeof(int32_t));
+  o.bounds_ok = take(sizeof(int32_t));
   o.segb = take((size_t)(k + 1) * sizeof(int32_t));
   o.stats = take((size_t)2 * k * sizeof(float));
   o.mtab = take((size_t)k * p.Hq * p.W * sizeof(float));
@@ -2094,7 +2127,7 @@ PruneLayout prune_layout(const DecodeDims& p, int k) {
 }
 
 hipError_t launch_chunk_prune(const DecodeDims& p, const PruneArgs& a, const void* q_obs,
-                              const void* k, const int32_t* bounds_host, int8_t* removed,
+                              const void* k, const int32_t* bounds_in, int8_t* removed,
                               int32_t* removed_tokens, float* prio, float* row_mass, void* workspace,
                               hipStream_t st) {
   const PruneLayout ly = prune_layout(p, a.k);
@@ -2106,8 +2139,9 @@ hipError_t launch_chunk_prune(const DecodeDims& p, const PruneArgs& a, const voi
   float* stats = reinterpret_cast<float*>(w + ly.stats);
   float* m = row_mass != nullptr ? row_mass : reinterpret_cast<float*>(w + ly.mtab);
   const int R = p.Hq * p.W;
-  hipError_t e = hipMemcpyAsync(bounds, bounds_host, (size_t)2 * a.k * sizeof(int32_t),
-                                hipMemcpyHostToDevice, st);
+  int32_t* bounds_ok = reinterpret_cast<int32_t*>(w + ly.bounds_ok);
+  chunk_bounds_kernel<<<1, 64, 0, st>>>(bounds_in, a.k, p.L - p.W, bounds, bounds_ok);
+  hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   chunk_of_kernel<<<(p.L + 255) / 256, 256, 0, st>>>(bounds, a.k, p.L, cid);
   if ((e = hipGetLastError()) != hipSuccess) return e;
@@ -2151,7 +2185,8 @@ hipError_t launch_chunk_prune(const DecodeDims& p, const PruneArgs& a, const voi
   if ((e = hipGetLastError()) != hipSuccess) return e;
 #define EGS_PS(RPT)                                                                              \
   prune_select_kernel<RPT><<<1, SEL_T, 0, st>>>(stats, bounds, a.k, R, m, a.eps_s, a.lam, a.eps, \
-                                                a.m0, a.target, prio, removed, removed_tokens)
+                                                a.m0, a.target, bounds_ok, prio, removed,      \
+                                                removed_tokens)
   if (R <= SEL_T) EGS_PS(1);
   else if (R <= 2 * SEL_T) EGS_PS(2);
   else if (R <= 4 * SEL_T) EGS_PS(4);
@@ -2218,20 +2253,16 @@ __global__ __launch_bounds__(SEL_T) void cert_total_kernel(const double* __restr
 }
 
 size_t certificate_workspace_bytes(int k) {
-  return align_up((size_t)2 * k * sizeof(int32_t)) + align_up((size_t)k * sizeof(double));
+  return align_up((size_t)k * sizeof(double));
 }
 
-hipError_t launch_prune_certificate(const int32_t* bounds_host, int k, int R, const float* m,
+hipError_t launch_prune_certificate(const int32_t* bounds, int k, int R, const float* m,
                                     const float* y, double eps, int m0, double t, double* out,
                                     void* workspace, hipStream_t st) {
-  char* w = static_cast<char*>(workspace);
-  int32_t* bounds = reinterpret_cast<int32_t*>(w);
-  double* hinge = reinterpret_cast<double*>(w + align_up((size_t)2 * k * sizeof(int32_t)));
-  hipError_t e = hipMemcpyAsync(bounds, bounds_host, (size_t)2 * k * sizeof(int32_t),
-                                hipMemcpyHostToDevice, st);
-  if (e != hipSuccess) return e;
+  double* hinge = static_cast<double*>(workspace);
   cert_chunk_kernel<<<k, 256, 0, st>>>(bounds, m, y, R, t, hinge);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
   cert_total_kernel<<<1, SEL_T, 0, st>>>(hinge, k, y, R, eps, m0, t, out);
   return hipGetLastError();
 }

@@ -47,7 +47,7 @@
 extern "C" {
 #endif
 
-#define EGS_ABI_VERSION 6
+#define EGS_ABI_VERSION 7
 
 typedef enum {
   EGS_OK = 0,
@@ -343,10 +343,14 @@ egs_status egs_sparse_decode_attn(const egs_decode_shape* shape,
  *                                                               (Sec. 4.2)
  * shape: batch 1, cache_len T, n_obs W, n_sink (and the heads); its n_keep
  * and n_recent are not used.  q_obs [Hq, W, d], k [Hkv, T, d] bf16 (device).
- * chunk_bounds: HOST int32 [n_chunks][2].  Outputs (device): removed [k] int8,
- * removed_tokens [1] int32, priority [k] float32, row_mass [k][Hq*W] float32
- * or NULL.  Valid: 1 <= n_chunks <= 4096, Hq*W <= 8192, eps_s > 0,
- * lambda >= 0, eps >= 0, m0 >= 0, target >= 0.
+ * chunk_bounds: device int32 [n_chunks][2] (begin, end), checked on the
+ * device: when the chunks are not ascending, disjoint, non-empty and before
+ * the observers, the call removes nothing and sets removed_tokens to -1 and
+ * every priority to NaN (every access stays in bounds whatever the values).
+ * Outputs (device): removed [k] int8, removed_tokens [1] int32, priority [k]
+ * float32, row_mass [k][Hq*W] float32 or NULL.  Valid: 1 <= n_chunks <= 4096,
+ * Hq*W <= 8192, eps_s > 0, lambda >= 0, eps >= 0, m0 >= 0, target >= 0.
+ * Nothing is copied from host memory, so the call can be captured in a graph.
  * ------------------------------------------------------------------------- */
 typedef struct {
   double eps_s;     /* null smoothing epsilon_s > 0 */
@@ -371,13 +375,14 @@ egs_status egs_chunk_prune(const egs_decode_shape* shape, const egs_prune_params
  * For prices y_a >= 0 (one per observer row) and t >= 0, U bounds the tokens
  * that any removal set keeping every row within eps and at most k - m0
  * chunks can remove; U - removed_tokens bounds the greedy scan's shortfall.
- * chunk_bounds: HOST int32 [n_chunks][2] (begin, end), only the lengths
- * n_i = end - begin are used.  Device: row_mass [n_chunks][n_rows] float32
- * (the egs_chunk_prune output), row_price [n_rows] float32, certificate [1]
- * float64.  Computed in float64.  Valid: 1 <= n_chunks <= 4096,
- * 1 <= n_rows <= 8192, every chunk non-empty, eps >= 0, t >= 0, m0 >= 0.
- * The prices are not checked (device memory): with a negative price U is no
- * bound.  workspace >= egs_prune_certificate_workspace(n_chunks) bytes.
+ * chunk_bounds: device int32 [n_chunks][2] (begin, end); only the lengths
+ * n_i = end - begin are used (as given: they are not checked).  Device:
+ * row_mass [n_chunks][n_rows] float32 (the egs_chunk_prune output),
+ * row_price [n_rows] float32, certificate [1] float64.  Computed in float64.
+ * Valid: 1 <= n_chunks <= 4096, 1 <= n_rows <= 8192, eps >= 0, t >= 0,
+ * m0 >= 0.  The prices are not checked (device memory): with a negative
+ * price U is no bound.  workspace >= egs_prune_certificate_workspace(n_chunks)
+ * bytes.
  * ------------------------------------------------------------------------- */
 size_t egs_prune_certificate_workspace(int32_t n_chunks);
 egs_status egs_prune_certificate(const int32_t* chunk_bounds, int32_t n_chunks, int32_t n_rows,

@@ -39,7 +39,7 @@ def test_library_exports_every_declared_symbol(L):
 
 
 def test_abi_version_and_status_strings(L):
-    assert L.LIB.egs_abi_version() == 6
+    assert L.LIB.egs_abi_version() == 7
     for st in range(5):
         assert L.LIB.egs_status_string(st).decode().startswith("EGS_")
 
@@ -261,22 +261,18 @@ def test_latent_step_errors(L):
 def test_chunk_prune_errors(L):
     import numpy as np
     sc = _dshape(L, batch=1, cache_len=4096, n_obs=64)
-    good = np.array([[10, 100], [100, 200], [300, 4032]], dtype=np.int32)
     P = lambda **kw: L.PruneParamsC(**{**dict(eps_s=0.1, lam=0.5, eps=0.05, m0=0, target=100,
                                               zeta=0.5, tau=1.0), **kw})
     ws = L.LIB.egs_chunk_prune_workspace(ctypes.byref(sc), 3)
     assert ws > 0
 
-    def call(bounds=good, nk=None, prm=None, wsb=ws, shape=sc):
-        b = np.ascontiguousarray(bounds, dtype=np.int32)
+    def call(bounds=FAKE, nk=3, prm=None, wsb=ws, shape=sc):
+        # chunk_bounds is device memory (never read on the host)
         return L.LIB.egs_chunk_prune(ctypes.byref(shape), ctypes.byref(prm or P()), FAKE, FAKE,
-                                     b.ctypes.data_as(ctypes.c_void_p),
-                                     len(b) if nk is None else nk, FAKE, FAKE, FAKE, None, FAKE,
-                                     wsb, None)
+                                     bounds, nk, FAKE, FAKE, FAKE, None, FAKE, wsb, None)
 
-    assert call(bounds=np.array([[10, 100], [90, 200]])) == L.EGS_EINVAL     # overlap
-    assert call(bounds=np.array([[10, 100], [100, 4040]])) == L.EGS_EINVAL   # into observers
-    assert call(bounds=np.array([[50, 50]])) == L.EGS_EINVAL                 # empty chunk
+    assert call(bounds=None) == L.EGS_EINVAL
+    assert call(bounds=ctypes.c_void_p((1 << 20) + 2)) == L.EGS_EINVAL       # misaligned
     assert call(nk=0) == L.EGS_EINVAL
     assert call(prm=P(eps_s=0.0)) == L.EGS_EINVAL
     assert call(prm=P(lam=-1.0)) == L.EGS_EINVAL
@@ -289,17 +285,14 @@ def test_chunk_prune_errors(L):
 
 def test_prune_certificate_errors(L):
     import numpy as np
-    good = np.array([[10, 100], [100, 200]], dtype=np.int32)
     ws = L.LIB.egs_prune_certificate_workspace(2)
     assert ws > 0 and L.LIB.egs_prune_certificate_workspace(0) == 0
 
-    def call(bounds=good, nk=None, R=512, eps=0.1, m0=0, t=1.0, wsb=ws, mass=FAKE):
-        b = np.ascontiguousarray(bounds, dtype=np.int32)
-        return L.LIB.egs_prune_certificate(b.ctypes.data_as(ctypes.c_void_p),
-                                           len(b) if nk is None else nk, R, mass, FAKE, eps, m0,
-                                           t, FAKE, FAKE, wsb, None)
+    def call(bounds=FAKE, nk=2, R=512, eps=0.1, m0=0, t=1.0, wsb=ws, mass=FAKE):
+        return L.LIB.egs_prune_certificate(bounds, nk, R, mass, FAKE, eps, m0, t, FAKE, FAKE,
+                                           wsb, None)
 
-    assert call(bounds=np.array([[10, 10]])) == L.EGS_EINVAL    # empty chunk
+    assert call(bounds=None) == L.EGS_EINVAL
     assert call(nk=0) == L.EGS_EINVAL
     assert call(R=0) == L.EGS_EINVAL
     assert call(R=8193) == L.EGS_EINVAL
@@ -370,3 +363,17 @@ def test_score_select_errors(L):
     assert call(q=None) == L.EGS_EINVAL
     assert call(rig=None) == L.EGS_EINVAL
     assert "rigid" in L.LIB.egs_last_error().decode()
+
+
+def test_binding_checks_host_chunk_bounds():
+    # host bounds are checked by the Python binding before anything reaches
+    # the device (the library itself checks device bounds on the device)
+    import numpy as np
+    import torch
+    from entropy_guided_sparse_amd import api
+    from entropy_guided_sparse_amd._lib import EgsError
+    dev = torch.device("cpu")   # never reached: every case fails the check
+    for bad, limit in (([[10, 100], [90, 200]], 4032), ([[10, 100], [100, 4040]], 4032),
+                       ([[50, 50]], 4032), ([[10, 10]], None)):
+        with pytest.raises(EgsError):
+            api.chunk_bounds_device(np.array(bad), dev, limit=limit)

@@ -127,3 +127,52 @@ def test_decode_step_graph_replays(api):
     outs = [r["keep_idx"], r["k_out"], r["v_out"], r["head_entropy"], r["scores"], out]
     _replays_match(g, outs, refs)
     assert np.all(np.diff(refs[0].cpu().numpy(), axis=-1) > 0)
+
+
+def test_fused_scoring_split_topk_and_chunk_prune_graph_replays(api):
+    """The fused scoring call, a 65,536-entry retention row (the split top-k)
+    and chunk pruning with device-side chunk bounds, captured together."""
+    L = api.L
+    cfg = synth.small_prefill_config(n_q_heads=8, n_kv_heads=2, head_dim=128, seq_len=8192,
+                                     block_size=128, segment_size=2048, probe_len=64,
+                                     head_types="fraction", hot_count="8", hot_dist="zipf1.2")
+    inp = synth.make_prefill(cfg, 1)
+    shape = prefill_shape(api, cfg)
+    q, k = (dev_tensor(x, cfg.dtype) for x in (inp.q_store, inp.k_store))
+    pol = api.BudgetPolicy(mode=L.EGS_BUDGET_TWO_LEVEL, frac_rigid=0.05, frac_dynamic=0.3,
+                           entropy_threshold=0.5)
+    import ctypes
+    sc = shape.c()
+    ws = torch.empty(L.LIB.egs_entropy_score_workspace(ctypes.byref(sc)), dtype=torch.uint8,
+                     device=q.device)
+    dc = synth.DecodeConfig("graph2", 1, 8, 2, 128, 65536, 64, 4, 256, 2048, "bf16", 0.01)
+    dinp = synth.make_decode(dc, seed=4)
+    dshape = api.DecodeShape(1, 8, 2, 128, 65536, 64, 4, 256, 2048)
+    qo, kk, vv = (dev_tensor(x, "bf16") for x in (dinp.q_obs_store, dinp.k_store,
+                                                 dinp.v_store))
+    prm = api.RetainParams(entropy_kind=L.EGS_SHANNON, zeta=0.5, tau=1.0)
+    dws = torch.empty(L.LIB.egs_kv_retain_workspace(ctypes.byref(dshape.c())),
+                      dtype=torch.uint8, device=q.device)
+    chunks = torch.from_numpy(synth.prune_chunks(65536, 64, 40, seed=4).astype(np.int32)).cuda()
+    pws = torch.empty(L.LIB.egs_chunk_prune_workspace(ctypes.byref(dshape.c()), 40),
+                      dtype=torch.uint8, device=q.device)
+    held = {}
+
+    def work():
+        held["sel"] = api.score_select(shape, pol, q, k, 40, workspace=ws)
+        held["ret"] = api.kv_retain(dshape, prm, qo, kk, vv, workspace=dws, gather=False)
+        held["pr"] = api.chunk_prune(dshape, qo[0], kk[0], chunks, 0.1, 0.5, 0.1, 4, 20000,
+                                     workspace=pws)
+
+    def outputs():
+        s, r, p = held["sel"], held["ret"], held["pr"]
+        return [s["block_scores"], s["entropy"], s["budget"], s["block_idx"], s["block_cnt"],
+                r["keep_idx"], p[0], p[1], p[2]]
+
+    log("[graph] fused scoring + 64k retention row + chunk pruning")
+    work()
+    torch.cuda.synchronize()
+    refs = [t.clone() for t in outputs()]
+    assert int(refs[7].item()) >= 0
+    g = _capture(work)
+    _replays_match(g, outputs(), refs)

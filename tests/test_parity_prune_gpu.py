@@ -243,3 +243,29 @@ def test_prune_certificate(api):
         assert U >= got_tokens - 1e-6
     assert float(api.prune_certificate(chunks, mass, torch.zeros(R, device="cuda"), eps, m0,
                                        0.0).cpu().item()) == float(n.sum())
+
+
+@pytest.mark.parametrize("bad", [[[10, 100], [90, 200]], [[10, 100], [100, 4040]],
+                                 [[50, 50], [60, 70]], [[-5, 10]], [[3000, 2000]]])
+def test_chunk_prune_invalid_device_bounds(api, bad):
+    """Chunk bounds handed over in device memory are checked on the device:
+    overlapping, observer-reaching, empty, negative or reversed chunks remove
+    nothing and report removed_tokens = -1 (all accesses stay in bounds)."""
+    T, W = 4096, 64
+    cfg = synth.DecodeConfig("prune-bad", 1, 8, 2, 128, T, W, 4, 16, 16)
+    inp = synth.make_decode(cfg, seed=21)
+    shape = api.DecodeShape(1, 8, 2, 128, T, W, 4, 16, 16)
+    q = dev_tensor(inp.q_obs_store[0], "bf16")
+    k = dev_tensor(inp.k_store[0], "bf16")
+    b = torch.tensor(bad, dtype=torch.int32, device="cuda")
+    removed, tokens, prio, _ = api.chunk_prune(shape, q, k, b, 0.1, 0.5, 1.0, 0, T)
+    torch.cuda.synchronize()
+    log(f"[prune bad bounds] {bad} -> tokens {int(tokens.item())}")
+    assert int(tokens.item()) == -1
+    assert not removed.cpu().numpy().any()
+    assert torch.isnan(prio).all()
+    # the same call on valid device bounds still works after a failed one
+    good = torch.tensor([[10, 100], [100, 200], [300, 4032]], dtype=torch.int32, device="cuda")
+    removed, tokens, prio, _ = api.chunk_prune(shape, q, k, good, 0.1, 0.5, 1.0, 0, T)
+    torch.cuda.synchronize()
+    assert int(tokens.item()) >= 0 and torch.isfinite(prio).all()
