@@ -168,9 +168,9 @@ __device__ __forceinline__ void load_obs_q(bf16x8 (&qf)[RT][D / 16], const bf16*
 // Workgroup = (1024-key span, batch x KV group, 4-head group); the four
 // wavefronts (one query head each) share every K stage.  Stages are copied
 // RT_DEPTH - 1 ahead of the one being computed (four LDS buffers), so each
-// workgroup keeps three 16-KB copies in flight against HBM latency; the pass-2
-// masses collect in LDS and leave after the loop, so that only the copies
-// are outstanding while the loop waits on them.
+// workgroup keeps three 16-KB copies in flight against HBM latency.  Pass 2
+// stores the masses of every stage as it goes; those stores share the vector
+// memory counter with the copies, and the wait before a stage counts them.
 // SEG (pass 1 of chunk pruning, one sequence): the same tile sums are also
 // split by candidate chunk.  A row's sum over the keys of chunk c in this
 // span, taken against the row's reference, is written with that reference as
@@ -231,17 +231,28 @@ __global__ __launch_bounds__(256) void obs_pass_kernel(
   float s1 = 0.f, s2 = 0.f;
   const float invW = 1.0f / (float)W;
   if (MASS) {
+    // every load is issued before the first result is used (row indices
+    // clamped into the window; h is a valid head even for an idle wave), so
+    // the wave waits out one memory latency here, not one per row
     const size_t rbase = ((size_t)b * Hq + h) * W;
+    float inv[RT][16];
+#pragma unroll
+    for (int rt = 0; rt < RT; ++rt)
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        const size_t at = rbase + min(rt * 32 + acc_row(i, lane), W - 1);
+        inv[rt][i] = row_inv[at];
+        rm[rt][i] = row_m[at];
+      }
 #pragma unroll
     for (int rt = 0; rt < RT; ++rt)
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         const int u = rt * 32 + acc_row(i, lane);
-        const bool ok = hvalid && u < W;
         // exp2(z sl2 - M) / L = exp2(z sl2 - (M + log2 L)); rows past the
         // window get an infinite offset, i.e. probability 0
-        const float inv = ok ? row_inv[rbase + u] : 0.f;
-        rm[rt][i] = ok && inv > 0.f ? row_m[rbase + u] - __log2f(inv) : INFINITY;
+        const bool ok = hvalid && u < W && inv[rt][i] > 0.f;
+        rm[rt][i] = ok ? rm[rt][i] - __log2f(inv[rt][i]) : INFINITY;
       }
   }
   // chunk segments: the chunk id of every key of the span (-1 outside the
@@ -431,14 +442,22 @@ __global__ __launch_bounds__(256) void obs_pass_kernel(
   };
   // Stage st sits in buffer st % RT_DEPTH.  At the top of stage st a wave
   // waits for its copies of stage st (the copies of the stages after it stay
-  // in flight; pass 2's mass stores are not counted, which only ever makes
-  // the wait longer), meets the others at the barrier and copies stage
-  // st + RT_DEPTH - 1 into the buffer stage st - 1 used.
-  auto stage_top = [&](int st) {
+  // in flight), meets the others at the barrier and copies stage
+  // st + RT_DEPTH - 1 into the buffer stage st - 1 used.  stores = the vector
+  // stores the wave is known to have issued after those copies: the
+  // pipelined pass-2 loop below stores once per stage, so from its stage 4 on
+  // the three stores of stages st - 4 .. st - 2 may stay in flight too.
+  // Counting fewer stores than were issued only makes the wait longer.
+  auto stage_top = [&](int st, int stores) {
     const int ahead = min(RT_DEPTH - 2, nst - 1 - st);   // copies issued after stage st's
-    if (ahead >= 2) wait_vmem_upto<2 * PW>();
-    else if (ahead == 1) wait_vmem_upto<PW>();
-    else wait_vmem();
+    if (ahead >= 2) {
+      if (stores >= 3) wait_vmem_upto<2 * PW + 3>();
+      else wait_vmem_upto<2 * PW>();
+    } else if (ahead == 1) {
+      wait_vmem_upto<PW>();
+    } else {
+      wait_vmem();
+    }
     __syncthreads();
     if (st + RT_DEPTH - 1 < nst)
       KPipe<D>::copy(Ks[(st + RT_DEPTH - 1) % RT_DEPTH], Kg, t_begin + (st + RT_DEPTH - 1) * RT_KT,
@@ -590,7 +609,7 @@ __global__ __launch_bounds__(256) void obs_pass_kernel(
     };
     float* mrow = MASS ? mass + ((size_t)b * Hq + h) * L : nullptr;
     floatx16 za[RT], zb[RT];
-    stage_top(0);
+    stage_top(0, 0);
     if (hvalid) first(Ks[0], za);
     for (int st = 0; st < NST; ++st) {
       float a0 = 0.f, a1 = 0.f;
@@ -602,7 +621,7 @@ __global__ __launch_bounds__(256) void obs_pass_kernel(
         else fold1(za, sm);
       }
       if (st + 1 < NST) {
-        stage_top(st + 1);
+        stage_top(st + 1, MASS && hvalid && st + 1 >= 4 ? 3 : 0);
         if (hvalid) {
           // tile 0 of stage st + 1 on the MFMA unit, tile 1 of stage st on the VALU
           float sm[RT];
@@ -622,7 +641,7 @@ __global__ __launch_bounds__(256) void obs_pass_kernel(
     }
   } else {
     for (int st = 0; st < nst; ++st) {
-      stage_top(st);
+      stage_top(st, 0);
       if (hvalid) {
         const int t0 = t_begin + st * RT_KT;
         if (t0 + RT_KT - 1 >= t_end || t0 + RT_KT - 1 > pos0)
