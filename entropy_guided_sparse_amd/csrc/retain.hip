@@ -13,7 +13,7 @@
 // always kept; compaction preserves token order (EntroPrefill Sec. 8.1).
 //
 // gfx950 design:
-//  * Both passes run obs_pass_kernel: one workgroup per (1024-key span,
+//  * Both passes run obs_pass_kernel: one workgroup per (2048-key span,
 //    batch x KV group, 4-head group).  64-key K stages are copied straight
 //    into LDS, four deep, and shared by the four wavefronts (one query head
 //    each); the logits of a stage take v_mfma_f32_32x32x16_bf16.
@@ -38,7 +38,7 @@
 //  * Chunk pruning (EntroPrefill Sec. 3.1-3.2, 4.2) runs both passes on one
 //    prompt; pass 1 also splits each row's sums by candidate chunk (a
 //    "chunk" below is always one of the prompt's candidate documents, a
-//    "span" the passes' 1024-key work unit).  The pooled measure is formed
+//    "span" the passes' 2048-key work unit).  The pooled measure is formed
 //    per position, one workgroup orders the chunks by priority and scans
 //    them greedily with block votes, and two small kernels evaluate the
 //    Sec. 4.2 optimality-gap certificate for caller prices.
@@ -57,7 +57,7 @@ __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0
 // only feeds a later sum cannot drift past the next fence.
 __device__ __forceinline__ void pin_vgpr(float& x) { asm volatile("" : "+v"(x)); }
 
-constexpr int RT_CK = 1024;   // keys per span (the pass 1 / pass 2 work unit)
+constexpr int RT_CK = 2048;   // keys per span (the pass 1 / pass 2 work unit)
 constexpr int RT_KT = 64;     // keys per LDS stage
 constexpr int SEL_T = 1024;   // threads of the select kernel
 constexpr int SEL_CH = 16384; // keys per chunk of the split top-k
@@ -67,7 +67,7 @@ constexpr int DA_SPL_MAX = 512;   // range the launcher chooses from (multiples 
 struct RetainLayout {
   size_t stat_m, stat_l, row_m, row_inv, mass, ent, weight, mu, qsum, tstats;
   size_t sel_hist, sel_state, sel_cnt, total;
-  int nch;    // 1024-key spans of the cache
+  int nch;    // 2048-key spans of the cache
   int nsel;   // key chunks of the split top-k (histogram and compaction)
 };
 
@@ -165,7 +165,7 @@ __device__ __forceinline__ void load_obs_q(bf16x8 (&qf)[RT][D / 16], const bf16*
 // 64 below the row's maximum in log2 units) and the sum of exp2(z - m).
 // pass 2 (MASS = true): per-head window-mean mass of every key and the
 // span's sink-isolated entropy partial sums.
-// Workgroup = (1024-key span, batch x KV group, 4-head group); the four
+// Workgroup = (2048-key span, batch x KV group, 4-head group); the four
 // wavefronts (one query head each) share every K stage.  Stages are copied
 // RT_DEPTH - 1 ahead of the one being computed (four LDS buffers), so each
 // workgroup keeps three 16-KB copies in flight against HBM latency.  Pass 2
@@ -1799,7 +1799,7 @@ __global__ __launch_bounds__(256) void chunk_of_kernel(const int32_t* __restrict
 }
 
 // first segment of every chunk: seg_base[c] = sum over c' < c of the number of
-// 1024-key spans chunk c' touches; seg_base[k] = the total.  One workgroup.
+// 2048-key spans chunk c' touches; seg_base[k] = the total.  One workgroup.
 __global__ __launch_bounds__(SEL_T) void seg_base_kernel(const int32_t* __restrict__ bounds,
                                                          int k, int32_t* __restrict__ seg_base) {
   __shared__ int ired[SEL_T / 64];
