@@ -16,15 +16,17 @@
 //    along d, 16 in flight per lane, fp32 sums reduced across the wave's row
 //    phases) and writes the block means as a bf16 hi/lo pair (k_bar ~= hi +
 //    lo to ~2^-17, so the logits run on bf16 MFMA with two products each).
-//  * probe_stats and probe_mass take (128-block piece, segment, KV group)
-//    work items.  The piece's hi/lo block means are copied straight from
+//  * probe_stats and probe_mass take (piece, segment, KV group) work items,
+//    96-block pieces for the statistics (three workgroups per CU: the 768
+//    items of the 128k layer run in one round) and 128-block pieces for the
+//    masses.  The piece's hi/lo block means are copied straight from
 //    global memory into LDS (one round trip, shared by the r heads of the
 //    group) while each wave loads the probe queries of its head into
 //    registers; then v_mfma_f32_32x32x16_bf16 forms the piece's logits.
 //      probe_stats  blocks as M (a lane owns a probe row): each row's maximum
 //                   and sum of exponentials over the piece, one partial per
 //                   (row, piece);
-//      probe_mass   folds a row's partials (at most C_B / 128) into the row's
+//      probe_mass   folds a row's partials (at most C_B / 96) into the row's
 //                   log2 offset M + log2 L, recomputes the logits with the
 //                   blocks as N (a lane owns a block, the probe mean is a
 //                   register sum) and writes the piece's block scores and its
@@ -46,12 +48,14 @@ namespace egs {
 constexpr int PS_NB = 16;     // key blocks per pool_keys workgroup
 constexpr int PS_NW = 8;      // waves per pool_keys workgroup
 constexpr int PS_U = 16;      // 16-byte key loads in flight per lane while pooling
-constexpr int PC = 128;       // key blocks per probe piece
+constexpr int PC = 128;       // key blocks per probe_mass piece (and entropy partial)
+constexpr int PC_S = 96;      // key blocks per probe_stats piece
 
 struct ScoreLayout {
   size_t kb_hi, kb_lo, stat_m, stat_l, ent, total;
   int npool;    // pool_keys chunks per KV group
-  int npc;      // probe pieces per segment (at most)
+  int npc;      // probe_mass pieces per segment (at most)
+  int npc_s;    // probe_stats pieces per segment (at most)
 };
 
 static size_t sc_align(size_t x) {
@@ -62,6 +66,7 @@ static ScoreLayout score_layout(const PrefillDims& p) {
   ScoreLayout o;
   o.npool = (p.CB + PS_NB - 1) / PS_NB;
   o.npc = (p.CB + PC - 1) / PC;
+  o.npc_s = (p.CB + PC_S - 1) / PC_S;
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -71,8 +76,8 @@ static ScoreLayout score_layout(const PrefillDims& p) {
   o.kb_hi = take((size_t)p.Hkv * p.CB * p.D * sizeof(bf16));
   o.kb_lo = take((size_t)p.Hkv * p.CB * p.D * sizeof(bf16));
   const size_t rows = (size_t)p.Hq * p.CS * p.P;
-  o.stat_m = take(rows * o.npc * sizeof(float));
-  o.stat_l = take(rows * o.npc * sizeof(float));
+  o.stat_m = take(rows * o.npc_s * sizeof(float));
+  o.stat_l = take(rows * o.npc_s * sizeof(float));
   o.ent = take((size_t)p.Hq * p.CS * o.npc * sizeof(float));
   o.total = off;
   return o;
@@ -209,15 +214,15 @@ __device__ __forceinline__ bf16x8 kbar_frag(const bf16* k, int row, int c, int h
 }
 
 // Direct global -> LDS copies of the hi / lo block means of blocks
-// c0 .. c0 + PC - 1 into the swizzled stage (4 waves).  Each copy lands at
+// c0 .. c0 + NB - 1 into the swizzled stage (4 waves).  Each copy lands at
 // a fixed LDS slot; the lane fetches the global chunk that belongs there.
 // Rows at or past nb repeat block c0 + nb - 1, whose logits every reader
 // masks or discards.  Completion: wait_vmem() and a workgroup barrier.
-template <int D>
+template <int D, int NB>
 __device__ __forceinline__ void stage_piece(bf16* kh, bf16* kl, const bf16* KH, const bf16* KL,
                                             int c0, int nb) {
   constexpr int KCH = D / 8;                    // 16-byte chunks per row
-  constexpr int NI = (PC * KCH + 255) / 256;    // copies per lane per plane
+  constexpr int NI = (NB * KCH + 255) / 256;    // copies per lane per plane
   const int lane = threadIdx.x & 63;
   const int w = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
   const bf16* sh = uniform_ptr(KH + (size_t)c0 * D);
@@ -227,7 +232,7 @@ __device__ __forceinline__ void stage_piece(bf16* kh, bf16* kl, const bf16* KH, 
 #pragma unroll
   for (int ii = 0; ii < NI; ++ii) {
     const int q = (w * NI + ii) * 64 + lane;    // destination chunk
-    if (w * NI + ii >= PC * KCH / 64) break;      // (wave-uniform) past the stage
+    if (w * NI + ii >= NB * KCH / 64) break;      // (wave-uniform) past the stage
     const int row = q / KCH, slot = q % KCH;
     const int src = min(row, nb - 1);
     const uint32_t off = (uint32_t)((src * D + (slot ^ kbar_swz<D>(row)) * 8) * sizeof(bf16));
@@ -271,35 +276,35 @@ __device__ __forceinline__ void load_probe(typename QFrag<TQ>::raw_t (&qr)[RTG][
 }
 
 // ---------------------------------------------------------------------------
-// K2a probe_stats: work item (piece of PC key blocks, segment s, KV group g).
+// K2a probe_stats: work item (piece of PC_S key blocks, segment s, KV group g).
 // For each head of the group (one per wave at a time) and probe row u:
 //   m = max_j z_uj, l = sum_j 2^(z_uj - m) over the piece's causal blocks
 //   j < C_B(s) (z in log2 units), stored at stat[h, s, piece, u].
 // Blocks are the MFMA M dimension: a lane owns a probe row, a register a block.
 // ---------------------------------------------------------------------------
 template <typename TQ, int D>
-__global__ __launch_bounds__(256, 2) void probe_stats_kernel(
+__global__ __launch_bounds__(256, 3) void probe_stats_kernel(
     const TQ* __restrict__ Q, const bf16* __restrict__ kb_hi, const bf16* __restrict__ kb_lo,
     int Hq, int r, int N, int LS, int LB, int P, int CS, int CB, int npc, float scale_log2,
     float* __restrict__ stat_m, float* __restrict__ stat_l) {
   constexpr int NC = D / 16;
-  constexpr int BT = PC / 32;
+  constexpr int BT = PC_S / 32;
   constexpr int RTG = sizeof(TQ) == 2 ? 2 : 1;   // 32-row probe tiles per group
   typedef typename QFrag<TQ>::raw_t raw_t;
-  __shared__ __attribute__((aligned(16))) bf16 kh[PC * D];
-  __shared__ __attribute__((aligned(16))) bf16 kl[PC * D];
+  __shared__ __attribute__((aligned(16))) bf16 kh[PC_S * D];
+  __shared__ __attribute__((aligned(16))) bf16 kl[PC_S * D];
   int ch, s, g;
   if (!probe_item(blockIdx.x, npc, CS, Hq / r, ch, s, g)) return;
   const int cb = (s + 1) * (LS / LB);
-  const int c0 = ch * PC;
+  const int c0 = ch * PC_S;
   if (c0 >= cb) return;
-  const int nb = min(PC, cb - c0);
+  const int nb = min(PC_S, cb - c0);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int l32 = lane & 31, hg = lane >> 5;
   const size_t u_begin = (size_t)(s + 1) * LS - P;
   const int ngrp = (P + 32 * RTG - 1) / (32 * RTG);
 
-  stage_piece<D>(kh, kl, kb_hi + (size_t)g * CB * D, kb_lo + (size_t)g * CB * D, c0, nb);
+  stage_piece<D, PC_S>(kh, kl, kb_hi + (size_t)g * CB * D, kb_lo + (size_t)g * CB * D, c0, nb);
   raw_t qr[RTG][NC];
   if (w < r) load_probe<TQ, D, RTG>(qr, Q, g * r + w, N, u_begin, P, 0);
   wait_vmem();
@@ -413,8 +418,9 @@ struct RowPartials {
 template <typename TQ, int D>
 __global__ __launch_bounds__(256, 2) void probe_mass_kernel(
     const TQ* __restrict__ Q, const bf16* __restrict__ kb_hi, const bf16* __restrict__ kb_lo,
-    int Hq, int r, int N, int LS, int LB, int P, int CS, int CB, int npc, float scale_log2,
-    int kind, float alpha, const float* __restrict__ stat_m, const float* __restrict__ stat_l,
+    int Hq, int r, int N, int LS, int LB, int P, int CS, int CB, int npc, int npc_s,
+    float scale_log2, int kind, float alpha, const float* __restrict__ stat_m,
+    const float* __restrict__ stat_l,
     float* __restrict__ ent, float* __restrict__ scores) {
   constexpr int NC = D / 16;
   constexpr int BT = PC / 32;
@@ -438,20 +444,20 @@ __global__ __launch_bounds__(256, 2) void probe_mass_kernel(
     return;
   }
   const int nb = min(PC, cb - c0);
-  const int nparts = (cb + PC - 1) / PC;   // probe_stats pieces of segment s
+  const int nparts = (cb + PC_S - 1) / PC_S;   // probe_stats pieces of segment s
   const size_t u_begin = (size_t)(s + 1) * LS - P;
   const float invP = 1.0f / (float)P;
   const int ngrp = (P + RG - 1) / RG;
   auto part_ptrs = [&](int h, int grp, const float*& sm, const float*& sl) {
     const int urow = min(grp * RG + lane % RG, P - 1);
-    const size_t o = ((size_t)h * CS + s) * npc * P + urow;
+    const size_t o = ((size_t)h * CS + s) * npc_s * P + urow;
     sm = stat_m + o;
     sl = stat_l + o;
   };
 
   // one round trip: the piece's block means, the first head's queries and
   // its rows' first partials are all in flight together
-  stage_piece<D>(kh, kl, kb_hi + (size_t)g * CB * D, kb_lo + (size_t)g * CB * D, c0, nb);
+  stage_piece<D, PC>(kh, kl, kb_hi + (size_t)g * CB * D, kb_lo + (size_t)g * CB * D, c0, nb);
   raw_t qr[RTG][NC];
   RowPartials rp;
   if (w < r) {
@@ -575,18 +581,19 @@ static hipError_t score_dispatch(const PrefillDims& p, const ScoreLayout& ly, co
   float* sl = reinterpret_cast<float*>(ws + ly.stat_l);
   float* en = reinterpret_cast<float*>(ws + ly.ent);
   const int g1 = (p.Hkv * ly.npool + 7) / 8 * 8;
+  const int g2s = (p.Hkv * p.CS * ly.npc_s + 7) / 8 * 8;
   const int g2 = (p.Hkv * p.CS * ly.npc + 7) / 8 * 8;
   hipError_t e;
 #define EGS_POOL(DD)                                                                         \
   pool_keys_kernel<T, DD, PS_NW><<<g1, 64 * PS_NW, 0, st>>>(K, p.N, p.LB, p.CB, p.Hkv,      \
                                                             ly.npool, H, L)
 #define EGS_STATS(DD)                                                                        \
-  probe_stats_kernel<T, DD><<<g2, 256, 0, st>>>(Q, H, L, p.Hq, p.r, p.N, p.LS, p.LB, p.P,   \
-                                                 p.CS, p.CB, ly.npc, sl2, sm, sl)
+  probe_stats_kernel<T, DD><<<g2s, 256, 0, st>>>(Q, H, L, p.Hq, p.r, p.N, p.LS, p.LB, p.P,  \
+                                                  p.CS, p.CB, ly.npc_s, sl2, sm, sl)
 #define EGS_MASS(DD)                                                                         \
   probe_mass_kernel<T, DD><<<g2, 256, 0, st>>>(Q, H, L, p.Hq, p.r, p.N, p.LS, p.LB, p.P,    \
-                                                p.CS, p.CB, ly.npc, sl2, kind, alpha, sm,  \
-                                                sl, en, scores)
+                                                p.CS, p.CB, ly.npc, ly.npc_s, sl2, kind,   \
+                                                alpha, sm, sl, en, scores)
 #define EGS_D_SWITCH(M)              \
   switch (p.D) {                     \
     case 16: M(16); break;           \
