@@ -18,8 +18,8 @@
 //    lo to ~2^-17, so the logits run on bf16 MFMA with two products each).
 //  * probe_stats and probe_mass take (piece, segment, KV group) work items,
 //    96-block pieces for the statistics (three workgroups per CU: the 768
-//    items of the 128k layer run in one round) and 128-block pieces for the
-//    masses.  The piece's hi/lo block means are copied straight from
+//    causal items of the 128k layer run in one round) and 160-block pieces
+//    for the masses (80 KB of LDS, two per CU: its 488 items, one round).  The piece's hi/lo block means are copied straight from
 //    global memory into LDS (one round trip, shared by the r heads of the
 //    group) while each wave loads the probe queries of its head into
 //    registers; then v_mfma_f32_32x32x16_bf16 forms the piece's logits.
@@ -48,7 +48,7 @@ namespace egs {
 constexpr int PS_NB = 16;     // key blocks per pool_keys workgroup
 constexpr int PS_NW = 8;      // waves per pool_keys workgroup
 constexpr int PS_U = 16;      // 16-byte key loads in flight per lane while pooling
-constexpr int PC = 128;       // key blocks per probe_mass piece (and entropy partial)
+constexpr int PC = 160;       // key blocks per probe_mass piece (and entropy partial)
 constexpr int PC_S = 96;      // key blocks per probe_stats piece
 
 struct ScoreLayout {
