@@ -12,8 +12,8 @@
 //
 // gfx950 design: four kernels, no logits stored.
 //  * pool_keys streams K once from HBM: a workgroup of eight waves pools a
-//    chunk of 16 key blocks (a wave takes two, 16-byte nontemporal loads
-//    along d, 16 in flight per lane, fp32 sums reduced across the wave's row
+//    chunk of 8 key blocks (a wave takes one, 16-byte nontemporal loads
+//    along d, 8 in flight per lane, fp32 sums reduced across the wave's row
 //    phases) and writes the block means as a bf16 hi/lo pair (k_bar ~= hi +
 //    lo to ~2^-17, so the logits run on bf16 MFMA with two products each).
 //  * probe_stats and probe_mass take (piece, segment, KV group) work items,
@@ -45,9 +45,9 @@
 
 namespace egs {
 
-constexpr int PS_NB = 16;     // key blocks per pool_keys workgroup
+constexpr int PS_NB = 8;      // key blocks per pool_keys workgroup
 constexpr int PS_NW = 8;      // waves per pool_keys workgroup
-constexpr int PS_U = 16;      // 16-byte key loads in flight per lane while pooling
+constexpr int PS_U = 8;       // 16-byte key loads in flight per lane while pooling
 constexpr int PC = 160;       // key blocks per probe_mass piece (and entropy partial)
 constexpr int PC_S = 96;      // key blocks per probe_stats piece
 
@@ -144,7 +144,7 @@ __device__ __forceinline__ void add16(const u32x4& v, float* acc, const float*) 
 }
 
 // ---------------------------------------------------------------------------
-// K1 pool_keys: one workgroup per (16-block chunk, KV group g);
+// K1 pool_keys: one workgroup per (8-block chunk, KV group g);
 //   kbar[g, j, :] = mean of keys j*LB .. (j+1)*LB-1, stored as bf16 hi + lo.
 // Every chunk of one KV group runs on one XCD (workgroup id mod 8), in order.
 // ---------------------------------------------------------------------------
