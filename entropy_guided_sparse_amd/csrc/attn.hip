@@ -43,6 +43,8 @@ namespace egs {
 constexpr int AT_KT = 64;     // keys per LDS stage and per V^T tile
 constexpr int AT_LCAP = 512;  // block-list entries staged in LDS at a time
 constexpr int PV_AHEAD = 4;   // V^T fragments read ahead of their MFMA
+constexpr int AT_NQUEUE = 8;  // work queues of the MFMA kernel (one per XCD)
+constexpr int AT_QSTRIDE = 16;   // ints between queue counters (one 64-byte line each)
 
 // The compiler schedules nothing across this point.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
@@ -58,13 +60,17 @@ __device__ __forceinline__ int vt_swap23(int x16) {
 // ---------------------------------------------------------------------------
 // vt_pack: V [Hkv, N, D] -> Vt [Hkv, N/64, D, 64] with permuted keys.
 // One workgroup per (64-key tile, KV head); coalesced 16-byte loads and stores.
+// The first workgroup also zeroes the MFMA kernel's queue counters, which
+// the launch that follows in stream order then finds at zero.
 // ---------------------------------------------------------------------------
 template <int D>
 __global__ __launch_bounds__(256) void vt_pack_kernel(const bf16* __restrict__ V, int N,
-                                                      bf16* __restrict__ Vt) {
+                                                      bf16* __restrict__ Vt,
+                                                      int* __restrict__ queue) {
   constexpr int VP = D + 2;   // padded row (bf16) to spread the column reads
   __shared__ bf16 tile[AT_KT * VP];
   const int t = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
+  if (t == 0 && g == 0 && tid < AT_NQUEUE) queue[tid * AT_QSTRIDE] = 0;
   const bf16* src = V + ((size_t)g * N + (size_t)t * AT_KT) * D;
   constexpr int CH = AT_KT * D / 8;
   for (int q = tid; q < CH; q += 256) {
@@ -102,13 +108,30 @@ struct AtItem {
   bool diag, valid;
 };
 
+//
+// Work distribution.  The hardware hands a grid's workgroups to the CUs in a
+// fixed rotation, whatever their length: with one workgroup per item, every
+// CU of an XCD kept serving the same head, and the CUs of heads with short
+// lists (rigid heads at a 5% budget against 30%) sat idle for a third of the
+// launch while the others set its length.  The launch is therefore a
+// persistent grid of as many workgroups as the CUs hold at once, and each
+// workgroup takes items (KV group, query block, head) from counters in the
+// workspace until they run out.  With xcd_remap the items of KV groups
+// x, x + 8, ... form queue x, which the workgroups of XCD x (workgroup id mod
+// 8) drain first, so a group's K / V blocks meet in one XCD's L2; a
+// workgroup whose queue is empty takes items from the next queues in turn.
+// Each queue holds its items heaviest (latest query block) first.  The
+// counters are zeroed by vt_pack before the launch and only ever
+// incremented, so every workgroup leaves the loop after at most
+// (items + 8) counter increments in all.
+
 template <int D, int LB>
 __global__ __launch_bounds__(LB * 2) __attribute__((amdgpu_waves_per_eu(2)))
 void sparse_attn_mfma_kernel(
     const bf16* __restrict__ Q, const bf16* __restrict__ K, const bf16* __restrict__ Vt,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ cnt, int k_max,
     bf16* __restrict__ O, float* __restrict__ lse, int Hkv, int r, int N, int LS, int CS,
-    int CB, float scale_log2, int xcd_remap) {
+    int CB, float scale_log2, int xcd_remap, int* __restrict__ queue) {
   constexpr int NW = LB / 32;
   constexpr int NT = NW * 64;
   constexpr int KT = AT_KT;
@@ -124,33 +147,49 @@ void sparse_attn_mfma_kernel(
   __shared__ __attribute__((aligned(1024))) bf16 Ks[2][KT * D];
   __shared__ __attribute__((aligned(1024))) bf16 Vs[2][D * KT];
   __shared__ int lst[AT_LCAP];
+  __shared__ int s_item;
 
-  // ---- work item: (KV group, query block) pair, head within group ----
-  // Pairs grp = k * Hkv + g run heaviest (latest query block) first.  With
-  // xcd_remap (Hkv * CB a multiple of 8) XCD x (workgroup id mod 8) takes
-  // pairs x, x + 8, ...: with 8 KV groups every XCD keeps one group, whose
-  // selected blocks (shared by all query blocks of a segment) then stay in
-  // that XCD's L2.  (Rotating the groups over the XCDs per query block
-  // balances rigid-heavy and dynamic-heavy groups but measured 5% slower;
-  // per segment it measured even.)
-  const int bid = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63;
+  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l32 = lane & 31, hg = lane >> 5;
+  const int nq = xcd_remap ? AT_NQUEUE : 1;
+  const int per_q = Hkv * r * CB / nq;
+  const int home = xcd_remap ? (int)(blockIdx.x & (AT_NQUEUE - 1)) : 0;
+  int tried = 0;   // queues found empty (thread 0 only)
+
+  for (;;) {
+  // ---- next work item: pair grp = k * Hkv + g (heaviest first), head hl ----
+  if (tid == 0) {
+    int item = -1;
+    while (tried < nq) {
+      const int qx = (home + tried) % nq;
+      const int slot = __hip_atomic_fetch_add(queue + qx * AT_QSTRIDE, 1, __ATOMIC_RELAXED,
+                                              __HIP_MEMORY_SCOPE_AGENT);
+      if (slot < per_q) {
+        item = qx * per_q + slot;
+        break;
+      }
+      ++tried;
+    }
+    s_item = item;
+  }
+  __syncthreads();
+  const int item = __builtin_amdgcn_readfirstlane(s_item);
+  if (item < 0) break;
   int grp, hl;
   if (xcd_remap) {
-    const int xcd = bid & 7, slot = bid >> 3;
-    grp = 8 * (slot / r) + xcd;
+    const int qx = item / per_q, slot = item % per_q;
+    grp = AT_NQUEUE * (slot / r) + qx;
     hl = slot % r;
   } else {
-    grp = bid / r;
-    hl = bid % r;
+    grp = item / r;
+    hl = item % r;
   }
   const int g = grp % Hkv;
   const int b = CB - 1 - grp / Hkv;
   const int h = g * r + hl;
   const int s = (b * LB) / LS;
 
-  const int tid = threadIdx.x, lane = tid & 63;
-  const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int l32 = lane & 31, hg = lane >> 5;
   const size_t qrow0 = (size_t)b * LB + w * 32;
   const int row_local = w * 32 + l32;
 
@@ -389,6 +428,7 @@ void sparse_attn_mfma_kernel(
   }
   if (lse != nullptr && hg == 0)
     lse[(size_t)h * N + qrow0 + l32] = (m_run * scale_log2 + log2f(lt)) * kLn2;
+  }
 }
 
 // ---------------------------------------------------------------------------
@@ -508,9 +548,25 @@ static bool mfma_path(const PrefillDims& p) {
   return p.dtype == EGS_BF16 && (p.D == 64 || p.D == 128) && (p.LB == 64 || p.LB == 128);
 }
 
+// V^T tiles, then the work-queue counters
+static size_t vt_bytes(const PrefillDims& p) { return (size_t)p.Hkv * p.N * p.D * sizeof(bf16); }
+constexpr size_t kQueueBytes = 1024;
+static_assert(AT_NQUEUE * AT_QSTRIDE * sizeof(int) <= kQueueBytes, "queue counters overflow");
+
 size_t sparse_attn_workspace_bytes(const PrefillDims& p) {
-  // V^T tiles for the MFMA path; nothing otherwise
-  return mfma_path(p) ? (size_t)p.Hkv * p.N * p.D * sizeof(bf16) : 0;
+  // V^T tiles and the queue counters for the MFMA path; nothing otherwise
+  return mfma_path(p) ? vt_bytes(p) + kQueueBytes : 0;
+}
+
+// Workgroups of the MFMA kernel that the device holds at once.
+template <typename Kern>
+static int resident_workgroups(Kern kernel, int threads) {
+  int dev = 0, cus = 0, per_cu = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+      hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess)
+    return 0;
+  return cus * per_cu;
 }
 
 hipError_t launch_sparse_attn(const PrefillDims& p, const void* q, const void* k,
@@ -522,22 +578,28 @@ hipError_t launch_sparse_attn(const PrefillDims& p, const void* q, const void* k
   const bf16* K = static_cast<const bf16*>(k);
   const bf16* V = static_cast<const bf16*>(v);
   bf16* Vt = static_cast<bf16*>(ws);
+  int* queue = reinterpret_cast<int*>(static_cast<char*>(ws) + vt_bytes(p));
   bf16* O = static_cast<bf16*>(out);
   const dim3 pgrid(p.N / AT_KT, p.Hkv);
-  if (p.D == 128) vt_pack_kernel<128><<<pgrid, 256, 0, st>>>(V, p.N, Vt);
-  else vt_pack_kernel<64><<<pgrid, 256, 0, st>>>(V, p.N, Vt);
+  if (p.D == 128) vt_pack_kernel<128><<<pgrid, 256, 0, st>>>(V, p.N, Vt, queue);
+  else vt_pack_kernel<64><<<pgrid, 256, 0, st>>>(V, p.N, Vt, queue);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  const int grid = p.Hq * p.CB;
-  const int remap = ((p.Hkv * p.CB) % 8 == 0) ? 1 : 0;
+  const int items = p.Hq * p.CB;
+  const int remap = ((p.Hkv * p.CB) % AT_NQUEUE == 0) ? 1 : 0;
   const float sl2 = p.sm_scale * kLog2e;
 #define EGS_MF(DD, BB)                                                                    \
-  sparse_attn_mfma_kernel<DD, BB><<<grid, BB * 2, 0, st>>>(                               \
-      Q, K, Vt, idx, cnt, k_max, O, lse, p.Hkv, p.r, p.N, p.LS, p.CS, p.CB, sl2, remap)
-  if (p.D == 128 && p.LB == 128) EGS_MF(128, 128);
-  else if (p.D == 128 && p.LB == 64) EGS_MF(128, 64);
-  else if (p.D == 64 && p.LB == 128) EGS_MF(64, 128);
-  else EGS_MF(64, 64);
+  {                                                                                       \
+    const int slots = resident_workgroups(sparse_attn_mfma_kernel<DD, BB>, BB * 2);       \
+    if (slots <= 0) return hipErrorInvalidDeviceFunction;                                 \
+    sparse_attn_mfma_kernel<DD, BB><<<std::min(items, slots), BB * 2, 0, st>>>(           \
+        Q, K, Vt, idx, cnt, k_max, O, lse, p.Hkv, p.r, p.N, p.LS, p.CS, p.CB, sl2, remap, \
+        queue);                                                                           \
+  }
+  if (p.D == 128 && p.LB == 128) EGS_MF(128, 128)
+  else if (p.D == 128 && p.LB == 64) EGS_MF(128, 64)
+  else if (p.D == 64 && p.LB == 128) EGS_MF(64, 128)
+  else EGS_MF(64, 64)
 #undef EGS_MF
   return hipGetLastError();
 }
