@@ -43,8 +43,9 @@ namespace egs {
 constexpr int AT_KT = 64;     // keys per LDS stage and per V^T tile
 constexpr int AT_LCAP = 512;  // block-list entries staged in LDS at a time
 constexpr int PV_AHEAD = 4;   // V^T fragments read ahead of their MFMA
-constexpr int AT_NQUEUE = 8;  // work queues of the MFMA kernel (one per XCD)
+constexpr int AT_NQUEUE = 8;  // XCDs, each with r work queues of the MFMA kernel
 constexpr int AT_QSTRIDE = 16;   // ints between queue counters (one 64-byte line each)
+constexpr int AT_QMAX = 128;     // queue counters zeroed by vt_pack (8 XCDs x r <= 16)
 
 // The compiler schedules nothing across this point.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
@@ -70,7 +71,7 @@ __global__ __launch_bounds__(256) void vt_pack_kernel(const bf16* __restrict__ V
   constexpr int VP = D + 2;   // padded row (bf16) to spread the column reads
   __shared__ bf16 tile[AT_KT * VP];
   const int t = blockIdx.x, g = blockIdx.y, tid = threadIdx.x;
-  if (t == 0 && g == 0 && tid < AT_NQUEUE) queue[tid * AT_QSTRIDE] = 0;
+  if (t == 0 && g == 0 && tid < AT_QMAX) queue[tid * AT_QSTRIDE] = 0;
   const bf16* src = V + ((size_t)g * N + (size_t)t * AT_KT) * D;
   constexpr int CH = AT_KT * D / 8;
   for (int q = tid; q < CH; q += 256) {
@@ -116,14 +117,18 @@ struct AtItem {
 // launch while the others set its length.  The launch is therefore a
 // persistent grid of as many workgroups as the CUs hold at once, and each
 // workgroup takes items (KV group, query block, head) from counters in the
-// workspace until they run out.  With xcd_remap the items of KV groups
-// x, x + 8, ... form queue x, which the workgroups of XCD x (workgroup id mod
-// 8) drain first, so a group's K / V blocks meet in one XCD's L2; a
-// workgroup whose queue is empty takes items from the next queues in turn.
-// Each queue holds its items heaviest (latest query block) first.  The
-// counters are zeroed by vt_pack before the launch and only ever
-// incremented, so every workgroup leaves the loop after at most
-// (items + 8) counter increments in all.
+// workspace until they run out.  With xcd_remap there is one queue per
+// (XCD x, head hl of the group): the items of head hl in KV groups x, x + 8,
+// ..., latest (heaviest) query block first.  The workgroups of XCD x
+// (workgroup id mod 8) form r sets (workgroup id / 8 mod r), and set hl
+// drains queue (x, hl) first: a group's K / V blocks then meet in one XCD's
+// L2, and the workgroups of one set run items of one head and one segment
+// (the same block list, of near-equal lengths) side by side, so their tile
+// reads stay close together in the list and hit in L2.  A set whose queue
+// is empty takes items from the other heads' queues of its XCD, then from
+// the other XCDs' queues in turn.  The counters are zeroed by vt_pack
+// before the launch and only ever incremented, so every workgroup leaves
+// the loop after at most (items + 8 r) counter increments in all.
 
 template <int D, int LB>
 __global__ __launch_bounds__(LB * 2) __attribute__((amdgpu_waves_per_eu(2)))
@@ -152,17 +157,21 @@ void sparse_attn_mfma_kernel(
   const int tid = threadIdx.x, lane = tid & 63;
   const int w = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l32 = lane & 31, hg = lane >> 5;
-  const int nq = xcd_remap ? AT_NQUEUE : 1;
+  // queue x * r + hl: XCD x, head hl; home: own XCD, set (workgroup id / 8) mod r
+  const int nq = xcd_remap ? AT_NQUEUE * r : 1;
   const int per_q = Hkv * r * CB / nq;
-  const int home = xcd_remap ? (int)(blockIdx.x & (AT_NQUEUE - 1)) : 0;
+  const int home = xcd_remap ? (int)((blockIdx.x & 7) * r + ((blockIdx.x >> 3) % r)) : 0;
   int tried = 0;   // queues found empty (thread 0 only)
 
   for (;;) {
   // ---- next work item: pair grp = k * Hkv + g (heaviest first), head hl ----
+  // (queue x * r + hl holds pairs grp = 8 k + x, k = 0, 1, ...)
   if (tid == 0) {
     int item = -1;
     while (tried < nq) {
-      const int qx = (home + tried) % nq;
+      // other heads of the own XCD first, then the other XCDs
+      const int qx = xcd_remap ? ((((home / r) + tried / r) % AT_NQUEUE) * r + (home % r + tried) % r)
+                               : 0;
       const int slot = __hip_atomic_fetch_add(queue + qx * AT_QSTRIDE, 1, __ATOMIC_RELAXED,
                                               __HIP_MEMORY_SCOPE_AGENT);
       if (slot < per_q) {
@@ -179,8 +188,8 @@ void sparse_attn_mfma_kernel(
   int grp, hl;
   if (xcd_remap) {
     const int qx = item / per_q, slot = item % per_q;
-    grp = AT_NQUEUE * (slot / r) + qx;
-    hl = slot % r;
+    grp = AT_NQUEUE * slot + qx / r;
+    hl = qx % r;
   } else {
     grp = item / r;
     hl = item % r;
@@ -550,8 +559,8 @@ static bool mfma_path(const PrefillDims& p) {
 
 // V^T tiles, then the work-queue counters
 static size_t vt_bytes(const PrefillDims& p) { return (size_t)p.Hkv * p.N * p.D * sizeof(bf16); }
-constexpr size_t kQueueBytes = 1024;
-static_assert(AT_NQUEUE * AT_QSTRIDE * sizeof(int) <= kQueueBytes, "queue counters overflow");
+constexpr size_t kQueueBytes = AT_QMAX * AT_QSTRIDE * sizeof(int);
+static_assert(AT_QMAX <= 256, "vt_pack zeroes the counters with its 256 threads");
 
 size_t sparse_attn_workspace_bytes(const PrefillDims& p) {
   // V^T tiles and the queue counters for the MFMA path; nothing otherwise
@@ -586,7 +595,7 @@ hipError_t launch_sparse_attn(const PrefillDims& p, const void* q, const void* k
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int items = p.Hq * p.CB;
-  const int remap = ((p.Hkv * p.CB) % AT_NQUEUE == 0) ? 1 : 0;
+  const int remap = ((p.Hkv * p.CB) % AT_NQUEUE == 0 && AT_NQUEUE * p.r <= AT_QMAX) ? 1 : 0;
   const float sl2 = p.sm_scale * kLog2e;
 #define EGS_MF(DD, BB)                                                                    \
   {                                                                                       \

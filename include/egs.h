@@ -235,7 +235,7 @@ egs_status egs_score_select(const egs_prefill_shape* shape, int32_t pool_kind,
  *   q: [Hq, N, d], k, v: [Hkv, N, d], out: [Hq, N, d] (dtype); lse [Hq, N] f32.
  *   workspace: >= egs_sparse_prefill_attn_workspace(shape) bytes, 256-byte
  *   aligned (the bf16 MFMA path packs V into d-major tiles there, Hkv*N*d*2
- *   bytes, followed by 1024 bytes of work-queue counters that the call
+ *   bytes, followed by 8 KB of work-queue counters that the call
  *   resets itself; other paths need none and accept NULL).  Calls that
  *   share a workspace must not overlap in time (one stream orders them).
  * ------------------------------------------------------------------------- */

@@ -133,9 +133,9 @@ def test_budget_and_select_errors(L):
                                          ctypes.c_void_p(3 << 20), FAKE, FAKE, 4, FAKE, None,
                                          FAKE, 1 << 30, None) == L.EGS_EINVAL
     # the bf16 MFMA path needs the packed-V workspace, Hkv * N * d * 2 bytes,
-    # and 1024 bytes of work-queue counters
+    # and 8 KB of work-queue counters
     aws = L.LIB.egs_sparse_prefill_attn_workspace(ctypes.byref(sc))
-    assert aws == 2 * 2048 * 64 * 2 + 1024
+    assert aws == 2 * 2048 * 64 * 2 + 8192
     assert L.LIB.egs_sparse_prefill_attn(ctypes.byref(sc), FAKE, ctypes.c_void_p(2 << 20),
                                          ctypes.c_void_p(3 << 20), FAKE, FAKE, 4,
                                          ctypes.c_void_p(4 << 20), None, FAKE, aws - 1,
