@@ -206,7 +206,16 @@ __global__ __launch_bounds__(256) void obs_pass_kernel(
   constexpr int PW = KPipe<D>::PER_W;
   __shared__ __attribute__((aligned(1024))) bf16 Ks[RT_DEPTH][RT_KT * D];
   __shared__ int cs[SEG ? RT_CK : 1];
-  const int span = blockIdx.x, bg = blockIdx.y;
+  // The hardware hands a grid's workgroups to the CUs in a fixed rotation
+  // (workgroup i to CU i mod 256 when each CU holds the same count), so with
+  // the span index fastest every CU would always get the same span position
+  // and the few CUs that get the edge spans (observer window, sinks; the
+  // slower masked path) would set the pass length.  The linear workgroup id
+  // therefore runs over (batch x group) fastest, and the edge spans - the
+  // last, then the first - come first.
+  const int lin = blockIdx.x + gridDim.x * blockIdx.y;
+  const int bg = lin % gridDim.y, srank = lin / gridDim.y;
+  const int span = srank == 0 ? (int)gridDim.x - 1 : srank - 1;
   const int b = bg / Hkv, g = bg % Hkv;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
   const int l32 = lane & 31, hg = lane >> 5;
