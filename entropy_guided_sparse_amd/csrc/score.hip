@@ -17,9 +17,10 @@
 //    phases) and writes the block means as a bf16 hi/lo pair (k_bar ~= hi +
 //    lo to ~2^-17, so the logits run on bf16 MFMA with two products each).
 //  * probe_stats and probe_mass take (piece, segment, KV group) work items,
-//    96-block pieces for the statistics (three workgroups per CU: the 768
-//    causal items of the 128k layer run in one round) and 160-block pieces
-//    for the masses (80 KB of LDS, two per CU: its 488 items, one round).  The piece's hi/lo block means are copied straight from
+//    only the pieces that hold causal blocks, 96-block pieces for the
+//    statistics (three workgroups per CU: the 768 items of the 128k layer,
+//    three per CU, run in one round) and 160-block pieces for the masses
+//    (80 KB of LDS, two per CU: its 488 items, one round).  The piece's hi/lo block means are copied straight from
 //    global memory into LDS (one round trip, shared by the r heads of the
 //    group) while each wave loads the probe queries of its head into
 //    registers; then v_mfma_f32_32x32x16_bf16 forms the piece's logits.
@@ -56,7 +57,17 @@ struct ScoreLayout {
   int npool;    // pool_keys chunks per KV group
   int npc;      // probe_mass pieces per segment (at most)
   int npc_s;    // probe_stats pieces per segment (at most)
+  int ipg;      // probe_mass pieces inside the causal ranges, per KV group
+  int ipg_s;    // probe_stats pieces inside the causal ranges, per KV group
 };
+
+// Pieces of pc blocks that hold causal blocks, over the segments of one KV
+// group: segment s sees blocks 0 .. (s + 1) bps - 1.
+__host__ __device__ inline int causal_pieces(int CS, int bps, int pc) {
+  int n = 0;
+  for (int s = 0; s < CS; ++s) n += ((s + 1) * bps + pc - 1) / pc;
+  return n;
+}
 
 static size_t sc_align(size_t x) {
   return (x + 255) / 256 * 256;
@@ -67,6 +78,8 @@ static ScoreLayout score_layout(const PrefillDims& p) {
   o.npool = (p.CB + PS_NB - 1) / PS_NB;
   o.npc = (p.CB + PC - 1) / PC;
   o.npc_s = (p.CB + PC_S - 1) / PC_S;
+  o.ipg = causal_pieces(p.CS, p.LS / p.LB, PC);
+  o.ipg_s = causal_pieces(p.CS, p.LS / p.LB, PC_S);
   size_t off = 0;
   auto take = [&](size_t bytes) {
     const size_t at = off;
@@ -242,18 +255,28 @@ __device__ __forceinline__ void stage_piece(bf16* kh, bf16* kl, const bf16* KH, 
   }
 }
 
-// 1-D grid -> (piece, segment, KV group): the items are numbered group-major
-// (group, segment, piece) and every XCD (workgroup id mod 8) takes one
-// contiguous eighth of them, so a group's pooled keys, probe queries and
-// partials are fetched into one L2 only.  Returns false for padding ids.
-__device__ __forceinline__ bool probe_item(int bid, int npc, int CS, int Hkv, int& ch, int& s,
-                                           int& g) {
-  const int items = Hkv * CS * npc, per_xcd = (items + 7) / 8;
+// 1-D grid -> (piece, segment, KV group) over the pieces that hold causal
+// blocks only (ipg per group): the items are numbered group-major (group,
+// segment, piece) and every XCD (workgroup id mod 8) takes one contiguous
+// eighth of them, so a group's pooled keys, probe queries and partials are
+// fetched into one L2 only.  No workgroups are launched for pieces past the
+// causal ranges: the hardware hands a grid's workgroups to the CUs of an XCD
+// in a fixed rotation, which with those pieces in the grid gave some CUs five
+// causal items and others two (at 128k: 96 causal statistics items per XCD,
+// now three per CU).  Returns false for padding ids.
+__device__ __forceinline__ bool probe_item(int bid, int pc, int bps, int CS, int Hkv, int ipg,
+                                           int& ch, int& s, int& g) {
+  const int items = Hkv * ipg, per_xcd = (items + 7) / 8;
   const int item = (bid & 7) * per_xcd + (bid >> 3);
   if (item >= items) return false;
-  ch = item % npc;
-  s = (item / npc) % CS;
-  g = item / (npc * CS);
+  g = item / ipg;
+  int k = item % ipg;
+  for (s = 0;; ++s) {
+    const int n = ((s + 1) * bps + pc - 1) / pc;
+    if (k < n) break;
+    k -= n;
+  }
+  ch = k;
   return true;
 }
 
@@ -285,7 +308,7 @@ __device__ __forceinline__ void load_probe(typename QFrag<TQ>::raw_t (&qr)[RTG][
 template <typename TQ, int D>
 __global__ __launch_bounds__(256, 3) void probe_stats_kernel(
     const TQ* __restrict__ Q, const bf16* __restrict__ kb_hi, const bf16* __restrict__ kb_lo,
-    int Hq, int r, int N, int LS, int LB, int P, int CS, int CB, int npc, float scale_log2,
+    int Hq, int r, int N, int LS, int LB, int P, int CS, int CB, int ipg, float scale_log2,
     float* __restrict__ stat_m, float* __restrict__ stat_l) {
   constexpr int NC = D / 16;
   constexpr int BT = PC_S / 32;
@@ -294,10 +317,10 @@ __global__ __launch_bounds__(256, 3) void probe_stats_kernel(
   __shared__ __attribute__((aligned(16))) bf16 kh[PC_S * D];
   __shared__ __attribute__((aligned(16))) bf16 kl[PC_S * D];
   int ch, s, g;
-  if (!probe_item(blockIdx.x, npc, CS, Hq / r, ch, s, g)) return;
+  if (!probe_item(blockIdx.x, PC_S, LS / LB, CS, Hq / r, ipg, ch, s, g)) return;
   const int cb = (s + 1) * (LS / LB);
   const int c0 = ch * PC_S;
-  if (c0 >= cb) return;
+  const int npc_s = (CB + PC_S - 1) / PC_S;   // partials per row (the stride)
   const int nb = min(PC_S, cb - c0);
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int l32 = lane & 31, hg = lane >> 5;
@@ -368,7 +391,7 @@ __global__ __launch_bounds__(256, 3) void probe_stats_kernel(
       for (int t = 0; t < RTG; ++t) {
         const int urow = grp * 32 * RTG + t * 32 + l32;
         if (hg == 0 && urow < P) {
-          const size_t o = (((size_t)h * CS + s) * npc + ch) * P + urow;
+          const size_t o = (((size_t)h * CS + s) * npc_s + ch) * P + urow;
           stat_m[o] = m[t];
           stat_l[o] = l[t];
         }
@@ -418,7 +441,7 @@ struct RowPartials {
 template <typename TQ, int D>
 __global__ __launch_bounds__(256, 2) void probe_mass_kernel(
     const TQ* __restrict__ Q, const bf16* __restrict__ kb_hi, const bf16* __restrict__ kb_lo,
-    int Hq, int r, int N, int LS, int LB, int P, int CS, int CB, int npc, int npc_s,
+    int Hq, int r, int N, int LS, int LB, int P, int CS, int CB, int npc, int npc_s, int ipg,
     float scale_log2, int kind, float alpha, const float* __restrict__ stat_m,
     const float* __restrict__ stat_l,
     float* __restrict__ ent, float* __restrict__ scores) {
@@ -430,19 +453,11 @@ __global__ __launch_bounds__(256, 2) void probe_mass_kernel(
   __shared__ __attribute__((aligned(16))) bf16 kh[PC * D];
   __shared__ __attribute__((aligned(16))) bf16 kl[PC * D];
   int ch, s, g;
-  if (!probe_item(blockIdx.x, npc, CS, Hq / r, ch, s, g)) return;
+  if (!probe_item(blockIdx.x, PC, LS / LB, CS, Hq / r, ipg, ch, s, g)) return;
   const int cb = (s + 1) * (LS / LB);
   const int c0 = ch * PC;
   const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   const int l32 = lane & 31, hg = lane >> 5;
-  if (c0 >= cb) {   // beyond the causal range: sentinels only
-    const int cend = min(CB, c0 + PC);
-    for (int hl = 0; hl < r; ++hl) {
-      float* out = scores + ((size_t)(g * r + hl) * CS + s) * CB;
-      for (int j = c0 + (int)threadIdx.x; j < cend; j += 256) out[j] = -1.0f;
-    }
-    return;
-  }
   const int nb = min(PC, cb - c0);
   const int nparts = (cb + PC_S - 1) / PC_S;   // probe_stats pieces of segment s
   const size_t u_begin = (size_t)(s + 1) * LS - P;
@@ -541,8 +556,10 @@ __global__ __launch_bounds__(256, 2) void probe_mass_kernel(
         if (a > 0.f) epart += (kind == EGS_SHANNON) ? -a * logf(a) : powf(a, alpha);
       }
     }
-    // blocks of the piece past the segment's causal range
-    for (int j = c0 + nb + lane; j < min(CB, c0 + PC); j += 64) out[j] = -1.0f;
+    // the segment's last causal piece also writes the sentinels of every
+    // block past the causal range (no items are launched for those pieces)
+    if (c0 + nb == cb)
+      for (int j = cb + lane; j < CB; j += 64) out[j] = -1.0f;
     epart = wave_sum(epart);
     if (lane == 0) ent[((size_t)h * CS + s) * npc + ch] = epart;
   }
@@ -581,18 +598,19 @@ static hipError_t score_dispatch(const PrefillDims& p, const ScoreLayout& ly, co
   float* sl = reinterpret_cast<float*>(ws + ly.stat_l);
   float* en = reinterpret_cast<float*>(ws + ly.ent);
   const int g1 = (p.Hkv * ly.npool + 7) / 8 * 8;
-  const int g2s = (p.Hkv * p.CS * ly.npc_s + 7) / 8 * 8;
-  const int g2 = (p.Hkv * p.CS * ly.npc + 7) / 8 * 8;
+  const int g2s = (p.Hkv * ly.ipg_s + 7) / 8 * 8;
+  const int g2 = (p.Hkv * ly.ipg + 7) / 8 * 8;
   hipError_t e;
 #define EGS_POOL(DD)                                                                         \
   pool_keys_kernel<T, DD, PS_NW><<<g1, 64 * PS_NW, 0, st>>>(K, p.N, p.LB, p.CB, p.Hkv,      \
                                                             ly.npool, H, L)
 #define EGS_STATS(DD)                                                                        \
   probe_stats_kernel<T, DD><<<g2s, 256, 0, st>>>(Q, H, L, p.Hq, p.r, p.N, p.LS, p.LB, p.P,  \
-                                                  p.CS, p.CB, ly.npc_s, sl2, sm, sl)
+                                                  p.CS, p.CB, ly.ipg_s, sl2, sm, sl)
 #define EGS_MASS(DD)                                                                         \
   probe_mass_kernel<T, DD><<<g2, 256, 0, st>>>(Q, H, L, p.Hq, p.r, p.N, p.LS, p.LB, p.P,    \
-                                                p.CS, p.CB, ly.npc, ly.npc_s, sl2, kind,   \
+                                                p.CS, p.CB, ly.npc, ly.npc_s, ly.ipg, sl2, \
+                                                kind,                                      \
                                                 alpha, sm, sl, en, scores)
 #define EGS_D_SWITCH(M)              \
   switch (p.D) {                     \
