@@ -125,10 +125,12 @@ struct AtItem {
 // L2, and the workgroups of one set run items of one head and one segment
 // (the same block list, of near-equal lengths) side by side, so their tile
 // reads stay close together in the list and hit in L2.  A set whose queue
-// is empty takes items from the other heads' queues of its XCD, then from
-// the other XCDs' queues in turn.  The counters are zeroed by vt_pack
-// before the launch and only ever incremented, so every workgroup leaves
-// the loop after at most (items + 8 r) counter increments in all.
+// is empty takes items from the other heads' queues of its XCD; once those
+// are empty too, wave 0 reads every counter (one lane each) and takes from
+// the queue with the most items left, so the XCDs of heavy KV groups get
+// help from all others at once.  The counters are zeroed by vt_pack before
+// the launch and only ever incremented; a workgroup fails to take an item
+// at most once per queue, so every workgroup leaves the loop.
 
 template <int D, int LB>
 __global__ __launch_bounds__(LB * 2) __attribute__((amdgpu_waves_per_eu(2)))
@@ -161,26 +163,56 @@ void sparse_attn_mfma_kernel(
   const int nq = xcd_remap ? AT_NQUEUE * r : 1;
   const int per_q = Hkv * r * CB / nq;
   const int home = xcd_remap ? (int)((blockIdx.x & 7) * r + ((blockIdx.x >> 3) % r)) : 0;
-  int tried = 0;   // queues found empty (thread 0 only)
+  int tried = 0;   // wave 0: queues of the own XCD found empty (home first)
 
   for (;;) {
   // ---- next work item: pair grp = k * Hkv + g (heaviest first), head hl ----
   // (queue x * r + hl holds pairs grp = 8 k + x, k = 0, 1, ...)
-  if (tid == 0) {
+  if (w == 0) {
     int item = -1;
-    while (tried < nq) {
-      // other heads of the own XCD first, then the other XCDs
-      const int qx = xcd_remap ? ((((home / r) + tried / r) % AT_NQUEUE) * r + (home % r + tried) % r)
-                               : 0;
-      const int slot = __hip_atomic_fetch_add(queue + qx * AT_QSTRIDE, 1, __ATOMIC_RELAXED,
-                                              __HIP_MEMORY_SCOPE_AGENT);
+    const int nown = xcd_remap ? r : 1;
+    while (tried < nown) {
+      const int qx = xcd_remap ? (home / r) * r + (home % r + tried) % r : 0;
+      int slot = 0;
+      if (lane == 0)
+        slot = __hip_atomic_fetch_add(queue + qx * AT_QSTRIDE, 1, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+      slot = __shfl(slot, 0);
       if (slot < per_q) {
         item = qx * per_q + slot;
         break;
       }
       ++tried;
     }
-    s_item = item;
+    // the own XCD's queues are empty: the queue with the most items left
+    // (ties: the first after home); a failed take means that queue emptied
+    // meanwhile, and every retry sees one more empty queue
+    while (item < 0 && tried >= nown) {
+      int best = 0, bq = -1;
+      for (int q0 = 0; q0 < nq; q0 += 64) {
+        const int k = q0 + lane;
+        const int qx = (home + k) % nq;
+        int left = 0;
+        if (k < nq)
+          left = per_q - min(per_q, __hip_atomic_load(queue + qx * AT_QSTRIDE, __ATOMIC_RELAXED,
+                                                       __HIP_MEMORY_SCOPE_AGENT));
+        int key = left > 0 ? (min(left, (1 << 22) - 1) << 8) | (255 - k) : 0;
+#pragma unroll
+        for (int o = 32; o > 0; o >>= 1) key = max(key, __shfl_xor(key, o));
+        if ((key >> 8) > best) {
+          best = key >> 8;
+          bq = (home + 255 - (key & 255)) % nq;
+        }
+      }
+      if (best == 0) break;
+      int slot = 0;
+      if (lane == 0)
+        slot = __hip_atomic_fetch_add(queue + bq * AT_QSTRIDE, 1, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_AGENT);
+      slot = __shfl(slot, 0);
+      if (slot < per_q) item = bq * per_q + slot;
+    }
+    if (lane == 0) s_item = item;
   }
   __syncthreads();
   const int item = __builtin_amdgcn_readfirstlane(s_item);
