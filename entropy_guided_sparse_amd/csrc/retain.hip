@@ -50,6 +50,8 @@
 
 namespace egs {
 
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+
 // The compiler schedules nothing across this point.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 // Keeps the computation of x before this point: an empty volatile asm that
@@ -1509,12 +1511,17 @@ hipError_t launch_kv_retain(const DecodeDims& p, const egs_retain_params& prm, c
 // One workgroup per (split of spl kept entries, batch x KV group); the GQA
 // group's query heads (one per wavefront, four at a time) share every 64-entry
 // K / V stage, copied straight into LDS two stages deep.
-//   QK: a lane owns one entry of the stage; the head's query is broadcast from
-//       LDS; the entry's K row is read as swizzled 16-byte chunks.
+//   QK: a lane owns one entry of the stage; the entry's K row is read as
+//       swizzled 16-byte chunks and meets the head's bf16 query (one
+//       broadcast LDS read per chunk) in v_dot2c_f32_bf16: exact products
+//       of bf16 pairs, fp32 sums, no conversions.
 //   softmax: online per head over the split (wave max / sum per stage).
 //   PV: a lane owns one 16-byte chunk of the V rows for a quarter (d 128) or
-//       an eighth (d 64) of the stage's entries (16-byte LDS reads); the
-//       lanes' partial outputs are summed once per split.
+//       an eighth (d 64) of the stage's entries (16-byte LDS reads); two keys
+//       at a time, their probabilities as a bf16 pair (the row sums stay in
+//       fp32) and each dimension's two V values as a pair go through
+//       v_dot2c_f32_bf16; the lanes' partial outputs are summed once per
+//       split.
 // Each split leaves its unnormalised output, maximum and sum for the combine.
 template <int D>
 __global__ __launch_bounds__(256) void decode_attn_split_kernel(
@@ -1529,7 +1536,7 @@ __global__ __launch_bounds__(256) void decode_attn_split_kernel(
   static_assert(PIECES % 4 == 0, "stage copies must split over four waves");
   __shared__ __attribute__((aligned(1024))) bf16 Ks[2][ST * D];
   __shared__ __attribute__((aligned(1024))) bf16 Vs[2][ST * D];
-  __shared__ float qsh[4][D];
+  __shared__ __attribute__((aligned(16))) bf16 qsb[4][D];
   __shared__ float psh[4][ST];
   const int sp = blockIdx.x, bg = blockIdx.y, b = bg / Hkv, g = bg % Hkv;
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6;
@@ -1557,7 +1564,7 @@ __global__ __launch_bounds__(256) void decode_attn_split_kernel(
     const int h = g * r + (hv ? hl : 0);
     {
       const bf16* q = Qn + ((size_t)b * Hq + h) * D;
-      for (int d = lane; d < D; d += 64) qsh[w][d] = hv ? bf2f(q[d]) * sl2 : 0.f;
+      for (int d = lane; d < D; d += 64) qsb[w][d] = hv ? q[d] : (bf16)0.f;
     }
     copy_stage(0, 0);
     // PV: lane = (key group kg, 16-byte chunk c of the V row): dims 8c .. 8c+7
@@ -1576,16 +1583,21 @@ __global__ __launch_bounds__(256) void decode_attn_split_kernel(
       const bf16* vs = Vs[st & 1];
       const int t = t_begin + st * ST + lane;
       // logit of this lane's entry (log2 units)
+      // bf16 pairs straight into v_dot2c_f32_bf16 (exact products, fp32
+      // sums); the query chunk is one broadcast LDS read
       float z = 0.f;
 #pragma unroll
       for (int c = 0; c < KCH; ++c) {
-        float x[8];
         const bf16x8 kv = load8(ks + lane * D + ((c ^ lds_swz<D * 2>(lane)) * 8));
+        const bf16x8 qv = load8(&qsb[w][8 * c]);
 #pragma unroll
-        for (int e = 0; e < 8; ++e) x[e] = (float)kv[e];
-#pragma unroll
-        for (int e = 0; e < 8; ++e) z = __builtin_fmaf(qsh[w][8 * c + e], x[e], z);
+        for (int e = 0; e < 4; ++e) {
+          const bf16x2 kp = {kv[2 * e], kv[2 * e + 1]};
+          const bf16x2 qp = {qv[2 * e], qv[2 * e + 1]};
+          z = __builtin_amdgcn_fdot2_f32_bf16(kp, qp, z, false);
+        }
       }
+      z *= sl2;
       if (t >= t_end) z = -INFINITY;
       const float mx = fmaxf(m, wave_max(z));
       const float pz = fast_exp2(z - mx);
@@ -1598,13 +1610,19 @@ __global__ __launch_bounds__(256) void decode_attn_split_kernel(
       __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
 #pragma unroll
       for (int e = 0; e < 8; ++e) o[e] *= alpha;
+      // two keys at a time: their probabilities as a bf16 pair and, per
+      // dimension, the two V values as a pair, into v_dot2c_f32_bf16
 #pragma unroll
-      for (int j = 0; j < KPG; ++j) {
+      for (int j = 0; j < KPG; j += 2) {
         const int k = kg * KPG + j;
-        const float pk = psh[w][k];
-        const bf16x8 vv = load8(vs + k * D + ((vc ^ lds_swz<D * 2>(k)) * 8));
+        const bf16x2 pp = {(bf16)psh[w][k], (bf16)psh[w][k + 1]};
+        const bf16x8 v0 = load8(vs + k * D + ((vc ^ lds_swz<D * 2>(k)) * 8));
+        const bf16x8 v1 = load8(vs + (k + 1) * D + ((vc ^ lds_swz<D * 2>(k + 1)) * 8));
 #pragma unroll
-        for (int e = 0; e < 8; ++e) o[e] = __builtin_fmaf(pk, (float)vv[e], o[e]);
+        for (int e = 0; e < 8; ++e) {
+          const bf16x2 vp = {v0[e], v1[e]};
+          o[e] = __builtin_amdgcn_fdot2_f32_bf16(vp, pp, o[e], false);
+        }
       }
     }
     // sum the key groups (lanes vc, vc + KCH, ...)
