@@ -52,6 +52,33 @@ namespace egs {
 
 typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 
+// All-reduces over the 64 lanes of a wave without the LDS path: DPP within
+// each 16-lane row (lane ^ 1, lane ^ 2, then the mirrored half and the
+// mirrored row, which pair lanes whose earlier steps already agree), then
+// the row and half swaps of v_permlane16_swap / v_permlane32_swap.
+__device__ __forceinline__ float dpp_row_max(float v) {
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false)));
+  v = fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false)));
+  return fmaxf(v, __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false)));
+}
+__device__ __forceinline__ float dpp_row_sum(float v) {
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0xB1, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x4E, 0xF, 0xF, false));
+  v += __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x141, 0xF, 0xF, false));
+  return v + __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), 0x140, 0xF, 0xF, false));
+}
+__device__ __forceinline__ float xrow_sum(float v) {   // lanes l and l ^ 16
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return __uint_as_float(r[0]) + __uint_as_float(r[1]);
+}
+__device__ __forceinline__ float wave_max_v(float v) {
+  v = dpp_row_max(v);
+  const auto r = __builtin_amdgcn_permlane16_swap(__float_as_uint(v), __float_as_uint(v), false, false);
+  return xhalf_max(fmaxf(__uint_as_float(r[0]), __uint_as_float(r[1])));
+}
+__device__ __forceinline__ float wave_sum_v(float v) { return xhalf_sum(xrow_sum(dpp_row_sum(v))); }
+
 // The compiler schedules nothing across this point.
 __device__ __forceinline__ void sched_fence() { __builtin_amdgcn_sched_barrier(0); }
 // Keeps the computation of x before this point: an empty volatile asm that
@@ -1599,10 +1626,10 @@ __global__ __launch_bounds__(256) void decode_attn_split_kernel(
       }
       z *= sl2;
       if (t >= t_end) z = -INFINITY;
-      const float mx = fmaxf(m, wave_max(z));
+      const float mx = fmaxf(m, wave_max_v(z));
       const float pz = fast_exp2(z - mx);
       const float alpha = fast_exp2(m - mx);
-      l = l * alpha + wave_sum(pz);
+      l = l * alpha + wave_sum_v(pz);
       m = mx;
       psh[w][lane] = pz;
       __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
@@ -1626,10 +1653,12 @@ __global__ __launch_bounds__(256) void decode_attn_split_kernel(
       }
     }
     // sum the key groups (lanes vc, vc + KCH, ...)
+    if constexpr (KCH < 16) {
 #pragma unroll
-    for (int sh = KCH; sh < 64; sh <<= 1)
+      for (int e = 0; e < 8; ++e) o[e] += __shfl_xor(o[e], KCH);
+    }
 #pragma unroll
-      for (int e = 0; e < 8; ++e) o[e] += __shfl_xor(o[e], sh);
+    for (int e = 0; e < 8; ++e) o[e] = xhalf_sum(xrow_sum(o[e]));
     if (hv) {
       float* pp = part + (((size_t)b * Hq + h) * nsplit + sp) * (D + 2);
       if (kg == 0) {
