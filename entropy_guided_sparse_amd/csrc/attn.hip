@@ -12,10 +12,11 @@
 //    order in which the softmax probabilities leave the accumulator.  Every
 //    MFMA operand of the main kernel is then one 16-byte LDS read, and no
 //    transposition is repeated by the many query blocks that select a block.
-//  * One workgroup per (head, query block), L_B/32 wavefronts of 32 query
-//    rows.  Workgroups run heaviest (latest) query block first, and the r
-//    heads of a KV group for the same query block go to the same XCD so their
-//    shared K/V blocks meet in that XCD's L2.
+//  * A work item is one (head, query block), run by a workgroup of L_B/32
+//    wavefronts of 32 query rows.  The launch is a persistent grid that takes
+//    items from work queues, one per (XCD, head of the group), each heaviest
+//    (latest query block) first; a KV group's items stay on one XCD so its
+//    shared K/V blocks meet in that XCD's L2 (details at the kernel).
 //  * Transposed flash formulation, no cross-lane shuffles:
 //        S^T = K Q^T     (A = K tile from LDS, B = Q^T held in registers)
 //        P^T = exp2(S^T - m)   (a lane owns one query row)
