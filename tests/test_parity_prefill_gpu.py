@@ -175,6 +175,18 @@ def test_mfma_d64_block128(api):
     run_pipeline(api, cfg, _policy(api, api.L.EGS_BUDGET_FIXED, frac=0.4), seed=5)
 
 
+# The attention's work queues: one per (XCD, head of the KV group), 8 r of
+# them, while 8 r fits the 128 counters the workspace holds; r = 16 uses every
+# counter, r = 17 falls back to one queue (H_kv * C_B is a multiple of 8 in
+# both, so only r decides).
+@pytest.mark.parametrize("n_q_heads", [32, 34])
+def test_mfma_work_queue_edges(api, n_q_heads):
+    cfg = synth.small_prefill_config(n_q_heads=n_q_heads, n_kv_heads=2, head_dim=128,
+                                     seq_len=2048, block_size=64, segment_size=1024,
+                                     probe_len=32, head_types="fraction", hot_count="2")
+    run_pipeline(api, cfg, _policy(api, api.L.EGS_BUDGET_FIXED, frac=0.3), seed=12)
+
+
 @pytest.mark.parametrize("case", ["one_block_segments", "single_segment", "probe_whole",
                                   "probe_one", "no_xcd_remap"])
 def test_degenerate_shapes(api, case):
