@@ -368,21 +368,26 @@ __global__ __launch_bounds__(256, 3) void probe_stats_kernel(
             if (QFrag<TQ>::kSplit) z[t] = mfma32(ah, ql[t][c], z[t]);
           }
         }
-        // z[t][i]: block c0 + bt*32 + acc_row(i, lane) against probe row l32 of tile t
+        // z[t][i]: block c0 + bt*32 + acc_row(i, lane) against probe row l32 of
+        // tile t.  Only the piece's last tile can hold blocks past it; the
+        // maximum is taken on the raw logits and scaled once (scale_log2 > 0
+        // and rounding keep the order), and each term is one FMA and one exp2.
+        const bool ragged = bt * 32 + 32 > nb;
 #pragma unroll
         for (int t = 0; t < RTG; ++t) {
-          float tmax = -INFINITY;
+          if (ragged) {
 #pragma unroll
-          for (int i = 0; i < 16; ++i) {
-            const float v = bt * 32 + acc_row(i, lane) < nb ? z[t][i] * scale_log2 : -INFINITY;
-            z[t][i] = v;
-            tmax = fmaxf(tmax, v);
+            for (int i = 0; i < 16; ++i)
+              if (bt * 32 + acc_row(i, lane) >= nb) z[t][i] = -INFINITY;
           }
-          tmax = xhalf_max(tmax);   // finite: the tile's first block is causal
+          float tmax = z[t][0];
+#pragma unroll
+          for (int i = 1; i < 16; ++i) tmax = fmaxf(tmax, z[t][i]);
+          tmax = xhalf_max(tmax) * scale_log2;   // finite: the tile's first block is causal
           const float mn = fmaxf(m[t], tmax);
           float sum = 0.f;
 #pragma unroll
-          for (int i = 0; i < 16; ++i) sum += fast_exp2(z[t][i] - mn);
+          for (int i = 0; i < 16; ++i) sum += fast_exp2(__builtin_fmaf(z[t][i], scale_log2, -mn));
           l[t] = l[t] * fast_exp2(m[t] - mn) + xhalf_sum(sum);
           m[t] = mn;
         }
