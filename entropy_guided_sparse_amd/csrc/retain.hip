@@ -91,7 +91,7 @@ constexpr int RT_KT = 64;     // keys per LDS stage
 constexpr int SEL_T = 1024;   // threads of the select kernel
 constexpr int SEL_CH = 16384; // keys per chunk of the split top-k
 constexpr int DA_SPL_MIN = 192;   // kept entries per decode-attention split: the
-constexpr int DA_SPL_MAX = 512;   // range the launcher chooses from (multiples of 64)
+constexpr int DA_SPL_MAX = 1024;   // range the launcher chooses from (multiples of 64)
 
 struct RetainLayout {
   size_t stat_m, stat_l, row_m, row_inv, mass, ent, weight, mu, qsum, tstats;
@@ -1741,8 +1741,9 @@ __global__ __launch_bounds__(256) void decode_attn_combine_kernel(const float* _
 // Split size: the largest multiple of 64 in [DA_SPL_MIN, DA_SPL_MAX] whose
 // last round of workgroups still fills 90% of the 512 workgroup slots (256
 // CUs x 2, LDS-bound); else the one that leaves the fewest slots idle.  Long
-// caches take 512 (fewer partials to combine); the 4,356 kept entries of a
-// batch-8 step take 192 (23 splits x 64 rows: 2.9 rounds instead of 2.25).
+// caches take 1024 (fewer prologues and partials to combine); the 4,356 kept
+// entries of a batch-8 step take 576 (8 splits x 64 rows: exactly one round,
+// where 192-entry splits needed three).
 static int decode_split(const DecodeDims& p, int n_total) {
   constexpr long kSlots = 512;
   const long rows = (long)p.B * p.Hkv;

@@ -206,11 +206,13 @@ def test_retain_all_scores_tied(api):
     np.testing.assert_array_equal(o_keep, want)
 
 
-# The launcher splits the kept entries into pieces of 192 to 512 entries, the
+# The launcher splits the kept entries into pieces of 192 to 1024 entries, the
 # size chosen from n_total and batch x KV groups (64 here); these n_total reach
-# every size it can pick: 1 and 4000 -> 512, 193 -> 192, 257 -> 256, 321 -> 320,
-# 2561 -> 384, 3137 -> 448.
-@pytest.mark.parametrize("n_total", [1, 193, 257, 321, 2561, 3137, 4000])
+# every size it can pick: 193 -> 192, 257 -> 256, 321 -> 320, 2561 -> 384,
+# 3137 -> 448, 4000 -> 512, 4033 -> 576, 4481 -> 640, 4929 -> 704, 5377 -> 768,
+# 5825 -> 832, 6273 -> 896, 6721 -> 960, 1 -> 1024.
+@pytest.mark.parametrize("n_total", [1, 193, 257, 321, 2561, 3137, 4000, 4033, 4481, 4929,
+                                     5377, 5825, 6273, 6721])
 def test_decode_attention_every_split_size(api, n_total):
     B, Hq, Hkv, d = 8, 32, 8, 128
     log(f"[decode attention splits] B={B} Hq={Hq} Hkv={Hkv} d={d} n_total={n_total}")

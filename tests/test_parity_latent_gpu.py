@@ -30,10 +30,10 @@ def _bf16(x):
 
 
 # (B, Hq, Hkv, prompt length, spare capacity, n_keep, N_D, interval, tokens).
-# The batch-8 case runs near 4,480 entries in an 8,192-row cache: there the
-# attention split the launcher picks (192 entries, 24 splits per row) yields
-# more partials than the cache's full length would (512, 16 splits), so the
-# step's workspace must be sized for every length up to the capacity.
+# The batch-8 case runs near 4,480 entries in an 8,192-row cache.  The
+# attention split the launcher picks is not monotone in the length (a shorter
+# list can take a smaller split and so more partials), so the step's workspace
+# is sized for every length up to the capacity, not for the capacity alone.
 CASES = [(2, 8, 2, 2048, 0, 512, 96, 64, 170),
          (2, 8, 2, 2048, 0, 512, 10, 0, 40),
          (8, 32, 8, 4466, 8192 - 4466 - 24, 4096, 16, 0, 24)]
