@@ -239,6 +239,48 @@ def test_empty_lists_attend_diagonal_only(api):
     assert ma <= ATTN_MAX_ABS and rel <= ATTN_REL_L2
 
 
+@pytest.mark.parametrize("jump", [8.0, 60.0])
+def test_logit_jumps_after_the_first_block(api, jump):
+    # Every block listed, ascending.  Keys of some blocks are scaled by `jump`,
+    # so rows meet logits far above the maximum of their first block: x8 (up
+    # to ~35 in log2 units) makes the MFMA kernel raise its running maximum
+    # mid-list and rescale O; x60 (~260) lies beyond the fp32 range of the
+    # probabilities, so the rescale factor underflows to zero and the earlier
+    # blocks drop out, as they do in float64.  Both must match the oracle.
+    Hq, Hkv, d, N, LB, LS = 4, 2, 128, 2048, 128, 512
+    CS, CB = N // LS, N // LB
+    rng = np.random.default_rng(31)
+    q = rng.standard_normal((Hq, N, d)).astype(np.float32)
+    k = rng.standard_normal((Hkv, N, d)).astype(np.float32)
+    v = rng.standard_normal((Hkv, N, d)).astype(np.float32)
+    for g, blk in ((0, 3), (1, 5), (1, 9)):
+        k[g, blk * LB:(blk + 1) * LB] *= jump
+    qt, kt, vt = (torch.from_numpy(x).to(torch.bfloat16) for x in (q, k, v))
+    q64, k64, v64 = (x.double().numpy() for x in (qt, kt, vt))
+    log(f"[prefill parity] logit jump x{jump} Hq={Hq} Hkv={Hkv} d={d} N={N} LB={LB} LS={LS}")
+    cfg = synth.small_prefill_config(n_q_heads=Hq, n_kv_heads=Hkv, head_dim=d, seq_len=N,
+                                     block_size=LB, segment_size=LS, probe_len=64)
+    shape = prefill_shape(api, cfg)
+    idx = np.full((Hq, CS, CB), -1, dtype=np.int32)
+    cnt = np.zeros((Hq, CS), dtype=np.int32)
+    for s_ in range(CS):
+        cb = (s_ + 1) * LS // LB
+        idx[:, s_, :cb] = np.arange(cb)
+        cnt[:, s_] = cb
+    out, lse = api.sparse_prefill_attn(shape, qt.cuda(), kt.cuda(), vt.cuda(),
+                                       torch.from_numpy(idx).cuda(), torch.from_numpy(cnt).cuda(),
+                                       return_lse=True)
+    torch.cuda.synchronize()
+    r_out, r_lse = O.sparse_prefill_attn(q64, k64, v64, idx, cnt, LS, LB)
+    ma, rel = attn_errors(out.float().cpu().numpy(), r_out)
+    g_lse = lse.cpu().numpy()
+    dl = float((np.abs(g_lse - r_lse) - 2e-6 * np.abs(r_lse)).max())
+    log(f"  attention max|d|={ma:.3e} relL2={rel:.3e} lse excess={dl:.3e}")
+    assert np.isfinite(g_lse).all()
+    assert ma <= ATTN_MAX_ABS and rel <= ATTN_REL_L2
+    assert dl <= 1e-3
+
+
 def test_select_zero_and_clamped_budgets(api):
     cfg = synth.small_prefill_config(n_q_heads=2, n_kv_heads=1, head_dim=64, seq_len=1024,
                                      block_size=64, segment_size=256, probe_len=32,
