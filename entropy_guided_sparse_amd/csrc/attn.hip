@@ -349,8 +349,31 @@ void sparse_attn_mfma_kernel(
     const int row = (f % ND) * 32 + l32, ch = f / ND;
     return load8(vs + row * KT + (((2 * ch + hg) ^ lds_swz<KT * 2>(row)) * 8));
   };
-  // causal mask of the own block, row maximum and (rarely) a raised maximum
-  auto softmax_max = [&](floatx16 (&st)[2], const AtItem& it) {
+  // probabilities of 16-key group q = exp2(S^T - m) (accumulator tile q / 2,
+  // slots 8 (q % 2) .. 8 (q % 2) + 7)
+  auto group_exp = [&](const floatx16 (&st)[2], int q, float moff, float (&pv)[8]) {
+#pragma unroll
+    for (int e = 0; e < 8; ++e)
+      pv[e] = fast_exp2(__builtin_fmaf(st[q >> 1][8 * (q & 1) + e], scale_log2, -moff));
+  };
+  // their bf16 B operand; their row sum joins l_run
+  auto group_operand = [&](const float (&pv)[8]) -> bf16x8 {
+    bf16x8 r;
+#pragma unroll
+    for (int e = 0; e < 8; ++e) r[e] = f2bf(pv[e]);
+    l_run += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
+    return r;
+  };
+  auto softmax_exp = [&](const floatx16 (&st)[2], int q, float moff) -> bf16x8 {
+    float pv[8];
+    group_exp(st, q, moff, pv);
+    return group_operand(pv);
+  };
+  // Causal mask of the own block, row maximum and (rarely) a raised maximum.
+  // Beside the maximum's serial chain the VALU forms group 0's probabilities
+  // against the current maximum (formed again in the rare stage that raises
+  // it); returns them as the first P^T operand.
+  auto softmax_max = [&](floatx16 (&st)[2], const AtItem& it) -> bf16x8 {
     if (it.diag && (it.sub * KT + KT - 1 > w * 32)) {
 #pragma unroll
       for (int kt = 0; kt < 2; ++kt)
@@ -358,6 +381,8 @@ void sparse_attn_mfma_kernel(
         for (int i = 0; i < 16; ++i)
           if (it.sub * KT + kt * 32 + acc_row(i, lane) > row_local) st[kt][i] = -INFINITY;
     }
+    float pv0[8];
+    group_exp(st, 0, m_run * scale_log2, pv0);
     float mx = st[0][0];
 #pragma unroll
     for (int kt = 0; kt < 2; ++kt)
@@ -374,28 +399,17 @@ void sparse_attn_mfma_kernel(
       for (int dt = 0; dt < ND; ++dt)
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[dt][i] *= alpha;
+      group_exp(st, 0, m_run * scale_log2, pv0);
     }
-  };
-  // P^T of 16-key group q = exp2(S^T - m) as a bf16 B operand (accumulator
-  // tile q / 2, slots 8 (q % 2) .. 8 (q % 2) + 7), and its row sum
-  auto softmax_exp = [&](const floatx16 (&st)[2], int q, float moff) -> bf16x8 {
-    bf16x8 r;
-    float pv[8];
-#pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      pv[e] = fast_exp2(__builtin_fmaf(st[q >> 1][8 * (q & 1) + e], scale_log2, -moff));
-      r[e] = f2bf(pv[e]);
-    }
-    l_run += ((pv[0] + pv[1]) + (pv[2] + pv[3])) + ((pv[4] + pv[5]) + (pv[6] + pv[7]));
-    return r;
+    return group_operand(pv0);
   };
   // O^T += V^T P^T, 16-key group outer: the ND MFMAs of group q run while the
   // VALU forms the probabilities of group q + 1.  fv[0 .. PV_AHEAD-1] hold
-  // the first V^T fragments on entry.
-  auto mma_pv = [&](const floatx16 (&st)[2], const bf16* vs, bf16x8 (&fv)[PV_AHEAD + 1]) {
+  // the first V^T fragments and pcur group 0's P^T on entry.
+  auto mma_pv = [&](const floatx16 (&st)[2], const bf16* vs, bf16x8 (&fv)[PV_AHEAD + 1],
+                    bf16x8 pcur) {
     constexpr int NF = ND * 4;
     const float moff = m_run * scale_log2;
-    bf16x8 pcur = softmax_exp(st, 0, moff);
 #pragma unroll
     for (int q = 0; q < 4; ++q) {
       sched_fence();
@@ -442,8 +456,8 @@ void sparse_attn_mfma_kernel(
 #pragma unroll
       for (int f = 0; f < PV_AHEAD; ++f) fv[f] = vfrag(v_cur, f);   // in flight during the max
       sched_fence();
-      softmax_max(st, it0);
-      mma_pv(st, v_cur, fv);
+      const bf16x8 p0 = softmax_max(st, it0);
+      mma_pv(st, v_cur, fv, p0);
     }
     if (!it1.valid) return false;
     wait_vmem();
