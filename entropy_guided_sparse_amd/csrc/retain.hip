@@ -30,7 +30,7 @@
 //  * Page-level retention (EntroPrefill Sec. 7) keeps whole pages: page maxima
 //    of the token scores, the same select over page scores, and unions over
 //    the heads of a group or the groups of a layer through an LDS bitmap.
-//  * Decode attention splits the kept range into 192- to 512-entry splits
+//  * Decode attention splits the kept range into 192- to 1024-entry splits
 //    (chosen per call so the last round of workgroups fills the CUs); the GQA
 //    group's heads share each 64-entry K / V stage in LDS (lane-per-entry dot
 //    products, lane-per-dim PV) and a combine kernel merges the splits with
