@@ -199,6 +199,7 @@ __global__ __launch_bounds__(256) void maxmin_score_kernel(
   // fold the segment's pooled query chunks
   for (int d = tid; d < D; d += 256) {
     float a = -INFINITY, b = INFINITY;
+#pragma unroll 8
     for (int c = 0; c < nqc; ++c) {
       const size_t o = ((size_t)h * qtot + (size_t)s * nqc + c) * D + d;
       a = fmaxf(a, (float)qmx[o]);
@@ -218,17 +219,30 @@ __global__ __launch_bounds__(256) void maxmin_score_kernel(
     const vec_t* kx = reinterpret_cast<const vec_t*>(kmx + ((size_t)g * CB + j) * D);
     const vec_t* kn = reinterpret_cast<const vec_t*>(kmn + ((size_t)g * CB + j) * D);
     double dot[4] = {0.0, 0.0, 0.0, 0.0};
-#pragma unroll 4
-    for (int c = 0; c < D / EPV; ++c) {
-      const vec_t x = kx[c], n = kn[c];
+    // the loads of half a row are issued together, before its products (a
+    // whole row at once spills registers)
+    constexpr int NV = D / EPV, HV = NV >= 8 ? NV / 2 : NV;
+#pragma unroll 1
+    for (int c0 = 0; c0 < NV; c0 += HV) {
+      vec_t xs[HV], ns[HV];
 #pragma unroll
-      for (int e = 0; e < EPV; ++e) {
-        const double qa = qr[0][c * EPV + e], qb = qr[1][c * EPV + e];
-        const double fx = (float)x[e], fn = (float)n[e];
-        dot[0] = __builtin_fma(qa, fx, dot[0]);
-        dot[1] = __builtin_fma(qa, fn, dot[1]);
-        dot[2] = __builtin_fma(qb, fx, dot[2]);
-        dot[3] = __builtin_fma(qb, fn, dot[3]);
+      for (int c = 0; c < HV; ++c) {
+        xs[c] = kx[c0 + c];
+        ns[c] = kn[c0 + c];
+      }
+#pragma unroll
+      for (int cc = 0; cc < HV; ++cc) {
+        const int c = c0 + cc;
+        const vec_t x = xs[cc], n = ns[cc];
+#pragma unroll
+        for (int e = 0; e < EPV; ++e) {
+          const double qa = qr[0][c * EPV + e], qb = qr[1][c * EPV + e];
+          const double fx = (float)x[e], fn = (float)n[e];
+          dot[0] = __builtin_fma(qa, fx, dot[0]);
+          dot[1] = __builtin_fma(qa, fn, dot[1]);
+          dot[2] = __builtin_fma(qb, fx, dot[2]);
+          dot[3] = __builtin_fma(qb, fn, dot[3]);
+        }
       }
     }
 #pragma unroll
